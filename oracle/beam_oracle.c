@@ -1,0 +1,307 @@
+/*
+ * CPU oracle for the Beam MoE sublayer. TEST INFRASTRUCTURE ONLY (see
+ * beam_oracle.h): plain, slow, single-threaded, obviously correct. Shares no
+ * code with the GPU library.
+ *
+ * Readings of points the pages leave open are marked "reading:" and are the
+ * same ones the GPU path implements.
+ */
+#include "beam_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+uint16_t oracle_bf16(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) /* inf or nan */
+    return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x0040u : 0u));
+  /* round to nearest, ties to even, on the 16 bits that are dropped */
+  uint32_t lsb = (u >> 16) & 1u;
+  u = u + 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+float oracle_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float v;
+  memcpy(&v, &u, 4);
+  return v;
+}
+
+/* [vLLM §MoE und Residual-Stream; SGLang §稠密层与分组 MoE 路由 (grouped MoE routing)]
+ * Scores are sigmoid(logit). Reading: evaluated in double and rounded once to
+ * FP32, which is the correctly rounded FP32 sigmoid for all practical inputs. */
+float oracle_sigmoid(float logit) {
+  return (float)(1.0 / (1.0 + exp(-(double)logit)));
+}
+
+/* SwiGLU's activation: silu(v) = v * sigmoid(v), written v / (1 + e^-v), FP32. */
+float oracle_silu(float v) {
+  return v / (1.0f + expf(-v));
+}
+
+/*
+ * O1 — the sublayer boundary.
+ * [vLLM §MoE und Residual-Stream]: sandwich norm (an RMSNorm before and after
+ *   every sublayer) and the depth-scaled residual: the n-th residual add is
+ *   h <- sqrt((n-1)/n) * h + x / sqrt(n).
+ * [vLLM §Agentengetriebene Optimierung, change 1]: post-norm, scaled residual
+ *   add and next pre-norm fused, FP32 math, the reference's BF16 rounding points.
+ * [SGLang §三明治归一化与深度缩放残差 (sandwich norm and depth-scaled residual)]:
+ *   both scaled operands are rounded to the activation dtype before the add;
+ *   the unfused path writes the normalised branch and reads it back for the
+ *   residual, so the post-norm output is itself a BF16 tensor.
+ * Readings: textbook RMSNorm y = x * 1/sqrt(mean(x^2) + eps) * w with eps
+ *   inside the root and one BF16 rounding of (x*r)*w; the coefficients are
+ *   computed in double and rounded once to FP32; x/sqrt(n) is a multiply by
+ *   the FP32 coefficient 1/sqrt(n).
+ */
+static void rmsnorm_row(int64_t d, const uint16_t* v, const uint16_t* w, float eps,
+                        uint16_t* out) {
+  float ss = 0.0f;
+  for (int64_t i = 0; i < d; ++i) {
+    float a = oracle_f32(v[i]);
+    ss = ss + a * a;
+  }
+  float r = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int64_t i = 0; i < d; ++i)
+    out[i] = oracle_bf16((oracle_f32(v[i]) * r) * oracle_f32(w[i]));
+}
+
+int oracle_boundary(int64_t T, int64_t d, const uint16_t* h, const uint16_t* x,
+                    const uint16_t* w_post, const uint16_t* w_pre, int64_t n, float eps,
+                    uint16_t* h_out, uint16_t* z_out) {
+  if (T < 0 || d <= 0 || n < 1 || !(eps >= 0.0f)) return -1;
+  const float c1 = (float)sqrt((double)(n - 1) / (double)n); /* scales the residual h */
+  const float c2 = (float)(1.0 / sqrt((double)n));           /* scales the branch */
+  uint16_t* xn = (uint16_t*)malloc((size_t)d * sizeof(uint16_t));
+  if (!xn) return -3;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* hr = h + t * d;
+    const uint16_t* xr = x + t * d;
+    uint16_t* ho = h_out + t * d;
+    uint16_t* zo = z_out + t * d;
+    rmsnorm_row(d, xr, w_post, eps, xn); /* post-norm of the branch, rounded */
+    for (int64_t i = 0; i < d; ++i) {
+      uint16_t a = oracle_bf16(c1 * oracle_f32(hr[i])); /* scaled residual, rounded */
+      uint16_t b = oracle_bf16(c2 * oracle_f32(xn[i])); /* scaled branch, rounded */
+      ho[i] = oracle_bf16(oracle_f32(a) + oracle_f32(b));
+    }
+    rmsnorm_row(d, ho, w_pre, eps, zo); /* next sublayer's pre-norm */
+  }
+  free(xn);
+  return 0;
+}
+
+/*
+ * O2 — the FP32 router.
+ * [vLLM §MoE und Residual-Stream]: router weights (5120 x 256), accumulation
+ *   and logits are all FP32.
+ * Readings: the router reads the MoE sublayer's pre-normed input z; W is
+ *   stored [E, d] (output features by input features).
+ */
+int oracle_router(int64_t T, int64_t d, int64_t E, const uint16_t* z, const float* W,
+                  float* logits) {
+  if (T < 0 || d <= 0 || E <= 0) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      for (int64_t i = 0; i < d; ++i) acc = acc + oracle_f32(z[t * d + i]) * W[e * d + i];
+      logits[t * E + e] = acc;
+    }
+  return 0;
+}
+
+/*
+ * O3 — grouped top-k.
+ * [vLLM §MoE und Residual-Stream]: routed as in DeepSeek-V3: sigmoid scores
+ *   plus a correction bias pick the best 4 of 8 expert groups, then the top 8
+ *   experts; the renormalised weights are scaled by 2.5; no shared expert.
+ * [SGLang §稠密层与分组 MoE 路由]: FP32 logits; grouped top-k over sigmoid
+ *   scores and the expert correction bias; FP32 routing coefficients; the
+ *   routing scale may be folded into the routing weights.
+ * Readings: a group's score is the sum of its two largest biased scores
+ *   (DeepSeek-V3's rule; one expert per group -> that expert's score); the bias
+ *   enters selection only, the weights use the unbiased scores; every order is
+ *   (value descending, index ascending), so the selection is unique; the k
+ *   outputs are in that order; the denominator is summed in slot order; the
+ *   scale is applied to each weight.
+ */
+static int better(float va, int64_t ia, float vb, int64_t ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+/* insertion sort of idx[0..m) by (val desc, idx asc) */
+static void sort_desc(int64_t m, int64_t* idx, const float* val) {
+  for (int64_t a = 1; a < m; ++a) {
+    int64_t cur = idx[a];
+    int64_t b = a - 1;
+    while (b >= 0 && better(val[cur], cur, val[idx[b]], idx[b])) {
+      idx[b + 1] = idx[b];
+      --b;
+    }
+    idx[b + 1] = cur;
+  }
+}
+
+int oracle_topk(int64_t T, int64_t E, int64_t G, int64_t kg, int64_t k, float scale,
+                const float* logits, const float* bias, int32_t* ids, float* w, float* ggap,
+                float* egap) {
+  if (T < 0 || E <= 0 || G <= 0 || E % G != 0 || kg < 1 || kg > G || k < 1) return -1;
+  const int64_t gs = E / G;
+  if (k > kg * gs) return -1;
+  float* s = (float*)malloc((size_t)E * sizeof(float));
+  float* c = (float*)malloc((size_t)E * sizeof(float));
+  float* g = (float*)malloc((size_t)G * sizeof(float));
+  int64_t* gi = (int64_t*)malloc((size_t)G * sizeof(int64_t));
+  int64_t* cand = (int64_t*)malloc((size_t)E * sizeof(int64_t));
+  if (!s || !c || !g || !gi || !cand) {
+    free(s); free(c); free(g); free(gi); free(cand);
+    return -3;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    for (int64_t e = 0; e < E; ++e) {
+      s[e] = oracle_sigmoid(l[e]);
+      c[e] = s[e] + bias[e];
+    }
+    /* group scores: sum of the two largest biased scores in the group */
+    for (int64_t j = 0; j < G; ++j) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int64_t q = 0; q < gs; ++q) {
+        float v = c[j * gs + q];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+      }
+      g[j] = (gs >= 2) ? m1 + m2 : m1;
+      gi[j] = j;
+    }
+    sort_desc(G, gi, g);
+    /* candidates: every expert of the kept groups */
+    int64_t m = 0;
+    for (int64_t a = 0; a < kg; ++a)
+      for (int64_t q = 0; q < gs; ++q) cand[m++] = gi[a] * gs + q;
+    sort_desc(m, cand, c);
+    float den = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      ids[t * k + j] = (int32_t)cand[j];
+      den = (j == 0) ? s[cand[0]] : den + s[cand[j]];
+    }
+    for (int64_t j = 0; j < k; ++j) w[t * k + j] = (s[cand[j]] / den) * scale;
+    if (ggap) ggap[t] = (kg < G) ? g[gi[kg - 1]] - g[gi[kg]] : INFINITY;
+    if (egap) {
+      float mg = INFINITY;
+      for (int64_t j = 0; j < k && j + 1 < m; ++j) {
+        float gap = c[cand[j]] - c[cand[j + 1]];
+        if (gap < mg) mg = gap;
+      }
+      egap[t] = mg;
+    }
+  }
+  free(s); free(c); free(g); free(gi); free(cand);
+  return 0;
+}
+
+/*
+ * O4 — expert histogram and stable permutation.
+ * [vLLM §Der fusionierte Graph]: the MoE path runs routing kernels ahead of
+ *   two grouped GEMMs, i.e. the token assignments are grouped by expert. The
+ *   pages do not describe the layout. Reading: rows ordered by expert
+ *   ascending, then by slot index t*k+j ascending (a counting sort).
+ */
+int oracle_permute(int64_t T, int64_t k, int64_t E, const int32_t* ids, int32_t* counts,
+                   int32_t* offsets, int32_t* perm, int32_t* inv) {
+  if (T < 0 || k < 1 || E <= 0) return -1;
+  const int64_t n = T * k;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < n; ++a)
+    if (ids[a] >= 0 && ids[a] < E) counts[ids[a]] += 1;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int64_t* cursor = (int64_t*)malloc((size_t)E * sizeof(int64_t));
+  if (!cursor) return -3;
+  for (int64_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t a = 0; a < n; ++a) perm[a] = -1;
+  for (int64_t a = 0; a < n; ++a) {
+    int32_t e = ids[a];
+    if (e < 0 || e >= E) {
+      inv[a] = -1;
+      continue;
+    }
+    int64_t r = cursor[e]++;
+    perm[r] = (int32_t)a;
+    inv[a] = (int32_t)r;
+  }
+  free(cursor);
+  return 0;
+}
+
+/*
+ * O5 — one routed SwiGLU expert, weighted.
+ * [vLLM §MoE und Residual-Stream]: 256 routed SwiGLU experts, d_ff 2560.
+ * [SGLang §BF16 MoE 内核优化 (BF16 MoE kernel optimisation)]: the decode path
+ *   keeps BF16 rounding boundaries for the gate/up projections and the
+ *   activation, and applies the FP32 routing weight to the down projection's
+ *   output before it is rounded to BF16.
+ * Reading: g and u are each rounded to BF16; act = bf16(silu(g) * u); the down
+ *   projection accumulates in FP32, is multiplied by the FP32 weight, and is
+ *   rounded once.
+ */
+int oracle_expert_rows(int64_t R, int64_t d, int64_t f, const uint16_t* zrows,
+                       const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                       const float* wrow, uint16_t* yk) {
+  if (R < 0 || d <= 0 || f <= 0) return -1;
+  uint16_t* act = (uint16_t*)malloc((size_t)f * sizeof(uint16_t));
+  if (!act) return -3;
+  for (int64_t r = 0; r < R; ++r) {
+    const uint16_t* z = zrows + r * d;
+    for (int64_t q = 0; q < f; ++q) {
+      float ag = 0.0f, au = 0.0f;
+      for (int64_t i = 0; i < d; ++i) {
+        float zi = oracle_f32(z[i]);
+        ag = ag + zi * oracle_f32(Wg[q * d + i]);
+        au = au + zi * oracle_f32(Wu[q * d + i]);
+      }
+      float gq = oracle_f32(oracle_bf16(ag));
+      float uq = oracle_f32(oracle_bf16(au));
+      act[q] = oracle_bf16(oracle_silu(gq) * uq);
+    }
+    for (int64_t o = 0; o < d; ++o) {
+      float acc = 0.0f;
+      for (int64_t q = 0; q < f; ++q) acc = acc + oracle_f32(act[q]) * oracle_f32(Wd[o * f + q]);
+      yk[r * d + o] = oracle_bf16(wrow[r] * acc);
+    }
+  }
+  free(act);
+  return 0;
+}
+
+/*
+ * O6 — the weighted top-k combine.
+ * [vLLM §Agentengetriebene Optimierung, change 3]: after the MoE, the norm
+ *   kernel also combines the top-8 expert outputs.
+ * [SGLang, kernel-fusion paragraph]: the BF16 MoE path merges the local expert
+ *   sum, the routing scale and the BF16 rounding.
+ * Reading: per token, an FP32 sum of the k BF16 expert rows in slot order,
+ *   rounded once. The sum starts from -0.0, the exact additive identity.
+ */
+int oracle_combine(int64_t T, int64_t k, int64_t d, int64_t E, const int32_t* ids,
+                   const uint16_t* yk, uint16_t* y) {
+  if (T < 0 || k < 1 || d <= 0) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t o = 0; o < d; ++o) {
+      float acc = -0.0f;
+      for (int64_t j = 0; j < k; ++j) {
+        if (ids && (ids[t * k + j] < 0 || ids[t * k + j] >= E)) continue;
+        acc = acc + oracle_f32(yk[(t * k + j) * d + o]);
+      }
+      y[t * d + o] = oracle_bf16(acc);
+    }
+  return 0;
+}

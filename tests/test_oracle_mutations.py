@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that the
+pins in test_oracle_pins.py catch every one of them."""
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTATIONS = [
+    ("swap residual coefficients", "uint16_t a = oracle_bf16(c1 *", "uint16_t a = oracle_bf16(c2 *"),
+    ("coefficient without root", "(float)sqrt((double)(n - 1) / (double)n)", "(float)((double)(n - 1) / (double)n)"),
+    ("eps outside the root", "1.0f / sqrtf(ss / (float)d + eps)", "1.0f / (sqrtf(ss / (float)d) + eps)"),
+    ("sum instead of mean", "1.0f / sqrtf(ss / (float)d + eps)", "1.0f / sqrtf(ss + eps)"),
+    ("norm weight dropped", "* oracle_f32(w[i]));", ");"),
+    ("operands not rounded", "ho[i] = oracle_bf16(oracle_f32(a) + oracle_f32(b));",
+     "ho[i] = oracle_bf16(c1 * oracle_f32(hr[i]) + c2 * oracle_f32(xn[i]));"),
+    ("router transposed", "* W[e * d + i]", "* W[(i % E) * d + (i / E) % d]"),
+    ("router in bf16", "acc = acc + oracle_f32(z[t * d + i]) * W[e * d + i];",
+     "acc = oracle_f32(oracle_bf16(acc + oracle_f32(z[t * d + i]) * W[e * d + i]));"),
+    ("sigmoid sign", "exp(-(double)logit)", "exp((double)logit)"),
+    ("group score = max", "g[j] = (gs >= 2) ? m1 + m2 : m1;", "g[j] = m1;"),
+    ("bias enters weights", "w[t * k + j] = (s[cand[j]] / den) * scale;",
+     "w[t * k + j] = (c[cand[j]] / den) * scale;"),
+    ("tie-break upward", "(va == vb && ia < ib)", "(va == vb && ia > ib)"),
+    ("scale dropped", "w[t * k + j] = (s[cand[j]] / den) * scale;", "w[t * k + j] = (s[cand[j]] / den);"),
+    ("permutation unstable", "for (int64_t a = 0; a < n; ++a) {\n    int32_t e = ids[a];",
+     "for (int64_t a = n - 1; a >= 0; --a) {\n    int32_t e = ids[a];"),
+    ("down weight transposed", "Wd[o * f + q]", "Wd[(q % d) * f + (o % f)]"),
+    ("gate and up swapped", "oracle_silu(gq) * uq", "oracle_silu(uq) * gq"),
+    ("weight after rounding", "yk[r * d + o] = oracle_bf16(wrow[r] * acc);",
+     "yk[r * d + o] = oracle_bf16(wrow[r] * oracle_f32(oracle_bf16(acc)));"),
+    ("combine rounds each add", "acc = acc + oracle_f32(yk[(t * k + j) * d + o]);",
+     "acc = oracle_f32(oracle_bf16(acc + oracle_f32(yk[(t * k + j) * d + o])));"),
+]
+
+PIN_TESTS = [(name, fn) for name, fn in inspect.getmembers(pins, inspect.isfunction)
+             if name.startswith("test_")]
+
+
+def _run_pins(golden):
+    failed = []
+    for name, fn in PIN_TESTS:
+        params = inspect.signature(fn).parameters
+        kwargs = {}
+        if "golden" in params:
+            kwargs["golden"] = golden
+        if "E" in params:  # the parametrised brute-force test: use one size
+            kwargs["E"] = 8
+        try:
+            fn(**kwargs)
+        except Exception:  # AssertionError or an error raised by a mutant
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(label, old, new, tmp_path, golden):
+    src = open(oracle.SRC_PATH).read()
+    assert src.count(old) >= 1, label
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mut.c"
+    c_path.write_text(mutated)
+    hdr = os.path.join(os.path.dirname(oracle.SRC_PATH), "beam_oracle.h")
+    (tmp_path / "beam_oracle.h").write_text(open(hdr).read())
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                           str(c_path), "-o", str(so), "-lm"])
+    saved_lib, saved_path = oracle._lib, oracle.LIB_PATH
+    try:
+        oracle._lib = None
+        oracle.LIB_PATH = str(so)
+        failed = _run_pins(golden)
+    finally:
+        oracle._lib, oracle.LIB_PATH = saved_lib, saved_path
+    assert failed, f"no pin caught the mutation '{label}'"
+
+
+def test_unmutated_oracle_passes_all_pins(golden):
+    assert _run_pins(golden) == []

@@ -1,0 +1,531 @@
+"""Pins for the CPU oracle: what the pages and plain mathematics fix, checked
+without re-typing the oracle's formulas.
+
+Each oracle step is pinned by closed forms on special inputs, invariants the
+pages state, brute-force enumeration on tiny sizes, or error bounds against an
+FP64 computation, chosen so that a dropped term, a wrong sign or index, a swapped
+coefficient or a transposed operand fails at least one test (the "mutation"
+test at the bottom plants such mistakes in a copy of the oracle and checks that
+the pins catch them).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+F = oracle.bf16_to_f32
+
+
+def to_bf16(a):
+    """numpy RNE float32 -> bf16 bits (test-side helper for building inputs)."""
+    a = np.asarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------------------------
+# scalar pieces
+
+def test_bf16_rne_golden(golden):
+    for case in golden["bf16_rne"]["cases"]:
+        f = np.array([int(case["f32_bits"], 16)], dtype=np.uint32).view(np.float32)[0]
+        assert oracle.bf16(float(f)) == int(case["bf16_bits"], 16), case
+
+
+def test_bf16_widen_exact():
+    bits = np.arange(0, 1 << 16, 7, dtype=np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    for b in bits[finite][:2000]:
+        assert oracle.bf16(oracle.f32(int(b))) == int(b)
+
+
+def test_sigmoid_golden(golden):
+    for case in golden["sigmoid"]["cases"]:
+        s = oracle.sigmoid(np.float32(case["logit"]))
+        ulp = np.spacing(np.float32(case["score"]))
+        assert abs(s - case["score"]) <= case["ulps"] * ulp + 0.0, case
+
+
+def test_sigmoid_symmetry_and_range():
+    xs = np.linspace(-30, 30, 2001, dtype=np.float32)
+    s = np.array([oracle.sigmoid(v) for v in xs])
+    sm = np.array([oracle.sigmoid(-v) for v in xs])
+    assert np.all(np.diff(s) >= 0)
+    assert np.all((s >= 0) & (s <= 1))
+    assert np.max(np.abs(s + sm - 1.0)) <= 2 * 2.0 ** -24
+
+
+def test_silu_identities():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(40.0) == 40.0
+    for v in np.linspace(-8, 8, 161, dtype=np.float32):
+        # silu(-v) = silu(v) - v and silu(v) = v * sigmoid(v)
+        assert abs(oracle.silu(-v) - (oracle.silu(v) - v)) <= 4e-6 * max(1.0, abs(v))
+        assert abs(oracle.silu(v) - v * oracle.sigmoid(v)) <= 4e-6 * max(1.0, abs(v))
+
+
+# ---------------------------------------------------------------------------------------------
+# O1 boundary
+
+def _rows(T, d, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return to_bf16(rng.standard_normal((T, d)).astype(np.float32) * scale)
+
+
+def test_boundary_n1_is_postnorm(golden):
+    """n = 1: sqrt(0) * h + x / 1 -> h' is the post-normed branch and ignores h."""
+    d = 256
+    x = _rows(4, d, 1)
+    w = to_bf16(np.linspace(0.9, 1.1, d))
+    h1 = _rows(4, d, 2)
+    h2 = _rows(4, d, 3)
+    a, za = oracle.boundary(h1, x, w, w, 1, 1e-6)
+    b, zb = oracle.boundary(h2, x, w, w, 1, 1e-6)
+    assert np.array_equal(a, b) and np.array_equal(za, zb)
+    # and h' = xn: post-norm of x with w -> check against the constant-row closed form below
+    xc = np.full((1, d), to_bf16(np.float32(1.5)), dtype=np.uint16)
+    hc, _ = oracle.boundary(np.zeros_like(xc), xc, w, w, 1, 0.0)
+    assert np.array_equal(hc[0], w)
+
+
+def test_boundary_constant_row_closed_form():
+    """A constant branch row c with eps = 0 normalises to sign(c) * w_post exactly."""
+    d = 512
+    w_post = to_bf16(np.random.default_rng(0).uniform(0.9, 1.1, d))
+    w_pre = to_bf16(np.random.default_rng(1).uniform(0.9, 1.1, d))
+    ones = to_bf16(np.ones(d))
+    for c in (1.5, -1.5, 3.0, 0.75):
+        x = np.full((1, d), to_bf16(np.float32(c)), dtype=np.uint16)
+        # n = 4: c2 = 1/2 exactly; h = 0 -> h' = bf16(0.5 * xn) = 0.5 * sign(c) * w_post (exact)
+        hp, z = oracle.boundary(np.zeros((1, d), np.uint16), x, w_post, w_pre, 4, 0.0)
+        assert np.array_equal(F(hp[0]), np.float32(0.5) * np.sign(c) * F(w_post))
+        # with w_post = 1 the next norm sees a constant row +-0.5 -> z = sign(c) * w_pre
+        hp, z = oracle.boundary(np.zeros((1, d), np.uint16), x, ones, w_pre, 4, 0.0)
+        assert np.array_equal(F(z[0]), np.sign(c) * F(w_pre))
+
+
+def test_boundary_coefficients_golden(golden):
+    """x = 0 isolates the residual scale: h' = bf16(c1 * h); h = 0 isolates the branch scale."""
+    d = 64
+    h = to_bf16(np.linspace(-4, 4, d)).reshape(1, d)
+    ones = to_bf16(np.ones(d))
+    for case in golden["depth_scaled_residual"]["cases"]:
+        n, c1, c2 = case["n"], case["c1"], case["c2"]
+        assert abs(c1 * c1 + c2 * c2 - 1.0) < 1e-11  # the unit-variance identity
+        hp, _ = oracle.boundary(h, np.zeros((1, d), np.uint16), ones, ones, n, 1e-6)
+        # the oracle multiplies by FP32(c1) and rounds twice (operand, then sum with +0)
+        want = F(to_bf16(np.float32(c1) * F(h[0])))
+        assert np.array_equal(F(hp[0]), want), n
+        # branch scale: constant x row of 1.5 normalises to exactly w (= 1) with eps = 0
+        x = np.full((1, d), to_bf16(np.float32(1.5)), dtype=np.uint16)
+        hp, _ = oracle.boundary(np.zeros((1, d), np.uint16), x, ones, ones, n, 0.0)
+        assert np.all(F(hp[0]) == F(to_bf16(np.float32(c2)))), n
+
+
+def test_boundary_eps_inside_root():
+    """A tiny constant row v with eps: xn = w * v / sqrt(v^2 + eps) (eps inside the root)."""
+    d = 128
+    v = float(F(to_bf16(np.float32(1e-3))))
+    x = np.full((1, d), to_bf16(np.float32(v)), dtype=np.uint16)
+    ones = to_bf16(np.ones(d))
+    hp, _ = oracle.boundary(np.zeros((1, d), np.uint16), x, ones, ones, 1, 1e-6)
+    want = v / math.sqrt(v * v + 1e-6)
+    assert abs(F(hp[0])[0] - want) <= 2.0 ** -8 * want
+
+
+def test_boundary_scale_invariance():
+    """Doubling the branch (eps = 0) changes nothing; doubling w_pre doubles z exactly."""
+    d = 256
+    x = _rows(6, d, 4)
+    h = _rows(6, d, 5)
+    w = to_bf16(np.random.default_rng(2).uniform(0.9, 1.1, d))
+    a, za = oracle.boundary(h, x, w, w, 20, 0.0)
+    x2 = to_bf16(F(x) * 2)
+    b, zb = oracle.boundary(h, x2, w, w, 20, 0.0)
+    assert np.array_equal(a, b) and np.array_equal(za, zb)
+    w2 = to_bf16(F(w) * 2)
+    c, zc = oracle.boundary(h, x, w, w2, 20, 0.0)
+    assert np.array_equal(c, a) and np.array_equal(F(zc), 2 * F(za))
+
+
+def test_boundary_unit_variance_invariant():
+    """With unit-variance h and x, and unit norm weights, h' keeps unit variance."""
+    T, d = 1024, 1024
+    h = _rows(T, d, 6)
+    x = _rows(T, d, 7)
+    ones = to_bf16(np.ones(d))
+    for n in (2, 20):
+        hp, z = oracle.boundary(h, x, ones, ones, n, 1e-6)
+        v = float(np.mean(F(hp).astype(np.float64) ** 2))
+        N = T * d
+        assert abs(v - 1.0) < 5 * math.sqrt(2.0 / N) + 2e-3, (n, v)
+        # the next pre-norm makes every row's mean square 1 (up to BF16 rounding)
+        ms = np.mean(F(z).astype(np.float64) ** 2, axis=1)
+        assert np.all(np.abs(ms - 1.0) < 4e-3)
+
+
+def test_boundary_rejects_bad_args():
+    d = 8
+    h = np.zeros((1, d), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.boundary(h, h, h[0], h[0], 0, 1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# O2 router
+
+def test_router_one_hot_rows_pick_entries():
+    """W[e] = one-hot at pi(e) -> logits[:, e] = z[:, pi(e)] exactly (catches a transpose)."""
+    T, d, E = 5, 96, 40
+    z = _rows(T, d, 8)
+    pi = np.random.default_rng(3).permutation(d)[:E]
+    W = np.zeros((E, d), np.float32)
+    W[np.arange(E), pi] = 1.0
+    lg = oracle.router(z, W)
+    assert np.array_equal(lg, F(z)[:, pi])
+
+
+def test_router_exact_small_integers():
+    T, d, E = 7, 128, 24
+    rng = np.random.default_rng(9)
+    zi = rng.integers(-8, 9, (T, d))
+    Wi = rng.integers(-16, 17, (E, d))
+    lg = oracle.router(to_bf16(zi.astype(np.float32)), Wi.astype(np.float32))
+    assert np.array_equal(lg.astype(np.int64), zi @ Wi.T)
+
+
+def test_router_fp32_error_bound():
+    """Sequential FP32 accumulation: |l - exact| <= gamma_d * sum |z W| (Higham 3.1)."""
+    T, d, E = 4, 5120, 16
+    z = _rows(T, d, 10)
+    W = (np.random.default_rng(11).standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    lg = oracle.router(z, W)
+    zf = F(z).astype(np.float64)
+    exact = zf @ W.astype(np.float64).T
+    mag = np.abs(zf) @ np.abs(W.astype(np.float64)).T
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    assert np.all(np.abs(lg - exact) <= gamma * mag)
+    # and it is FP32, not a lower precision: typical error far below a BF16 rounding
+    assert np.max(np.abs(lg - exact)) < 1e-4
+
+
+# ---------------------------------------------------------------------------------------------
+# O3 grouped top-k
+
+def _brute_topk(logit_row, bias, G, kg, k, scale):
+    """Enumerate every kept-group subset and expert subset; keep the one that
+    dominates under (value desc, index asc). Independent of the oracle's sort."""
+    E = len(logit_row)
+    gs = E // G
+    s = np.array([oracle.sigmoid(v) for v in logit_row], dtype=np.float32)
+    c = (s + bias).astype(np.float32)
+
+    def beats(va, ia, vb, ib):
+        return va > vb or (va == vb and ia < ib)
+
+    g = []
+    for j in range(G):
+        mem = c[j * gs:(j + 1) * gs]
+        if gs == 1:
+            g.append(np.float32(mem[0]))
+        else:  # best pair sum = sum of the two largest
+            g.append(max(np.float32(mem[a] + mem[b]) for a in range(gs) for b in range(gs) if a != b))
+    good_groups = []
+    for S in itertools.combinations(range(G), kg):
+        rest = [j for j in range(G) if j not in S]
+        if all(beats(g[a], a, g[b], b) for a in S for b in rest):
+            good_groups.append(S)
+    assert len(good_groups) == 1
+    cand = [j * gs + q for j in good_groups[0] for q in range(gs)]
+    good = []
+    for K in itertools.combinations(cand, k):
+        rest = [e for e in cand if e not in K]
+        if all(beats(c[a], a, c[b], b) for a in K for b in rest):
+            good.append(K)
+    assert len(good) == 1
+    ids = sorted(good[0], key=lambda e: (-float(c[e]), e))
+    den = np.float32(0)
+    for j, e in enumerate(ids):
+        den = s[e] if j == 0 else np.float32(den + s[e])
+    w = [np.float32(np.float32(s[e] / den) * np.float32(scale)) for e in ids]
+    return np.array(ids, np.int32), np.array(w, np.float32)
+
+
+@pytest.mark.parametrize("E", [4, 6, 8, 12])
+def test_topk_brute_force(E):
+    rng = np.random.default_rng(E)
+    for G in [g for g in range(1, E + 1) if E % g == 0]:
+        gs = E // G
+        for kg in range(1, G + 1):
+            for k in range(1, min(kg * gs, 6) + 1):
+                for trial in range(2):
+                    lg = rng.standard_normal((1, E)).astype(np.float32)
+                    if trial == 1:  # forced ties: quantised logits, zero bias
+                        lg = np.round(lg * 2) / 2
+                        bias = np.zeros(E, np.float32)
+                    else:
+                        bias = rng.uniform(-0.01, 0.01, E).astype(np.float32)
+                    ids, w, _, _ = oracle.topk(lg, bias, G, kg, k, 2.5)
+                    bi, bw = _brute_topk(lg[0], bias, G, kg, k, 2.5)
+                    assert np.array_equal(ids[0], bi), (E, G, kg, k, trial)
+                    assert np.array_equal(w[0], bw), (E, G, kg, k, trial)
+
+
+def test_topk_weights_sum_to_scale():
+    E, G, kg, k = 256, 8, 4, 8
+    rng = np.random.default_rng(12)
+    lg = rng.standard_normal((500, E)).astype(np.float32)
+    bias = rng.uniform(-0.01, 0.01, E).astype(np.float32)
+    ids, w, _, _ = oracle.topk(lg, bias, G, kg, k, 2.5)
+    sums = w.astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(sums - 2.5) <= 4 * np.spacing(np.float32(2.5)))
+    # distinct ids, each row's ids from at most kg groups
+    for row in ids:
+        assert len(set(row.tolist())) == k
+        assert len(set((row // (E // G)).tolist())) <= kg
+
+
+def test_topk_single_group_is_plain_topk():
+    E, k = 64, 8
+    rng = np.random.default_rng(13)
+    lg = rng.standard_normal((50, E)).astype(np.float32)
+    bias = rng.uniform(-0.01, 0.01, E).astype(np.float32)
+    ids, _, _, _ = oracle.topk(lg, bias, 1, 1, k, 2.5)
+    for t in range(50):
+        s = np.array([oracle.sigmoid(v) for v in lg[t]], np.float32)
+        c = (s + bias).astype(np.float32)
+        order = np.lexsort((np.arange(E), -c.astype(np.float64)))
+        assert np.array_equal(ids[t], order[:k])
+
+
+def test_topk_all_experts_is_dense_softmax_free_mixture():
+    """kg = G, k = E: every expert selected; w = s / sum(s) * scale in c order."""
+    E, G = 16, 4
+    rng = np.random.default_rng(14)
+    lg = rng.standard_normal((3, E)).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    ids, w, _, _ = oracle.topk(lg, bias, G, G, E, 2.5)
+    for t in range(3):
+        assert sorted(ids[t].tolist()) == list(range(E))
+        s = np.array([oracle.sigmoid(v) for v in lg[t]], np.float64)
+        assert np.allclose(w[t], s[ids[t]] / s.sum() * 2.5, rtol=1e-6)
+
+
+def test_topk_bias_selects_but_does_not_weight():
+    """A large bias forces a low-score expert in; its weight still uses its unbiased score."""
+    E, G, kg, k = 8, 1, 1, 2
+    lg = np.array([[3.0, 2.0, 1.0, 0.0, -1.0, -2.0, -3.0, -4.0]], np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[7] = 1.0
+    ids, w, _, _ = oracle.topk(lg, bias, G, kg, k, 2.5)
+    assert ids[0].tolist() == [7, 0]  # c7 = sigmoid(-4) + 1 = 1.018 > c0 = 0.953
+    s7, s0 = oracle.sigmoid(-4.0), oracle.sigmoid(3.0)
+    assert abs(w[0][0] - s7 / (s7 + s0) * 2.5) < 1e-6
+    assert abs(w[0][1] - s0 / (s7 + s0) * 2.5) < 1e-6
+
+
+def test_topk_group_score_is_top2_sum():
+    """Group A: one strong expert; group B: two good ones. Top-2 sum prefers B,
+    a max rule would prefer A, a sum over the whole group would prefer C."""
+    # 3 groups of 4 experts, keep 1 group, pick 1 expert
+    E, G = 12, 3
+    s_target = {0: 0.95, 1: 0.10, 2: 0.10, 3: 0.10,   # A: max 0.95, top2 1.05, all 1.25
+                4: 0.60, 5: 0.58, 6: 0.05, 7: 0.05,   # B: max 0.60, top2 1.18, all 1.28
+                8: 0.40, 9: 0.40, 10: 0.40, 11: 0.40}  # C: max 0.40, top2 0.80, all 1.60
+    lg = np.array([[math.log(p / (1 - p)) for p in (s_target[e] for e in range(E))]], np.float32)
+    ids, _, _, _ = oracle.topk(lg, np.zeros(E, np.float32), G, 1, 1, 2.5)
+    assert ids[0].tolist() == [4]
+
+
+def test_topk_gaps_report_near_ties():
+    E, G, kg, k = 16, 4, 2, 3
+    lg = np.zeros((1, E), np.float32)  # all equal: every gap is zero
+    ids, w, ggap, egap = oracle.topk(lg, np.zeros(E, np.float32), G, kg, k, 2.5)
+    assert ggap[0] == 0 and egap[0] == 0
+    assert ids[0].tolist() == [0, 1, 2]  # lower index wins every tie
+    # w = (s / den) * scale with each step rounded to FP32: (0.5 / 1.5) * 2.5
+    assert np.all(w[0] == np.float32(np.float32(np.float32(0.5) / np.float32(1.5)) * np.float32(2.5)))
+
+
+# ---------------------------------------------------------------------------------------------
+# O4 permutation
+
+def test_permute_matches_brute_force_sort():
+    rng = np.random.default_rng(15)
+    for T, k, E in [(1, 8, 256), (37, 8, 32), (200, 4, 16), (3, 2, 5)]:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        counts, offsets, perm, inv = oracle.permute(ids, E)
+        pairs = sorted((int(ids.ravel()[a]), a) for a in range(T * k))
+        assert perm.tolist() == [a for _, a in pairs]
+        assert counts.tolist() == np.bincount(ids.ravel(), minlength=E).tolist()
+        assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) >= 0)
+        assert np.array_equal(inv[perm], np.arange(T * k))
+
+
+def test_permute_skips_invalid_ids():
+    ids = np.array([[0, 5, -1], [2, 9, 0]], np.int32)  # E = 6: -1 and 9 are invalid
+    counts, offsets, perm, inv = oracle.permute(ids, 6)
+    assert counts.tolist() == [2, 0, 1, 0, 0, 1]
+    assert perm.tolist() == [0, 5, 3, 1, -1, -1]
+    assert inv.tolist() == [0, 3, -1, 2, -1, 1]
+
+
+# ---------------------------------------------------------------------------------------------
+# O5 / O6 experts and combine
+
+def _perm_matrix(rows, cols, pi, val):
+    M = np.zeros((rows, cols), np.float32)
+    M[np.arange(rows), pi] = val
+    return to_bf16(M)
+
+
+def test_expert_permutation_closed_form():
+    """Wg = 2 P_g, Wu = 0.5 P_u, Wd = P_d (one-hot rows): every sum has one
+    non-zero term, so y_o = bf16(w * act[pd(o)]) with
+    act_q = bf16(silu(2 z[pg(q)]) * 0.5 z[pu(q)]). A transposed operand reads
+    the inverse permutation and fails."""
+    d = f = 64
+    rng = np.random.default_rng(16)
+    pg, pu, pd = rng.permutation(f), rng.permutation(f), rng.permutation(d)
+    Wg = _perm_matrix(f, d, pg, 2.0)
+    Wu = _perm_matrix(f, d, pu, 0.5)
+    Wd = _perm_matrix(d, f, pd, 1.0)
+    z = _rows(3, d, 17)
+    wrow = np.array([2.5, 0.75, 1.0], np.float32)
+    yk = oracle.expert_rows(z, Wg, Wu, Wd, wrow)
+    zf = F(z).astype(np.float64)
+    for r in range(3):
+        g = 2.0 * zf[r, pg]
+        u = 0.5 * zf[r, pu]
+        act = F(to_bf16((g / (1.0 + np.exp(-g)) * u).astype(np.float32)))
+        want = F(to_bf16((wrow[r] * act[pd]).astype(np.float32)))
+        got = F(yk[r])
+        # silu differs from the FP64 form only at FP32 rounding -> at most one BF16 step
+        step = np.spacing(np.maximum(np.abs(want), 1e-30).astype(np.float32)) * 65536
+        assert np.all(np.abs(got - want) <= step), r
+        assert np.mean(got == want) > 0.97
+
+
+def _dense_swiglu_fp64(z, Wg, Wu, Wd, w):
+    """Independent FP64 dense SwiGLU with the BF16 rounding points (test-side)."""
+    zf = F(z).astype(np.float64)
+    g = F(to_bf16((zf @ F(Wg).astype(np.float64).T).astype(np.float32)))
+    u = F(to_bf16((zf @ F(Wu).astype(np.float64).T).astype(np.float32)))
+    gd = g.astype(np.float64)
+    act = F(to_bf16((gd / (1.0 + np.exp(-gd)) * u).astype(np.float32)))
+    dn = act.astype(np.float64) @ F(Wd).astype(np.float64).T
+    return F(to_bf16((w[:, None] * dn).astype(np.float32)))
+
+
+def test_one_expert_is_dense_swiglu_times_scale():
+    """E = G = k = 1: the weight is s/s * 2.5 = 2.5 exactly, the output a dense SwiGLU x 2.5."""
+    d, f, T = 128, 96, 6
+    rng = np.random.default_rng(18)
+    z = _rows(T, d, 19)
+    Wg = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wu = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wd = to_bf16(rng.standard_normal((d, f)) * 0.1)
+    lg = rng.standard_normal((T, 1)).astype(np.float32)
+    ids, w, _, _ = oracle.topk(lg, np.zeros(1, np.float32), 1, 1, 1, 2.5)
+    assert np.all(ids == 0) and np.all(w == np.float32(2.5))
+    y, _ = oracle.moe_experts(z, ids, w, 1, lambda e: (Wg, Wu, Wd))
+    want = _dense_swiglu_fp64(z, Wg, Wu, Wd, np.full(T, 2.5))
+    got = F(y)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert rel < 2e-3
+    assert np.mean(got == want) > 0.95  # identical except rare FP32-vs-FP64 rounding flips
+
+
+def test_all_experts_is_dense_mixture():
+    """k = E: y = bf16(sum_e bf16(w_e * D_e(z))) in selection order."""
+    d, f, E, G, T = 64, 64, 4, 2, 3
+    rng = np.random.default_rng(20)
+    Ws = [(to_bf16(rng.standard_normal((f, d)) * 0.1), to_bf16(rng.standard_normal((f, d)) * 0.1),
+           to_bf16(rng.standard_normal((d, f)) * 0.1)) for _ in range(E)]
+    z = _rows(T, d, 21)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w, _, _ = oracle.topk(lg, np.zeros(E, np.float32), G, G, E, 2.5)
+    y, _ = oracle.moe_experts(z, ids, w, E, lambda e: Ws[e])
+    for t in range(T):
+        acc = np.float32(-0.0)
+        for j in range(E):
+            e = ids[t, j]
+            part = _dense_swiglu_fp64(z[t:t + 1], *Ws[e], np.array([w[t, j]], np.float64))[0]
+            acc = (acc + part).astype(np.float32)
+        want = F(to_bf16(acc))
+        got = F(y[t])
+        assert np.linalg.norm(got - want) / np.linalg.norm(want) < 2e-3
+        assert np.mean(got == want) > 0.9
+
+
+def test_combine_slot_order_and_invalid_slots():
+    """FP32 sum in slot order, one rounding; invalid slots are skipped."""
+    big, small = 256.0, 1.0  # 256 + 1 is exact in FP32; rounding only at the end
+    yk = to_bf16(np.array([[[big], [small], [small], [-big]]], np.float32))
+    y = oracle.combine(yk)
+    assert F(y)[0, 0] == 2.0
+    ids = np.array([[0, 1, 9, 2]], np.int32)  # slot 2 invalid for E = 4
+    y2 = oracle.combine(yk, ids, 4)
+    assert F(y2)[0, 0] == 1.0
+    # all-negative-zero rows stay -0 (the sum starts from -0.0)
+    yz = np.full((1, 3, 1), 0x8000, np.uint16)
+    assert oracle.combine(yz)[0, 0] == 0x8000
+
+
+def test_boundary_operands_rounded_before_add():
+    """[SGLang, sandwich norm section] both scaled operands are rounded to BF16
+    before the add. Pick h where bf16(c1*h) + b rounds differently from
+    c1*h + b, so an implementation that adds unrounded operands fails."""
+    n = 20
+    c1 = np.float32(math.sqrt(19 / 20))
+    d = 64
+    # x row constant 1.5 with eps = 0 -> xn = w_post exactly; w_post = 1 -> b = bf16(c2)
+    ones = to_bf16(np.ones(d))
+    x = np.full((1, d), to_bf16(np.float32(1.5)), dtype=np.uint16)
+    b = F(to_bf16(np.float32(1.0 / math.sqrt(20))))
+    cand = to_bf16(np.linspace(0.5, 8.0, 20000).astype(np.float32))
+    hv = F(cand)
+    rounded = F(to_bf16(F(to_bf16(c1 * hv)) + b))
+    unrounded = F(to_bf16((c1 * hv).astype(np.float32) + b))
+    pick = np.nonzero(rounded != unrounded)[0]
+    assert len(pick) >= d
+    h = cand[pick[:d]].reshape(1, d)
+    hp, _ = oracle.boundary(h, x, ones, ones, n, 0.0)
+    assert np.array_equal(F(hp[0]), rounded[pick[:d]])
+
+
+def test_expert_weight_applied_before_rounding():
+    """[SGLang, BF16 MoE kernel section] the FP32 routing weight multiplies the
+    down projection's FP32 output before its BF16 rounding. Two-term down sums
+    make the difference visible: y = bf16(w * (act_a + act_b)), exact in FP32."""
+    d = f = 32
+    rng = np.random.default_rng(22)
+    pg, pu = rng.permutation(f), rng.permutation(f)
+    Wg = _perm_matrix(f, d, pg, 1.0)
+    Wu = _perm_matrix(f, d, pu, 1.0)
+    Wd = np.zeros((d, f), np.float32)
+    a_idx, b_idx = rng.permutation(f), rng.permutation(f)
+    b_idx = np.where(b_idx == a_idx, (b_idx + 1) % f, b_idx)
+    Wd[np.arange(d), a_idx] = 1.0
+    Wd[np.arange(d), b_idx] = 1.0
+    Wd = to_bf16(Wd)
+    z = _rows(2, d, 23)
+    wrow = np.array([2.5, 1.25], np.float32)
+    yk = oracle.expert_rows(z, Wg, Wu, Wd, wrow)
+    for r in range(2):
+        g = F(z[r])[pg].astype(np.float32)
+        u = F(z[r])[pu].astype(np.float32)
+        act = np.array([oracle.f32(oracle.bf16(oracle.silu(gv) * uv)) for gv, uv in zip(g, u)],
+                       np.float32)
+        s = (act[a_idx] + act[b_idx]).astype(np.float32)  # exact: both BF16 of similar size
+        want = F(to_bf16((np.float32(wrow[r]) * s).astype(np.float32)))
+        alt = F(to_bf16((np.float32(wrow[r]) * F(to_bf16(s))).astype(np.float32)))
+        assert np.array_equal(F(yk[r]), want)
+        assert not np.array_equal(want, alt)  # the case does tell the two readings apart
