@@ -1,0 +1,186 @@
+/*
+ * beam_moe.h — C ABI of the Beam sparse-decoder MoE sublayer for MI355X (gfx950).
+ *
+ * One library, libbeam_moe.so, built from hand-written HIP kernels. It computes
+ * one sublayer boundary (post-RMSNorm -> depth-scaled residual -> next
+ * pre-RMSNorm) and the routed MoE FFN that follows it (FP32 router, sigmoid
+ * scores + correction bias, grouped top-k, BF16 SwiGLU experts, FP32 weighted
+ * combine), on one GPU.
+ *
+ * Sources, cited by page title and section:
+ *   [vLLM]   "Serving Reflection Beam auf vLLM ab Tag 0"
+ *   [SGLang] "SGLang 支撑编程模型 Beam 生产部署" (SGLang powers Beam in production)
+ *
+ * Conventions shared by every entry point:
+ *   - BF16 tensors are passed as uint16_t* holding bit patterns; FP32 as float*.
+ *   - Every array argument is DEVICE memory owned by the caller, row-major and
+ *     contiguous, 16-byte aligned. The library never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Compute calls only enqueue work on it and return; BEAM_OK means
+ *     "validated and enqueued". Device-side faults surface at the caller's next
+ *     synchronisation. beam_moe_init and beam_moe_destroy synchronise.
+ *   - All arguments are validated on the host before any HIP call; a call that
+ *     returns an error has enqueued nothing and written nothing.
+ *   - Non-finite inputs give unspecified (but in-bounds) results.
+ *   - Compute calls allocate nothing, so they can be captured in a HIP graph.
+ *   - A handle must not be used by two streams at the same time (its
+ *     workspace is shared by its calls).
+ *   - No exception or signal crosses the ABI.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  BEAM_OK = 0,
+  BEAM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scalar */
+  BEAM_ERR_UNSUPPORTED = -2, /* a shape this build does not implement */
+  BEAM_ERR_OOM = -3,         /* device allocation failed (init only) */
+  BEAM_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  BEAM_ERR_CAPACITY = -5     /* T larger than the handle's max_tokens */
+};
+
+/* Layer shape, fixed at init.
+ * [vLLM §MoE und Residual-Stream]: Beam uses hidden 5120, 256 routed experts
+ * in 8 groups, best 4 groups then top 8 experts, d_ff 2560, scale 2.5.
+ * Supported here: hidden % 256 == 0 and hidden <= 16384; d_ff % 256 == 0 and
+ * d_ff <= 16384; n_experts <= 256 and a multiple of n_groups; n_groups <= 64;
+ * 1 <= topk_groups <= n_groups; 1 <= topk <= min(32, topk_groups * E/G);
+ * 1 <= max_tokens and max_tokens * topk < 2^31; routed_scale finite. */
+typedef struct {
+  int32_t hidden;      /* d */
+  int32_t n_experts;   /* E */
+  int32_t n_groups;    /* G */
+  int32_t topk_groups; /* kg: groups kept per token */
+  int32_t topk;        /* k: experts per token */
+  int32_t d_ff;        /* f: expert intermediate size */
+  int32_t max_tokens;  /* largest T any compute call on this handle may use */
+  float routed_scale;  /* multiplies the renormalised routing weights */
+} beam_moe_config;
+
+typedef struct beam_moe_ctx* beam_moe_handle;
+
+/*
+ * beam_moe_init — create a handle for one MoE layer.
+ * Inputs (device memory, read during the call only):
+ *   router_w    [E, d] FP32   router weight, row e = expert e's logit weights
+ *   router_bias [E]    FP32   per-expert correction bias (selection only)
+ *   w_gate, w_up [E, f, d] BF16   expert gate / up projections (row q = output q)
+ *   w_down      [E, d, f] BF16    expert down projections (row o = output o)
+ * The weights are copied and repacked into handle-owned device memory laid out
+ * for the kernels (about the same size again), and all workspace for
+ * max_tokens is allocated here. The caller may free its copies after return.
+ * [vLLM §MoE und Residual-Stream]: router weights, accumulation and logits
+ * are FP32. Returns BEAM_ERR_UNSUPPORTED for shapes outside the list above,
+ * BEAM_ERR_OOM if device memory runs out. *out is set only on BEAM_OK.
+ */
+int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float* router_bias,
+                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                  void* stream, beam_moe_handle* out);
+
+/* beam_moe_destroy — synchronise and free everything the handle owns. NULL is a no-op. */
+int beam_moe_destroy(beam_moe_handle h);
+
+/*
+ * beam_sublayer_norm_residual — the fused sublayer boundary, per token row:
+ *   xn = bf16(RMSNorm(x) * w_post)                 post-norm of the branch x
+ *   h' = bf16(bf16(c1 * h) + bf16(c2 * xn))         depth-scaled residual,
+ *        c1 = sqrt((n-1)/n), c2 = 1/sqrt(n)         both operands rounded first
+ *   z  = bf16(RMSNorm(h') * w_pre)                  next sublayer's pre-norm
+ * with RMSNorm(v) = v / sqrt(mean(v^2) + eps), FP32 math throughout.
+ * [vLLM §MoE und Residual-Stream] sandwich norm and the depth-scaled residual;
+ * [vLLM §Agentengetriebene Optimierung, change 1] one fused kernel, FP32 math,
+ * BF16 rounding points; [SGLang §三明治归一化与深度缩放残差] both scaled operands
+ * are rounded to BF16 before the add.
+ * Arguments: h_in, x [T, d] BF16; w_post, w_pre [d] BF16; n >= 1 is the 1-based
+ * index of this residual add; eps >= 0. Outputs h_out, z_out [T, d] BF16.
+ * h_out may equal h_in (in place); no other overlap is allowed.
+ * Needs d % 8 == 0 and d <= 65536. T == 0 is a no-op.
+ */
+int beam_sublayer_norm_residual(int32_t T, int32_t d, const uint16_t* h_in, const uint16_t* x,
+                                const uint16_t* w_post, const uint16_t* w_pre, int32_t n,
+                                float eps, uint16_t* h_out, uint16_t* z_out, void* stream);
+
+/*
+ * beam_router_topk — FP32 router logits and grouped top-k for T tokens.
+ *   logits[t, e] = sum_i z[t, i] * W[e, i]          FP32
+ *   s = sigmoid(logits), c = s + bias
+ *   group score = sum of the two largest c in the group (one if E/G == 1)
+ *   keep the topk_groups best groups, then the topk best experts in them by c
+ *   (every order: value descending, then index ascending)
+ *   w[t, j] = s[ids[t, j]] / sum_j s[ids[t, j]] * routed_scale   (sum in slot order)
+ * [vLLM §MoE und Residual-Stream]: DeepSeek-V3-style routing, sigmoid scores
+ * plus correction bias, 4 of 8 groups, top 8, renormalised x 2.5, FP32 router.
+ * [SGLang §稠密层与分组 MoE 路由]: FP32 logits and routing coefficients.
+ * Arguments: z [T, d] BF16 (the MoE input). Outputs: logits_out [T, E] FP32 or
+ * NULL; ids_out [T, k] int32 in selection order; w_out [T, k] FP32.
+ * T <= max_tokens.
+ */
+int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* logits_out,
+                     int32_t* ids_out, float* w_out, void* stream);
+
+/*
+ * beam_grouped_topk — the routing step of beam_router_topk on caller-supplied
+ * FP32 logits [T, E] (same rules, same handle bias and scale). Outputs ids_out
+ * [T, k] and w_out [T, k]. For callers with their own router, and for
+ * checking the selection on fixed logits.
+ */
+int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t* ids_out,
+                      float* w_out, void* stream);
+
+/*
+ * beam_moe_forward — the routed MoE FFN for T tokens of z [T, d] BF16:
+ *   route (unless replayed), group the T*k assignments by expert (stable:
+ *   expert ascending, then slot t*k+j ascending), run each expert's SwiGLU on
+ *   its rows, and combine:
+ *     g = bf16(z . Wg[e]^T), u = bf16(z . Wu[e]^T)  FP32 accumulation
+ *     act = bf16(silu(g) * u)
+ *     y_j = bf16(w[t, j] * (act . Wd[e]^T))         weight applied before rounding
+ *     y[t] = bf16(y_0 + y_1 + ... + y_{k-1})         FP32 sum in slot order
+ * [SGLang §BF16 MoE 内核优化]: BF16 boundaries at gate/up and the activation;
+ * the FP32 routing weight is applied before the down output is rounded.
+ * [vLLM §Agentengetriebene Optimierung, change 3] and [SGLang, kernel-fusion
+ * paragraph]: the top-k outputs are summed, scaled and rounded once.
+ * Routing replay: if ids_in != NULL, ids_in [T, k] and w_in [T, k] (FP32) are
+ * used instead of routing ([SGLang §在 Miles 中进行强化学习] records and
+ * replays the selected experts); a slot whose id is outside [0, E) contributes
+ * nothing. Otherwise w_in must be NULL.
+ * Optional outputs (NULL to skip): logits_out [T, E] FP32 (computed routing
+ * only); ids_out [T, k]; w_out [T, k]; perm_out [T*k] int32 (row r of the
+ * expert-grouped order holds slot t*k+j; rows past the valid count are -1);
+ * offsets_out [E+1] int32 (exclusive prefix of per-expert row counts).
+ * Output y_out [T, d] BF16 must not overlap z.
+ */
+int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                     const int32_t* ids_in, const float* w_in, float* logits_out,
+                     int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
+                     void* stream);
+
+/* beam_status_string — a static description of a status code. */
+const char* beam_status_string(int status);
+
+/*
+ * Kernel timing, for measurement tools. While enabled, every kernel the
+ * library launches is bracketed by two HIP events on its stream.
+ * beam_profile_read synchronises the recorded events and returns, for kernel
+ * id `kernel` (0 <= kernel < beam_kernel_count()), the summed duration in
+ * milliseconds and the number of launches since the last reset. Not for use
+ * during graph capture. beam_kernel_name returns a static name or NULL.
+ */
+int beam_profile_enable(int enable);
+int beam_profile_reset(void);
+int beam_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+int32_t beam_kernel_count(void);
+const char* beam_kernel_name(int32_t kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -1,0 +1,405 @@
+// C ABI of the Beam MoE sublayer library: host-side validation, the handle and
+// its workspace, and the launch sequence of each entry point. Every check runs
+// before the first HIP call, so a rejected call has no side effects.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/beam_moe.h"
+#include "kernels.h"
+
+using namespace beam;
+
+// ---------------------------------------------------------------------------------------------
+// Kernel timing (measurement tools only)
+
+namespace {
+
+enum KernelId {
+  K_BOUNDARY = 0,
+  K_ROUTER,
+  K_TOPK,
+  K_PERMUTE,
+  K_GATEUP,
+  K_DOWN,
+  K_COMBINE,
+  K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {"boundary", "router", "topk",   "permute",
+                                           "gate_up",  "down",   "combine"};
+
+struct ProfRecord {
+  int id;
+  hipEvent_t start, stop;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<ProfRecord> records;
+  std::vector<hipEvent_t> pool;
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+hipEvent_t take_event(Profiler& p) {
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when timing is on.
+struct ProfScope {
+  int id;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(int id_, hipStream_t s_) : id(id_), s(s_) {
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.enabled) return;
+    a = take_event(p);
+    b = take_event(p);
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!(a && b)) return;
+    (void)hipEventRecord(b, s);
+    Profiler& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.records.push_back({id, a, b});
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BEAM_OK : BEAM_ERR_HIP; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Handle
+
+struct beam_moe_ctx {
+  beam_moe_config cfg;
+  int device = 0;
+  // weights (owned)
+  float* router_w = nullptr;  // [E, d]
+  float* bias = nullptr;      // [E]
+  uint16_t* wgu = nullptr;    // packed gate/up
+  uint16_t* wdp = nullptr;    // packed down
+  // workspace (owned), sized for max_tokens
+  float* logits = nullptr;     // [maxT, E]
+  int32_t* ids = nullptr;      // [maxT, k]
+  float* w = nullptr;          // [maxT, k]
+  int32_t* counts = nullptr;   // [E]
+  int32_t* offsets = nullptr;  // [E + 1]
+  int32_t* active = nullptr;   // [E]
+  int32_t* n_active = nullptr; // [1]
+  int32_t* tile_start = nullptr;  // [E + 1]
+  int32_t* perm = nullptr;        // [maxT * k]
+  int32_t* block_cnt = nullptr;   // [nb * E]
+  int32_t* block_base = nullptr;  // [nb * E]
+  uint16_t* act = nullptr;        // [maxT * k, f]
+  uint16_t* yk = nullptr;         // [maxT * k, d]
+  std::vector<void*> allocations;
+};
+
+namespace {
+
+int validate_config(const beam_moe_config* c) {
+  if (!c) return BEAM_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 ||
+      c->topk <= 0 || c->d_ff <= 0 || c->max_tokens <= 0 || !isfinite(c->routed_scale))
+    return BEAM_ERR_INVALID_ARG;
+  if (c->n_experts % c->n_groups != 0 || c->topk_groups > c->n_groups) return BEAM_ERR_INVALID_ARG;
+  const int gs = c->n_experts / c->n_groups;
+  if (c->topk > c->topk_groups * gs) return BEAM_ERR_INVALID_ARG;
+  if ((int64_t)c->max_tokens * c->topk >= (1ll << 31)) return BEAM_ERR_INVALID_ARG;
+  if (c->hidden % 256 != 0 || c->hidden > 16384) return BEAM_ERR_UNSUPPORTED;
+  if (c->d_ff % 256 != 0 || c->d_ff > 16384) return BEAM_ERR_UNSUPPORTED;
+  if (c->n_experts > 256 || c->n_groups > 64 || c->topk > 32) return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+template <class T>
+bool dev_alloc(beam_moe_ctx* h, T** p, size_t count) {
+  void* q = nullptr;
+  if (count == 0) count = 1;
+  if (hipMalloc(&q, count * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  h->allocations.push_back(q);
+  *p = (T*)q;
+  return true;
+}
+
+void free_all(beam_moe_ctx* h) {
+  for (void* p : h->allocations) (void)hipFree(p);
+  h->allocations.clear();
+}
+
+int route(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, int32_t* ids_copy,
+          float* w_copy, hipStream_t s) {
+  const beam_moe_config& c = h->cfg;
+  {
+    ProfScope ps(K_ROUTER, s);
+    RouterArgs ra{T, c.hidden, c.n_experts, z, h->router_w, logits};
+    hipError_t e = launch_router_fp32(ra, s);
+    if (e != hipSuccess) return BEAM_ERR_HIP;
+  }
+  ProfScope ps(K_TOPK, s);
+  TopkArgs ta{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
+              logits, h->bias, h->ids, h->w, ids_copy, w_copy};
+  return hip_status(launch_topk(ta, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_status_string(int status) {
+  switch (status) {
+    case BEAM_OK: return "ok";
+    case BEAM_ERR_INVALID_ARG: return "invalid argument";
+    case BEAM_ERR_UNSUPPORTED: return "unsupported shape";
+    case BEAM_ERR_OOM: return "out of device memory";
+    case BEAM_ERR_HIP: return "HIP runtime error";
+    case BEAM_ERR_CAPACITY: return "T exceeds the handle's max_tokens";
+    default: return "unknown status";
+  }
+}
+
+int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float* router_bias,
+                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                  void* stream, beam_moe_handle* out) {
+  int st = validate_config(cfg);
+  if (st != BEAM_OK) return st;
+  if (!out || !router_w || !router_bias || !w_gate || !w_up || !w_down) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(router_w) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      ((uintptr_t)router_bias & 3u))
+    return BEAM_ERR_INVALID_ARG;
+  beam_moe_ctx* h = new (std::nothrow) beam_moe_ctx();
+  if (!h) return BEAM_ERR_OOM;
+  h->cfg = *cfg;
+  const beam_moe_config& c = h->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return BEAM_ERR_HIP;
+  }
+  const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, k = c.topk, T = c.max_tokens;
+  const size_t slots = T * k;
+  const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
+  bool ok = dev_alloc(h, &h->router_w, E * d) && dev_alloc(h, &h->bias, E) &&
+            dev_alloc(h, &h->wgu, E * 2 * f * d) && dev_alloc(h, &h->wdp, E * d * f) &&
+            dev_alloc(h, &h->logits, T * E) && dev_alloc(h, &h->ids, slots) &&
+            dev_alloc(h, &h->w, slots) && dev_alloc(h, &h->counts, E) &&
+            dev_alloc(h, &h->offsets, E + 1) && dev_alloc(h, &h->active, E) &&
+            dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
+            dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->block_cnt, nb * E) &&
+            dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
+            dev_alloc(h, &h->yk, slots * d);
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return BEAM_ERR_OOM;
+  }
+  hipError_t e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float),
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, (int)E, (int)f, (int)d, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free_all(h);
+    delete h;
+    return BEAM_ERR_HIP;
+  }
+  *out = h;
+  return BEAM_OK;
+}
+
+int beam_moe_destroy(beam_moe_handle h) {
+  if (!h) return BEAM_OK;
+  int st = hip_status(hipDeviceSynchronize());
+  free_all(h);
+  delete h;
+  return st;
+}
+
+int beam_sublayer_norm_residual(int32_t T, int32_t d, const uint16_t* h_in, const uint16_t* x,
+                                const uint16_t* w_post, const uint16_t* w_pre, int32_t n,
+                                float eps, uint16_t* h_out, uint16_t* z_out, void* stream) {
+  if (T < 0 || d <= 0 || (d % 8) != 0 || n < 1 || !(eps >= 0.0f) || !isfinite(eps))
+    return BEAM_ERR_INVALID_ARG;
+  if (d > 65536) return BEAM_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_OK;
+  if (!h_in || !x || !w_post || !w_pre || !h_out || !z_out) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(h_in) || !aligned16(x) || !aligned16(w_post) || !aligned16(w_pre) ||
+      !aligned16(h_out) || !aligned16(z_out))
+    return BEAM_ERR_INVALID_ARG;
+  const float c1 = (float)sqrt((double)(n - 1) / (double)n);
+  const float c2 = (float)(1.0 / sqrt((double)n));
+  hipStream_t s = (hipStream_t)stream;
+  ProfScope ps(K_BOUNDARY, s);
+  BoundaryArgs a{T, d, h_in, x, w_post, w_pre, h_out, z_out, c1, c2, eps};
+  return hip_status(launch_boundary(a, s));
+}
+
+int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* logits_out,
+                     int32_t* ids_out, float* w_out, void* stream) {
+  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  if (!z || !ids_out || !w_out || !aligned16(z) || ((uintptr_t)ids_out & 3u) ||
+      ((uintptr_t)w_out & 3u) || (logits_out && ((uintptr_t)logits_out & 3u)))
+    return BEAM_ERR_INVALID_ARG;
+  return route(h, T, z, logits_out ? logits_out : h->logits, ids_out, w_out, (hipStream_t)stream);
+}
+
+int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t* ids_out,
+                      float* w_out, void* stream) {
+  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  if (!logits || !ids_out || !w_out || ((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) ||
+      ((uintptr_t)w_out & 3u))
+    return BEAM_ERR_INVALID_ARG;
+  const beam_moe_config& c = h->cfg;
+  hipStream_t s = (hipStream_t)stream;
+  ProfScope ps(K_TOPK, s);
+  TopkArgs ta{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
+              logits, h->bias, ids_out, w_out, nullptr, nullptr};
+  return hip_status(launch_topk(ta, s));
+}
+
+int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                     const int32_t* ids_in, const float* w_in, float* logits_out,
+                     int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
+                     void* stream) {
+  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  if (!z || !y_out || !aligned16(z) || !aligned16(y_out)) return BEAM_ERR_INVALID_ARG;
+  if ((ids_in == nullptr) != (w_in == nullptr)) return BEAM_ERR_INVALID_ARG;
+  if (ids_in && logits_out) return BEAM_ERR_INVALID_ARG;
+  const void* ptrs4[] = {ids_in, w_in, logits_out, ids_out, w_out, perm_out, offsets_out};
+  for (const void* p : ptrs4)
+    if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
+  const beam_moe_config& c = h->cfg;
+  const int64_t bytes_z = (int64_t)T * c.hidden * 2;
+  if ((const char*)y_out < (const char*)z + bytes_z && (const char*)z < (const char*)y_out + bytes_z)
+    return BEAM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = c.topk, E = c.n_experts;
+  const int slots = T * k;
+
+  const int32_t* ids = ids_in;
+  const float* w = w_in;
+  if (!ids_in) {
+    int st = route(h, T, z, logits_out ? logits_out : h->logits, ids_out, w_out, s);
+    if (st != BEAM_OK) return st;
+    ids = h->ids;
+    w = h->w;
+  } else {
+    if (ids_out &&
+        hipMemcpyAsync(ids_out, ids_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    if (w_out &&
+        hipMemcpyAsync(w_out, w_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+  }
+  {
+    ProfScope ps(K_PERMUTE, s);
+    PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, ids, h->counts,
+                h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
+                h->tile_start, perm_out, offsets_out};
+    if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
+                h->n_active, h->tile_start, w, h->act, h->yk};
+  if (T <= kStreamMaxT) {
+    const int max_active = slots < E ? slots : E;
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    {
+      ProfScope ps(K_DOWN, s);
+      if (launch_down_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+  } else {
+    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    {
+      ProfScope ps(K_DOWN, s);
+      if (launch_down_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+  }
+  ProfScope ps(K_COMBINE, s);
+  return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+}
+
+int beam_profile_enable(int enable) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.enabled = enable != 0;
+  return BEAM_OK;
+}
+
+int beam_profile_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (auto& r : p.records) {
+    (void)hipEventSynchronize(r.stop);
+    p.pool.push_back(r.start);
+    p.pool.push_back(r.stop);
+  }
+  p.records.clear();
+  return BEAM_OK;
+}
+
+int beam_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= K_COUNT || !total_ms || !launches) return BEAM_ERR_INVALID_ARG;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  for (auto& r : p.records) {
+    if (r.id != kernel) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return BEAM_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return BEAM_ERR_HIP;
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return BEAM_OK;
+}
+
+int32_t beam_kernel_count(void) { return K_COUNT; }
+
+const char* beam_kernel_name(int32_t kernel) {
+  return (kernel >= 0 && kernel < K_COUNT) ? kKernelNames[kernel] : nullptr;
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Fused sublayer boundary: post-RMSNorm -> depth-scaled residual -> next pre-RMSNorm.
+//
+// [vLLM "Serving Reflection Beam auf vLLM ab Tag 0", §MoE und Residual-Stream]
+//   sandwich norm; the n-th residual add is h <- sqrt((n-1)/n) h + x / sqrt(n).
+// [same page, §Agentengetriebene Optimierung, change 1] post-norm, scaled add and
+//   next pre-norm as one kernel with FP32 math and BF16 rounding points.
+// [SGLang "SGLang 支撑编程模型 Beam 生产部署", §三明治归一化与深度缩放残差]
+//   both scaled operands are rounded to BF16 before the add.
+//
+// One wavefront per token row. A row of d BF16 values is read as 16-byte
+// chunks, chunk c of the row going to lane c % 64 (consecutive lanes read
+// consecutive 16 bytes). For d <= 8192 the row stays in registers between the
+// three phases (sum of squares of x; scaled add and sum of squares of h';
+// pre-norm), so each row costs 2 reads and 2 writes of d BF16 values.
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+__device__ __forceinline__ float sumsq8(const u32x4& v) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = lo_bf(v[i]), b = hi_bf(v[i]);
+    s += a * a;
+    s += b * b;
+  }
+  return s;
+}
+
+// (v * r) * w, rounded, for 8 packed values
+__device__ __forceinline__ u32x4 norm8(const u32x4& v, float r, const u32x4& w) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_bf2((lo_bf(v[i]) * r) * lo_bf(w[i]), (hi_bf(v[i]) * r) * hi_bf(w[i]));
+  return o;
+}
+
+// h' = bf16(bf16(c1 h) + bf16(c2 xn)) for 8 packed values; accumulates sum of h'^2
+__device__ __forceinline__ u32x4 residual8(const u32x4& h, const u32x4& xn, float c1, float c2,
+                                           float& ss) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a0 = bf2f(f2bf(c1 * lo_bf(h[i]))), a1 = bf2f(f2bf(c1 * hi_bf(h[i])));
+    float b0 = bf2f(f2bf(c2 * lo_bf(xn[i]))), b1 = bf2f(f2bf(c2 * hi_bf(xn[i])));
+    float s0 = bf2f(f2bf(a0 + b0)), s1 = bf2f(f2bf(a1 + b1));
+    ss += s0 * s0;
+    ss += s1 * s1;
+    o[i] = (uint32_t)f2bf(s0) | ((uint32_t)f2bf(s1) << 16);
+  }
+  return o;
+}
+
+__device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+// Register-resident variant: NC = max 16-byte chunks per lane.
+template <int NC>
+__global__ __launch_bounds__(256) void boundary_rows_kernel(BoundaryArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int nch = a.d >> 3;
+  const u32x4* xr = (const u32x4*)(a.x + t * a.d);
+  const u32x4* hr = (const u32x4*)(a.h + t * a.d);
+  const u32x4* wpo = (const u32x4*)a.w_post;
+  const u32x4* wpr = (const u32x4*)a.w_pre;
+  u32x4* ho = (u32x4*)(a.h_out + t * a.d);
+  u32x4* zo = (u32x4*)(a.z_out + t * a.d);
+
+  u32x4 xv[NC], hv[NC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    int idx = lane + 64 * c;
+    if (idx < nch) {
+      xv[c] = ld_u32x4(xr + idx);
+      hv[c] = ld_u32x4(hr + idx);
+      ss += sumsq8(xv[c]);
+    }
+  }
+  const float r = rms_scale(wave_sum(ss), a.d, a.eps);
+  float ss2 = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    int idx = lane + 64 * c;
+    if (idx < nch) {
+      u32x4 xn = norm8(xv[c], r, ld_u32x4(wpo + idx));
+      hv[c] = residual8(hv[c], xn, a.c1, a.c2, ss2);
+      st_u32x4(ho + idx, hv[c]);
+    }
+  }
+  const float r2 = rms_scale(wave_sum(ss2), a.d, a.eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    int idx = lane + 64 * c;
+    if (idx < nch) st_u32x4(zo + idx, norm8(hv[c], r2, ld_u32x4(wpr + idx)));
+  }
+}
+
+// Any-width variant: re-reads x and h' instead of keeping the row in registers.
+__global__ __launch_bounds__(256) void boundary_rows_wide_kernel(BoundaryArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int nch = a.d >> 3;
+  const u32x4* xr = (const u32x4*)(a.x + t * a.d);
+  const u32x4* hr = (const u32x4*)(a.h + t * a.d);
+  const u32x4* wpo = (const u32x4*)a.w_post;
+  const u32x4* wpr = (const u32x4*)a.w_pre;
+  u32x4* ho = (u32x4*)(a.h_out + t * a.d);
+  u32x4* zo = (u32x4*)(a.z_out + t * a.d);
+  float ss = 0.0f;
+  for (int idx = lane; idx < nch; idx += 64) ss += sumsq8(ld_u32x4(xr + idx));
+  const float r = rms_scale(wave_sum(ss), a.d, a.eps);
+  float ss2 = 0.0f;
+  for (int idx = lane; idx < nch; idx += 64) {
+    u32x4 xn = norm8(ld_u32x4(xr + idx), r, ld_u32x4(wpo + idx));
+    st_u32x4(ho + idx, residual8(ld_u32x4(hr + idx), xn, a.c1, a.c2, ss2));
+  }
+  const float r2 = rms_scale(wave_sum(ss2), a.d, a.eps);
+  // each lane re-reads only the chunks it wrote itself
+  for (int idx = lane; idx < nch; idx += 64)
+    st_u32x4(zo + idx, norm8(ld_u32x4(ho + idx), r2, ld_u32x4(wpr + idx)));
+}
+
+hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s) {
+  const int nch = a.d >> 3;
+  const int nc = (nch + 63) / 64;
+  dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+  if (nc <= 1)
+    hipLaunchKernelGGL(boundary_rows_kernel<1>, grid, block, 0, s, a);
+  else if (nc <= 2)
+    hipLaunchKernelGGL(boundary_rows_kernel<2>, grid, block, 0, s, a);
+  else if (nc <= 4)
+    hipLaunchKernelGGL(boundary_rows_kernel<4>, grid, block, 0, s, a);
+  else if (nc <= 8)
+    hipLaunchKernelGGL(boundary_rows_kernel<8>, grid, block, 0, s, a);
+  else if (nc <= 10)
+    hipLaunchKernelGGL(boundary_rows_kernel<10>, grid, block, 0, s, a);
+  else if (nc <= 16)
+    hipLaunchKernelGGL(boundary_rows_kernel<16>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(boundary_rows_wide_kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace beam

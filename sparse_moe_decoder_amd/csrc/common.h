@@ -1,0 +1,89 @@
+// Shared device helpers for the Beam MoE kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+// BF16 <-> FP32. Widening is exact; narrowing is the hardware round-to-nearest-even
+// conversion (v_cvt_pk_bf16_f32), which keeps NaN quiet.
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Butterfly sum over the 64 lanes. Every step adds the same two values in
+// every lane that uses them (a + b and b + a), so all lanes end with the
+// bitwise-identical total. Steps 1, 2 use DPP quad permutes, 4 and 8 DPP row
+// half-mirror / mirror (lane i <-> 7-i, 15-i within a row), 16 and 32 swizzle.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp_quad_xor1(v);
+  v = v + dpp_quad_xor2(v);
+  v = v + dpp_half_mirror(v);
+  v = v + dpp_mirror(v);
+  v = v + __shfl_xor(v, 16, 64);
+  v = v + __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// 64-bit max over the wave (all lanes get the result); keys are unique per lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint64_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Order-preserving map of a finite FP32 value to uint32 (larger value -> larger key).
+// -0.0 is folded onto +0.0 first so the two compare equal, as in FP compares.
+__device__ __forceinline__ uint32_t f32_order_key(float v) {
+  v = v + 0.0f;
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ u32x4 ld_u32x4(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st_u32x4(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Streaming 16-byte load: weights are read once per call, so hint the caches
+// not to keep them (non-temporal).
+__device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// SiLU in FP32, v / (1 + e^-v), with the accurate library exp.
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+}  // namespace beam

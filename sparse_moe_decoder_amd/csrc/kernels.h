@@ -1,0 +1,87 @@
+// Kernel argument blocks and launchers shared between the kernels and the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+constexpr int kPermChunk = 1024;  // slots per permutation block (256 threads x 4 rounds)
+constexpr int kGemmBM = 128;      // rows per grouped-GEMM tile
+constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming expert path
+
+struct BoundaryArgs {
+  int T, d;
+  const uint16_t* h;
+  const uint16_t* x;
+  const uint16_t* w_post;
+  const uint16_t* w_pre;
+  uint16_t* h_out;  // may equal h
+  uint16_t* z_out;
+  float c1, c2, eps;
+};
+
+struct RouterArgs {
+  int T, d, E;
+  const uint16_t* z;  // [T, d] BF16
+  const float* W;     // [E, d] FP32
+  float* logits;      // [T, E]
+};
+
+struct TopkArgs {
+  int T, E, G, kg, k;
+  float scale;
+  const float* logits;  // [T, E]
+  const float* bias;    // [E]
+  int32_t* ids;         // [T, k]
+  float* w;             // [T, k]
+  int32_t* ids2;        // optional copy for the caller, or null
+  float* w2;
+};
+
+struct PermArgs {
+  int n;   // T * k slots
+  int E;
+  int nb;  // blocks = ceil(n / kPermChunk)
+  int bm;  // rows per grouped-GEMM tile (for the tile table)
+  const int32_t* ids;
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E + 1]
+  int32_t* perm;        // [n]: row -> slot, -1 past the valid rows
+  int32_t* block_cnt;   // [nb * E]
+  int32_t* block_base;  // [nb * E]
+  int32_t* active;      // [E]: experts with rows, ascending
+  int32_t* n_active;    // [1]
+  int32_t* tile_start;  // [E + 1]: exclusive prefix of ceil(count / bm)
+  int32_t* perm2;       // optional copies for the caller, or null
+  int32_t* offsets2;
+};
+
+struct ExpertArgs {
+  int T, k, d, f, E;
+  const uint16_t* z;          // [T, d]
+  const uint16_t* wgu;        // packed gate/up
+  const uint16_t* wdp;        // packed down
+  const int32_t* perm;        // [T*k] row -> slot
+  const int32_t* offsets;     // [E + 1]
+  const int32_t* active;      // [E]
+  const int32_t* n_active;    // [1]
+  const int32_t* tile_start;  // [E + 1]
+  const float* w;             // [T*k] routing weight by slot
+  uint16_t* act;              // [T*k, f] by row (expert-grouped order)
+  uint16_t* yk;               // [T*k, d] by slot t*k+j
+};
+
+hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
+hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_permute(const PermArgs& a, hipStream_t s);
+hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                         uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
+hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);
+hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s);
+hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,
+                          uint16_t* y, hipStream_t s);
+
+}  // namespace beam

@@ -1,0 +1,154 @@
+"""GPU parity at Beam's shapes (d 5120, 256 experts in 8 groups, top 4 groups /
+top 8, d_ff 2560, ~20 GB of BF16 experts) for the decode batches (T = 1, 32, 128:
+every element compared) and the prefill workloads (16384 tokens with near-uniform
+routing; 32768 tokens with 16 hot experts): h', z and routing for every token,
+the permutation's invariants for the whole batch, and the MoE output on a sample
+of tokens (the oracle computes them one by one). All calls go through the C ABI."""
+import os
+import threading
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+BASE = synth.WORKLOADS["decode1"]
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+class ExpertCache:
+    """Host expert weights drawn from the input generator, kept for the session."""
+
+    def __init__(self, wl):
+        self.wl, self.store, self.lock = wl, {}, threading.Lock()
+
+    def prefetch(self, experts):
+        need = [e for e in sorted(set(int(e) for e in experts)) if e not in self.store]
+        if need:
+            print(f"[beam] drawing {len(need)} experts on the host", flush=True)
+        for e in need:
+            self.store[e] = synth.expert_weights(self.wl, e)
+
+    def __call__(self, e):
+        with self.lock:
+            if e not in self.store:
+                self.store[e] = synth.expert_weights(self.wl, e)
+            return self.store[e]
+
+
+@pytest.fixture(scope="module")
+def beam_gpu():
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    print("[beam] drawing device weights (20 GB) and creating handles", flush=True)
+    d = {}
+    d["wpost"], d["wpre"] = sd.norm_weights(BASE)
+    W, b = sd.router(BASE)
+    wg, wu, wd = sd.experts(BASE)
+    d["moe"] = beam.BeamMoE(sd.moe_config(BASE, max_tokens=32768), W, b, wg, wu, wd)
+    skew = synth.WORKLOADS["skew32k"]
+    _, b_skew = sd.router(skew)
+    d["moe_skew"] = beam.BeamMoE(sd.moe_config(skew, max_tokens=32768), W, b_skew, wg, wu, wd)
+    del wg, wu, wd
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    yield d
+    d["moe"].close()
+    d["moe_skew"].close()
+
+
+@pytest.fixture(scope="module")
+def experts():
+    return ExpertCache(BASE)
+
+
+def host_front(wl, T):
+    """Oracle boundary, router and routing for tokens 0..T-1."""
+    hh = synth.token_rows(wl, range(T), "h")
+    xx = synth.token_rows(wl, range(T), "x")
+    h_out, z = oracle.boundary(hh, xx, synth.norm_weight(wl, "post"), synth.norm_weight(wl, "pre"),
+                               wl.n, wl.eps)
+    logits = oracle.router_threaded(z, synth.router_weight(wl), THREADS)
+    ids, w, ggap, egap = oracle.topk(logits, synth.router_bias(wl), wl.G, wl.kg, wl.k, wl.scale)
+    return dict(h_out=h_out, z=z, logits=logits, ids=ids, w=w, ggap=ggap, egap=egap)
+
+
+def gpu_run(d, moe, wl, T):
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    h, x = sd.tokens(wl, "h", T=T), sd.tokens(wl, "x", T=T)
+    h_out, z = beam.beam_sublayer_norm_residual(h, x, d["wpost"], d["wpre"], wl.n, wl.eps)
+    y, r = moe.forward(z, want_routing=True)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in r.items()}
+    out["h_out"], out["z"], out["y"] = P.bits(h_out), P.bits(z), P.bits(y)
+    del h, x, h_out, z, y
+    return out
+
+
+def compare_front(g, ref, wl, what):
+    P.assert_bf16_close(g["h_out"], ref["h_out"], f"{what} h'")
+    P.assert_bf16_close(g["z"], ref["z"], f"{what} z")
+    rel = P.logit_rel_rows(g["logits_out"], ref["logits"])
+    print(f"[parity] {what} logits max row rel-L2 {rel.max():.3e}", flush=True)
+    assert rel.max() <= P.LOGIT_REL_MAX
+    same, st = P.check_routing(g["ids_out"], g["w_out"], ref["ids"], ref["w"], ref["ggap"],
+                               ref["egap"], g["logits_out"], ref["logits"], what)
+    P.check_permutation_valid(g["ids_out"], g["perm_out"], g["offsets_out"], wl.E)
+    if np.all(same):
+        _, o_off, o_perm, _ = oracle.permute(ref["ids"], wl.E)
+        assert np.array_equal(g["perm_out"], o_perm)
+        assert np.array_equal(g["offsets_out"], o_off)
+    return same
+
+
+@pytest.mark.parametrize("T", [1, 32, 128])
+def test_decode_full(beam_gpu, experts, T):
+    wl = BASE.with_tokens(T)
+    print(f"[beam] decode T={T}", flush=True)
+    g = gpu_run(beam_gpu, beam_gpu["moe"], wl, T)
+    ref = host_front(wl, T)
+    same = compare_front(g, ref, wl, f"decode T={T}")
+    experts.prefetch(ref["ids"].ravel())
+    y, _ = oracle.moe_experts(ref["z"], ref["ids"], ref["w"], wl.E, experts, threads=THREADS)
+    n_exp = len(set(ref["ids"].ravel().tolist()))
+    print(f"[beam] decode T={T}: {n_exp} distinct experts", flush=True)
+    P.assert_bf16_close(g["y"][same], y[same], f"decode T={T} y")
+
+
+def sampled_tokens(ids, T, hot=(), n_rand=32, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set(range(8)) | set(range(T - 8, T)) | set(rng.choice(T, n_rand, replace=False).tolist())
+    for e in hot:  # at least one token routed to each hot expert
+        rows = np.nonzero(np.any(ids == e, axis=1))[0]
+        if len(rows):
+            pick.add(int(rows[0]))
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("name", ["prefill16k", "skew32k"])
+def test_prefill_sampled(beam_gpu, experts, name):
+    wl = synth.WORKLOADS[name]
+    T = wl.T
+    moe = beam_gpu["moe_skew"] if wl.hot_experts else beam_gpu["moe"]
+    print(f"[beam] {name}: GPU run T={T}", flush=True)
+    g = gpu_run(beam_gpu, moe, wl, T)
+    print(f"[beam] {name}: oracle boundary/router/routing for all {T} tokens", flush=True)
+    ref = host_front(wl, T)
+    same = compare_front(g, ref, wl, name)
+    counts = np.bincount(g["ids_out"].ravel(), minlength=wl.E)
+    hot_share = counts[list(wl.hot_experts)].sum() / counts.sum() if wl.hot_experts else 0.0
+    print(f"[beam] {name}: rows per expert min {counts.min()} max {counts.max()}, "
+          f"hot share {hot_share:.3f}", flush=True)
+    rows = sampled_tokens(ref["ids"], T, wl.hot_experts)
+    rows = rows[same[rows]]
+    experts.prefetch(ref["ids"][rows].ravel())
+    y, _ = oracle.moe_experts(ref["z"][rows], ref["ids"][rows], ref["w"][rows], wl.E, experts,
+                              threads=THREADS)
+    P.assert_bf16_close(g["y"][rows], y, f"{name} y ({len(rows)} sampled tokens)")

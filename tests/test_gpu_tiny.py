@@ -1,0 +1,240 @@
+"""GPU parity on the tiny sublayer (T 8, d 512, 32 experts in 8 groups of 4, d_ff 256),
+every element compared with the CPU oracle, plus routing on fixed logits, replay,
+determinism, batch invariance and edge cases. All calls go through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS["tiny"]
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    assert torch.cuda.is_available()
+    print(f"[tiny] building device inputs {WL}", flush=True)
+    d = dict(h=sd.tokens(WL, "h"), x=sd.tokens(WL, "x"))
+    d["wpost"], d["wpre"] = sd.norm_weights(WL)
+    d["W"], d["b"] = sd.router(WL)
+    d["wg"], d["wu"], d["wd"] = sd.experts(WL)
+    d["moe"] = beam.BeamMoE(sd.moe_config(WL, max_tokens=64), d["W"], d["b"], d["wg"], d["wu"],
+                            d["wd"])
+    torch.cuda.synchronize()
+    yield d
+    d["moe"].close()
+
+
+@pytest.fixture(scope="module")
+def host():
+    hh = synth.token_rows(WL, range(WL.T), "h")
+    xx = synth.token_rows(WL, range(WL.T), "x")
+    experts = {e: synth.expert_weights(WL, e) for e in range(WL.E)}
+    ref = oracle.sublayer(hh, xx, synth.norm_weight(WL, "post"), synth.norm_weight(WL, "pre"),
+                          WL.n, WL.eps, synth.router_weight(WL), synth.router_bias(WL), WL.G,
+                          WL.kg, WL.k, WL.scale, experts.__getitem__)
+    ref["h"], ref["x"], ref["experts"] = hh, xx, experts
+    return ref
+
+
+def test_device_generator_matches_host(gpu):
+    """The device input generator draws the same bits as the host one."""
+    assert np.array_equal(P.bits(gpu["h"]), synth.token_rows(WL, range(WL.T), "h"))
+    assert np.array_equal(P.bits(gpu["x"]), synth.token_rows(WL, range(WL.T), "x"))
+    assert np.array_equal(P.bits(gpu["wpost"]), synth.norm_weight(WL, "post"))
+    assert np.array_equal(P.bits(gpu["wpre"]), synth.norm_weight(WL, "pre"))
+    assert np.array_equal(gpu["W"].cpu().numpy(), synth.router_weight(WL))
+    assert np.array_equal(gpu["b"].cpu().numpy(), synth.router_bias(WL))
+    for e in (0, 7, WL.E - 1):
+        wg, wu, wd = synth.expert_weights(WL, e)
+        assert np.array_equal(P.bits(gpu["wg"][e]), wg)
+        assert np.array_equal(P.bits(gpu["wu"][e]), wu)
+        assert np.array_equal(P.bits(gpu["wd"][e]), wd)
+
+
+def test_boundary(gpu, host):
+    import sparse_moe_decoder_amd as beam
+    h_out, z = beam.beam_sublayer_norm_residual(gpu["h"], gpu["x"], gpu["wpost"], gpu["wpre"],
+                                                WL.n, WL.eps)
+    P.assert_bf16_close(P.bits(h_out), host["h_out"], "tiny h'")
+    P.assert_bf16_close(P.bits(z), host["z"], "tiny z")
+
+
+def test_boundary_in_place_and_n1(gpu):
+    """h_out may alias h; n = 1 makes h' the post-normed branch (oracle closed form)."""
+    import sparse_moe_decoder_amd as beam
+    h = gpu["h"].clone()
+    _, z1 = beam.beam_sublayer_norm_residual(gpu["h"], gpu["x"], gpu["wpost"], gpu["wpre"], 20,
+                                            1e-6)
+    h_ref = P.bits(beam.beam_sublayer_norm_residual(gpu["h"], gpu["x"], gpu["wpost"],
+                                                    gpu["wpre"], 20, 1e-6)[0])
+    _, z2 = beam.beam_sublayer_norm_residual(h, gpu["x"], gpu["wpost"], gpu["wpre"], 20, 1e-6,
+                                            h_out=h)
+    assert np.array_equal(P.bits(h), h_ref)
+    assert np.array_equal(P.bits(z1), P.bits(z2))
+    hn1, _ = beam.beam_sublayer_norm_residual(gpu["h"], gpu["x"], gpu["wpost"], gpu["wpre"], 1,
+                                              1e-6)
+    o_h, _ = oracle.boundary(P.bits(gpu["h"]), P.bits(gpu["x"]), P.bits(gpu["wpost"]),
+                             P.bits(gpu["wpre"]), 1, 1e-6)
+    P.assert_bf16_close(P.bits(hn1), o_h, "tiny h' at n=1")
+
+
+def test_router_logits_and_routing(gpu, host):
+    z = P.to_dev(host["z"])
+    logits, ids, w = gpu["moe"].router_topk(z)
+    lg = logits.cpu().numpy()
+    rel = P.logit_rel_rows(lg, host["logits"])
+    print(f"[parity] tiny logits max row rel-L2 {rel.max():.3e}", flush=True)
+    assert rel.max() <= P.LOGIT_REL_MAX
+    P.check_routing(ids.cpu().numpy(), w.cpu().numpy(), host["ids"], host["w"], host["ggap"],
+                    host["egap"], lg, host["logits"], "tiny")
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "wide"])
+def test_routing_bit_exact_on_identical_logits(gpu, kind):
+    """Same FP32 logits on both sides -> expert ids bit-exact, weights bit-exact."""
+    import torch
+    T = 64
+    lg = synth.synthetic_logits(WL, T, seed=3, std=1.0 if kind != "wide" else 6.0)
+    if kind == "ties":
+        lg = (np.round(lg * 2) / 2).astype(np.float32)  # many exact ties
+    bias = synth.router_bias(WL)
+    o_ids, o_w, _, _ = oracle.topk(lg, bias, WL.G, WL.kg, WL.k, WL.scale)
+    ids, w = gpu["moe"].grouped_topk(torch.from_numpy(lg).cuda())
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    ulps = np.abs(w.cpu().numpy().view(np.int32).astype(np.int64) - o_w.view(np.int32))
+    print(f"[parity] tiny routing on identical logits ({kind}): max weight ulps {ulps.max()}",
+          flush=True)
+    assert ulps.max() <= 1 and np.mean(ulps == 0) > 0.999
+
+
+def test_forward_matches_oracle(gpu, host):
+    z = P.to_dev(host["z"])
+    y, r = gpu["moe"].forward(z, want_routing=True)
+    g_ids = r["ids_out"].cpu().numpy()
+    same, _ = P.check_routing(g_ids, r["w_out"].cpu().numpy(), host["ids"], host["w"],
+                              host["ggap"], host["egap"], r["logits_out"].cpu().numpy(),
+                              host["logits"], "tiny forward")
+    perm, offs = r["perm_out"].cpu().numpy(), r["offsets_out"].cpu().numpy()
+    P.check_permutation_valid(g_ids, perm, offs, WL.E)
+    if np.all(same):
+        _, o_off, o_perm, _ = oracle.permute(host["ids"], WL.E)
+        assert np.array_equal(perm, o_perm) and np.array_equal(offs, o_off)
+    P.assert_bf16_close(P.bits(y)[same], host["y"][same], "tiny y")
+
+
+def test_replay_matches_oracle(gpu, host):
+    """Caller-supplied routing (replay): permutation bit-exact, output vs oracle."""
+    import torch
+    z = P.to_dev(host["z"])
+    ids = torch.from_numpy(host["ids"]).cuda()
+    w = torch.from_numpy(host["w"]).cuda()
+    y, r = gpu["moe"].forward(z, ids_in=ids, w_in=w, want_routing=True)
+    _, o_off, o_perm, _ = oracle.permute(host["ids"], WL.E)
+    assert np.array_equal(r["perm_out"].cpu().numpy(), o_perm)
+    assert np.array_equal(r["offsets_out"].cpu().numpy(), o_off)
+    assert np.array_equal(r["ids_out"].cpu().numpy(), host["ids"])
+    P.assert_bf16_close(P.bits(y), host["y"], "tiny y (replay)")
+
+
+def test_replay_invalid_and_all_experts(gpu, host):
+    """Invalid ids contribute nothing; a token may use every expert (k = E style)."""
+    import torch
+    z = P.to_dev(host["z"])
+    ids = host["ids"].copy()
+    ids[0, 3] = -1
+    ids[2, 0] = WL.E + 5
+    w = host["w"].copy()
+    y, r = gpu["moe"].forward(z, ids_in=torch.from_numpy(ids).cuda(),
+                              w_in=torch.from_numpy(w).cuda(), want_routing=True)
+    o_y, _ = oracle.moe_experts(host["z"], ids, w, WL.E, host["experts"].__getitem__)
+    P.assert_bf16_close(P.bits(y), o_y, "tiny y (replay, invalid slots)")
+    P.check_permutation_valid(ids, r["perm_out"].cpu().numpy(), r["offsets_out"].cpu().numpy(),
+                              WL.E)
+
+
+def test_deterministic(gpu, host):
+    z = P.to_dev(host["z"])
+    a = P.bits(gpu["moe"].forward(z))
+    b = P.bits(gpu["moe"].forward(z))
+    assert np.array_equal(a, b)
+
+
+def test_batch_invariance(gpu, host):
+    """A token's routing and output do not depend on the other tokens in the batch."""
+    z = P.to_dev(host["z"])
+    full = P.bits(gpu["moe"].forward(z))
+    for t in (0, 5):
+        one = P.bits(gpu["moe"].forward(z[t:t + 1].contiguous()))
+        assert np.array_equal(one[0], full[t])
+
+
+def test_edge_sizes(gpu, host):
+    """T = 0 is a no-op; T = max_tokens works; T > max_tokens is rejected up front."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    moe = gpu["moe"]
+    z0 = torch.empty((0, WL.d), dtype=torch.bfloat16, device="cuda")
+    y0 = torch.empty_like(z0)
+    beam.beam_moe_forward(moe.handle, z0, y0)
+    zmax = torch.randn((64, WL.d), device="cuda").to(torch.bfloat16)
+    ymax = moe.forward(zmax)
+    assert torch.isfinite(ymax.float()).all()
+    with pytest.raises(beam.BeamError) as ei:
+        moe.forward(torch.zeros((65, WL.d), dtype=torch.bfloat16, device="cuda"))
+    assert ei.value.status == -5
+    # the 64-token batch matches the oracle on its first rows
+    zb = P.bits(zmax)
+    ref = oracle.router(zb[:4], synth.router_weight(WL))
+    ids, w, _, _ = oracle.topk(ref, synth.router_bias(WL), WL.G, WL.kg, WL.k, WL.scale)
+    o_y, _ = oracle.moe_experts(zb[:4], ids, w, WL.E, host["experts"].__getitem__)
+    P.assert_bf16_close(P.bits(ymax)[:4], o_y, "tiny y at T = max_tokens (first rows)")
+
+
+def test_prefill_path_ragged_tiles():
+    """T above the weight-streaming range takes the grouped-GEMM path: expert row
+    counts that span several 128-row tiles and ragged tails, checked in full."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    T = 1000
+    wl = WL.with_tokens(T)
+    h, x = sd.tokens(wl, "h"), sd.tokens(wl, "x")
+    wpost, wpre = sd.norm_weights(wl)
+    W, b = sd.router(wl)
+    wg, wu, wd = sd.experts(wl)
+    moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, wg, wu, wd)
+    try:
+        _, z = beam.beam_sublayer_norm_residual(h, x, wpost, wpre, wl.n, wl.eps)
+        y, r = moe.forward(z, want_routing=True)
+        torch.cuda.synchronize()
+        hh = synth.token_rows(wl, range(T), "h")
+        xx = synth.token_rows(wl, range(T), "x")
+        experts = {e: synth.expert_weights(wl, e) for e in range(wl.E)}
+        ref = oracle.sublayer(hh, xx, synth.norm_weight(wl, "post"), synth.norm_weight(wl, "pre"),
+                              wl.n, wl.eps, synth.router_weight(wl), synth.router_bias(wl), wl.G,
+                              wl.kg, wl.k, wl.scale, experts.__getitem__, threads=8)
+        P.assert_bf16_close(P.bits(z), ref["z"], "tiny@1000 z")
+        g_ids = r["ids_out"].cpu().numpy()
+        counts = np.bincount(g_ids.ravel(), minlength=wl.E)
+        print(f"[parity] tiny@1000 rows per expert: min {counts.min()} max {counts.max()}",
+              flush=True)
+        assert counts.max() > 128  # several tiles per expert
+        same, _ = P.check_routing(g_ids, r["w_out"].cpu().numpy(), ref["ids"], ref["w"],
+                                  ref["ggap"], ref["egap"], r["logits_out"].cpu().numpy(),
+                                  ref["logits"], "tiny@1000")
+        P.check_permutation_valid(g_ids, r["perm_out"].cpu().numpy(),
+                                  r["offsets_out"].cpu().numpy(), wl.E)
+        P.assert_bf16_close(P.bits(y)[same], ref["y"][same], "tiny@1000 y")
+        # replay with the oracle's routing on the oracle's z: the expert path alone
+        y2 = moe.forward(P.to_dev(ref["z"]), ids_in=torch.from_numpy(ref["ids"]).cuda(),
+                         w_in=torch.from_numpy(ref["w"]).cuda())
+        P.assert_bf16_close(P.bits(y2), ref["y"], "tiny@1000 y (replay)")
+    finally:
+        moe.close()
