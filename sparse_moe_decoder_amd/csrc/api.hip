@@ -151,19 +151,26 @@ void free_all(beam_moe_ctx* h) {
   h->allocations.clear();
 }
 
+int run_router(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, hipStream_t s) {
+  const beam_moe_config& c = h->cfg;
+  ProfScope ps(K_ROUTER, s);
+  RouterArgs ra{T, c.hidden, c.n_experts, z, h->router_w, logits};
+  return hip_status(launch_router_fp32(ra, s));
+}
+
+TopkArgs topk_args(beam_moe_ctx* h, int T, const float* logits, int32_t* ids_copy,
+                   float* w_copy) {
+  const beam_moe_config& c = h->cfg;
+  return TopkArgs{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
+                  logits, h->bias, h->ids, h->w, ids_copy, w_copy};
+}
+
 int route(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, int32_t* ids_copy,
           float* w_copy, hipStream_t s) {
-  const beam_moe_config& c = h->cfg;
-  {
-    ProfScope ps(K_ROUTER, s);
-    RouterArgs ra{T, c.hidden, c.n_experts, z, h->router_w, logits};
-    hipError_t e = launch_router_fp32(ra, s);
-    if (e != hipSuccess) return BEAM_ERR_HIP;
-  }
+  int st = run_router(h, T, z, logits, s);
+  if (st != BEAM_OK) return st;
   ProfScope ps(K_TOPK, s);
-  TopkArgs ta{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
-              logits, h->bias, h->ids, h->w, ids_copy, w_copy};
-  return hip_status(launch_topk(ta, s));
+  return hip_status(launch_topk(topk_args(h, T, logits, ids_copy, w_copy), s));
 }
 
 }  // namespace
@@ -280,11 +287,11 @@ int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t
   if (!logits || !ids_out || !w_out || ((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) ||
       ((uintptr_t)w_out & 3u))
     return BEAM_ERR_INVALID_ARG;
-  const beam_moe_config& c = h->cfg;
   hipStream_t s = (hipStream_t)stream;
   ProfScope ps(K_TOPK, s);
-  TopkArgs ta{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
-              logits, h->bias, ids_out, w_out, nullptr, nullptr};
+  TopkArgs ta = topk_args(h, T, logits, nullptr, nullptr);
+  ta.ids = ids_out;
+  ta.w = w_out;
   return hip_status(launch_topk(ta, s));
 }
 
@@ -311,11 +318,28 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
 
   const int32_t* ids = ids_in;
   const float* w = w_in;
+  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, h->counts,
+              h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
+              h->tile_start, perm_out, offsets_out};
   if (!ids_in) {
-    int st = route(h, T, z, logits_out ? logits_out : h->logits, ids_out, w_out, s);
+    float* lg = logits_out ? logits_out : h->logits;
+    int st = run_router(h, T, z, lg, s);
     if (st != BEAM_OK) return st;
     ids = h->ids;
     w = h->w;
+    pa.ids = ids;
+    TopkArgs ta = topk_args(h, T, lg, ids_out, w_out);
+    if (slots <= kPermChunk) {
+      ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
+      if (launch_route_permute_small(ta, pa, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else {
+      {
+        ProfScope ps(K_TOPK, s);
+        if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
+      }
+      ProfScope ps(K_PERMUTE, s);
+      if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
   } else {
     if (ids_out &&
         hipMemcpyAsync(ids_out, ids_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -323,12 +347,8 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (w_out &&
         hipMemcpyAsync(w_out, w_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
       return BEAM_ERR_HIP;
-  }
-  {
+    pa.ids = ids;
     ProfScope ps(K_PERMUTE, s);
-    PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, ids, h->counts,
-                h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
-                h->tile_start, perm_out, offsets_out};
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,

@@ -75,6 +75,8 @@ hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
+// grouped top-k + permutation in one launch; needs T * k <= kPermChunk
+hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);

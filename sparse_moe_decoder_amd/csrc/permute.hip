@@ -11,6 +11,7 @@
 // every run.
 #include "common.h"
 #include "kernels.h"
+#include "topk_device.h"
 
 namespace beam {
 
@@ -37,10 +38,79 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(PermArgs a) {
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.block_cnt[blockIdx.x * a.E + e] = cnt[e];
 }
 
-// One block: per-expert running sums over blocks, offsets, active list, tile table.
+// Exclusive scan of three per-expert quantities over up to 256 experts, by the
+// first four waves of the block (shuffle scan per wave, then wave totals).
+// q0 = row counts, q1 = 1 if the expert has rows, q2 = grouped-GEMM tiles.
+// Thread e < 256 receives its exclusive prefixes; totals go to tot[3].
+__device__ void scan256x3(int e, int v0, int v1, int v2, int& x0, int& x1, int& x2, int* tot) {
+  __shared__ int wsum[3][4];
+  const int lane = e & 63, wv = e >> 6;
+  int i0 = v0, i1 = v1, i2 = v2;
+  if (e < 256) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int a0 = __shfl_up(i0, off, 64), a1 = __shfl_up(i1, off, 64), a2 = __shfl_up(i2, off, 64);
+      if (lane >= off) {
+        i0 += a0;
+        i1 += a1;
+        i2 += a2;
+      }
+    }
+    if (lane == 63) {
+      wsum[0][wv] = i0;
+      wsum[1][wv] = i1;
+      wsum[2][wv] = i2;
+    }
+  }
+  __syncthreads();
+  if (e < 256) {
+    int p0 = 0, p1 = 0, p2 = 0;
+    for (int w = 0; w < wv; ++w) {
+      p0 += wsum[0][w];
+      p1 += wsum[1][w];
+      p2 += wsum[2][w];
+    }
+    x0 = p0 + i0 - v0;
+    x1 = p1 + i1 - v1;
+    x2 = p2 + i2 - v2;
+    if (e == 255) {
+      tot[0] = x0 + v0;
+      tot[1] = x1 + v1;
+      tot[2] = x2 + v2;
+    }
+  }
+  __syncthreads();
+}
+
+// Offsets, counts, active list and tile table from per-expert totals held by
+// threads e < E (others pass 0). Returns the valid row count to every thread.
+__device__ int publish_offsets(const PermArgs& a, int e, int cnt, int* excl_lds) {
+  __shared__ int tot[3];
+  const bool has = e < a.E;
+  int x0 = 0, x1 = 0, x2 = 0;
+  scan256x3(e, has ? cnt : 0, (has && cnt > 0) ? 1 : 0, has ? (cnt + a.bm - 1) / a.bm : 0, x0,
+            x1, x2, tot);
+  if (has) {
+    excl_lds[e] = x0;
+    a.counts[e] = cnt;
+    a.offsets[e] = x0;
+    if (a.offsets2) a.offsets2[e] = x0;
+    a.tile_start[e] = x2;
+    if (cnt > 0) a.active[x1] = e;
+  }
+  if (e == 0) {
+    a.offsets[a.E] = tot[0];
+    if (a.offsets2) a.offsets2[a.E] = tot[0];
+    a.tile_start[a.E] = tot[2];
+    *a.n_active = tot[1];
+  }
+  __syncthreads();
+  return tot[0];
+}
+
+// One block: per-expert running sums over the histogram blocks, then offsets.
 __device__ void scan_all(const PermArgs& a) {
-  __shared__ int tot[257];
-  __shared__ int excl[257];
+  __shared__ int excl_s[256];
   const int e = threadIdx.x;
   int run = 0;
   if (e < a.E) {
@@ -49,32 +119,12 @@ __device__ void scan_all(const PermArgs& a) {
       a.block_base[b * a.E + e] = run;
       run += c;
     }
-    a.counts[e] = run;
   }
-  tot[e] = (e < a.E) ? run : 0;
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0, na = 0, tiles = 0;
-    for (int x = 0; x < a.E; ++x) {
-      excl[x] = acc;
-      a.offsets[x] = acc;
-      if (a.offsets2) a.offsets2[x] = acc;
-      a.tile_start[x] = tiles;
-      if (tot[x] > 0) a.active[na++] = x;
-      acc += tot[x];
-      tiles += (tot[x] + a.bm - 1) / a.bm;
-    }
-    excl[a.E] = acc;
-    a.offsets[a.E] = acc;
-    if (a.offsets2) a.offsets2[a.E] = acc;
-    a.tile_start[a.E] = tiles;
-    *a.n_active = na;
-  }
-  __syncthreads();
+  const int total = publish_offsets(a, e, run, excl_s);
   if (e < a.E)
-    for (int b = 0; b < a.nb; ++b) a.block_base[b * a.E + e] += excl[e];
+    for (int b = 0; b < a.nb; ++b) a.block_base[b * a.E + e] += excl_s[e];
   // rows past the valid ones (slots with invalid ids) read as -1
-  for (int r = excl[a.E] + threadIdx.x; r < a.n; r += blockDim.x) {
+  for (int r = total + threadIdx.x; r < a.n; r += blockDim.x) {
     a.perm[r] = -1;
     if (a.perm2) a.perm2[r] = -1;
   }
@@ -139,6 +189,59 @@ __global__ __launch_bounds__(256) void perm_single_kernel(PermArgs a) {
   scan_all(a);
   __syncthreads();
   chunk_scatter(a, 0);
+}
+
+// Small batches (T*k <= 1024): grouped top-k for every token (16 waves, one
+// token per wave at a time), then the histogram, offsets and stable scatter from
+// LDS, all in one launch.
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, PermArgs a) {
+  __shared__ float s_lds[16][256];
+  __shared__ float c_lds[16][256];
+  __shared__ int32_t sel[16][32];
+  __shared__ int32_t ids_lds[1024];
+  __shared__ int cnt[256];
+  __shared__ int excl[256];
+  __shared__ int wave_cnt[16][256];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < 256; e += 1024) cnt[e] = 0;
+  for (int i = tid; i < 16 * 256; i += 1024) (&wave_cnt[0][0])[i] = 0;
+  for (int64_t t = wv; t < ta.T; t += 16) {
+    topk_token(ta, t, s_lds[wv], c_lds[wv], sel[wv], lane);
+    if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
+  }
+  __syncthreads();
+  const int n = a.n;
+  const int e_mine = tid < n ? ids_lds[tid] : -1;
+  const bool v = valid_id(e_mine, a.E);
+  if (v) atomicAdd(&cnt[e_mine], 1);
+  __syncthreads();
+  const int total = publish_offsets(a, tid, (tid < a.E) ? cnt[tid] : 0, excl);
+  // stable scatter: rank among earlier lanes with the same expert, then earlier waves
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint64_t match = __ballot(v);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    uint64_t bb = __ballot(v && ((e_mine >> bit) & 1));
+    match &= ((e_mine >> bit) & 1) ? bb : ~bb;
+  }
+  const int rank = __popcll(match & lt_mask);
+  if (v && rank == 0) wave_cnt[wv][e_mine] = __popcll(match);
+  __syncthreads();
+  if (v) {
+    int pos = excl[e_mine] + rank;
+    for (int w = 0; w < wv; ++w) pos += wave_cnt[w][e_mine];
+    a.perm[pos] = tid;
+    if (a.perm2) a.perm2[pos] = tid;
+  }
+  for (int r = total + tid; r < n; r += 1024) {
+    a.perm[r] = -1;
+    if (a.perm2) a.perm2[r] = -1;
+  }
+}
+
+hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(1024), 0, s, t, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const PermArgs& a, hipStream_t s) {

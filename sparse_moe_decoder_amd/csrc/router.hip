@@ -9,6 +9,7 @@
 //   FP32 routing coefficients, scale folded into the weights.
 #include "common.h"
 #include "kernels.h"
+#include "topk_device.h"
 
 namespace beam {
 
@@ -52,9 +53,61 @@ __global__ __launch_bounds__(256) void router_fp32_kernel(RouterArgs a) {
   }
 }
 
+// Small batches: one workgroup per (expert, block of RT tokens); its four waves
+// split d, so a W row is fetched by 256 lanes at once. Partials from the four
+// waves are added in wave order.
+__global__ __launch_bounds__(256) void router_fp32_small_kernel(RouterArgs a) {
+  __shared__ float part[3][RT];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * RT;
+  const int nt = min(RT, a.T - t0);
+  const int nch = a.d >> 2, per = nch >> 2;  // 4-float chunks; d % 256 == 0
+  const f32x4* wr = (const f32x4*)(a.W + (int64_t)e * a.d) + wv * per;
+  float acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = 0.0f;
+  for (int c = lane; c < per; c += 64) {
+    f32x4 w = *(wr + c);
+    const int col = 4 * (wv * per + c);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if (t < nt) {
+        const uint2 zz = *(const uint2*)(a.z + (int64_t)(t0 + t) * a.d + col);
+        acc[t] += lo_bf(zz.x) * w[0];
+        acc[t] += hi_bf(zz.x) * w[1];
+        acc[t] += lo_bf(zz.y) * w[2];
+        acc[t] += hi_bf(zz.y) * w[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    if (t < nt) {
+      float v = wave_sum(acc[t]);
+      if (wv > 0 && lane == 0) part[wv - 1][t] = v;
+      acc[t] = v;
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && lane < nt) {
+    float v = 0.0f;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+      if (t == lane) v = acc[t];
+    v = ((v + part[0][lane]) + part[1][lane]) + part[2][lane];
+    a.logits[(int64_t)(t0 + lane) * a.E + e] = v;
+  }
+}
+
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((a.E + 3) / 4), (unsigned)((a.T + RT - 1) / RT));
-  hipLaunchKernelGGL(router_fp32_kernel, grid, dim3(256), 0, s, a);
+  if (a.T <= kStreamMaxT) {
+    dim3 grid((unsigned)a.E, (unsigned)((a.T + RT - 1) / RT));
+    hipLaunchKernelGGL(router_fp32_small_kernel, grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((unsigned)((a.E + 3) / 4), (unsigned)((a.T + RT - 1) / RT));
+    hipLaunchKernelGGL(router_fp32_kernel, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -66,88 +119,14 @@ hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s) {
 //   w_j = (s_j / den) * scale, den summed over the slots in order
 // Selection uses 64-bit keys (order-preserving value bits << 32 | ~index), so one
 // wave max picks the winner and breaks ties toward the lower index.
-__device__ __forceinline__ uint64_t make_key(float v, int idx) {
-  return ((uint64_t)f32_order_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ float s_lds[4][256];
   __shared__ float c_lds[4][256];
   __shared__ int32_t sel_ids[4][32];
   const int wv = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= a.T) return;
-  const int E = a.E, G = a.G, gs = E / G;
-  float* s = s_lds[wv];
-  float* c = c_lds[wv];
-  for (int e = lane; e < E; e += 64) {
-    float l = a.logits[t * E + e];
-    float sv = (float)(1.0 / (1.0 + exp(-(double)l)));
-    s[e] = sv;
-    c[e] = sv + a.bias[e];
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // group scores: lane j < G scans its group
-  uint64_t gkey = 0;
-  if (lane < G) {
-    float m1 = -INFINITY, m2 = -INFINITY;
-    for (int q = 0; q < gs; ++q) {
-      float v = c[lane * gs + q];
-      if (v > m1) {
-        m2 = m1;
-        m1 = v;
-      } else if (v > m2) {
-        m2 = v;
-      }
-    }
-    gkey = make_key(gs >= 2 ? m1 + m2 : m1, lane);
-  }
-  // keep the kg best groups
-  uint64_t kept = 0;  // bit j set: group j kept
-  for (int r = 0; r < a.kg; ++r) {
-    uint64_t best = wave_max_u64(gkey);
-    int j = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-    kept |= 1ull << j;
-    if (lane == j) gkey = 0;
-  }
-  // candidate keys: each lane owns experts lane, lane + 64, ...
-  uint64_t key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
-    key[i] = (e < E && ((kept >> (e / gs)) & 1)) ? make_key(c[e], e) : 0;
-  }
-  for (int j = 0; j < a.k; ++j) {
-    uint64_t m = key[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) m = key[i] > m ? key[i] : m;
-    uint64_t best = wave_max_u64(m);
-    int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (key[i] == best) key[i] = 0;
-    if (lane == 0) sel_ids[wv][j] = e;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  // denominator in slot order (every lane computes the same sequential sum)
-  float den = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
-    float sj = s[sel_ids[wv][j]];
-    den = (j == 0) ? sj : den + sj;
-  }
-  if (lane < a.k) {
-    int e = sel_ids[wv][lane];
-    float wj = (s[e] / den) * a.scale;
-    a.ids[t * a.k + lane] = e;
-    a.w[t * a.k + lane] = wj;
-    if (a.ids2) a.ids2[t * a.k + lane] = e;
-    if (a.w2) a.w2[t * a.k + lane] = wj;
-  }
+  topk_token(a, t, s_lds[wv], c_lds[wv], sel_ids[wv], threadIdx.x & 63);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

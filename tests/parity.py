@@ -68,8 +68,9 @@ def check_routing(g_ids, g_w, o_ids, o_w, ggap, egap, g_logits, o_logits, what):
     Expert ids and slot order must match exactly, except on tokens whose oracle
     selection gap is within what the logit difference between the two sides can
     move (scores are sigmoid(logit), slope <= 1/4; a group score sums two scores):
-    those are counted as near-tie flips. Returns (mask of tokens that match,
-    stats)."""
+    those are counted as near-tie flips. Weights of matching tokens must agree to
+    1e-5 relative plus what the logit difference explains (w = s / sum(s) * scale,
+    so |dw|/w <= 2 max|ds| / min(s)). Returns (mask of matching tokens, stats)."""
     T = g_ids.shape[0]
     dl = np.max(np.abs(g_logits.astype(np.float64) - o_logits.astype(np.float64)), axis=1)
     tol = 4 * 0.25 * dl + NEAR_TIE
@@ -80,13 +81,18 @@ def check_routing(g_ids, g_w, o_ids, o_w, ggap, egap, g_logits, o_logits, what):
     near = int(np.count_nonzero(gap < NEAR_TIE))
     stats = dict(tokens=T, flips=int(np.count_nonzero(flips)), near_ties=near,
                  unexplained=int(np.count_nonzero(bad)), max_dlogit=float(dl.max()))
+    wbad = 0
     if np.any(same):
-        wd = np.abs(g_w[same].astype(np.float64) - o_w[same].astype(np.float64))
-        stats["w_max_rel"] = float(np.max(wd / np.abs(o_w[same])))
+        s_sel = 1.0 / (1.0 + np.exp(-np.take_along_axis(o_logits.astype(np.float64),
+                                                          o_ids.astype(np.int64), axis=1)))
+        wrel = np.abs(g_w.astype(np.float64) - o_w) / np.abs(o_w)
+        wtol = 1e-5 + 2 * 0.25 * dl[:, None] / s_sel.min(axis=1, keepdims=True)
+        wbad = int(np.count_nonzero((wrel > wtol)[same]))
+        stats["w_max_rel"] = float(wrel[same].max())
+        stats["w_bad"] = wbad
     print(f"[parity] {what} routing: {stats}", flush=True)
     assert stats["unexplained"] == 0, f"{what}: routing differs beyond near ties: {stats}"
-    if "w_max_rel" in stats:
-        assert stats["w_max_rel"] < 1e-5, stats
+    assert wbad == 0, f"{what}: routing weights differ beyond the logit difference: {stats}"
     return same, stats
 
 

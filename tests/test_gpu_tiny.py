@@ -212,7 +212,7 @@ def test_prefill_path_ragged_tiles():
     moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, wg, wu, wd)
     try:
         _, z = beam.beam_sublayer_norm_residual(h, x, wpost, wpre, wl.n, wl.eps)
-        y, r = moe.forward(z, want_routing=True)
+        y = moe.forward(z)
         torch.cuda.synchronize()
         hh = synth.token_rows(wl, range(T), "h")
         xx = synth.token_rows(wl, range(T), "x")
@@ -221,6 +221,12 @@ def test_prefill_path_ragged_tiles():
                               wl.n, wl.eps, synth.router_weight(wl), synth.router_bias(wl), wl.G,
                               wl.kg, wl.k, wl.scale, experts.__getitem__, threads=8)
         P.assert_bf16_close(P.bits(z), ref["z"], "tiny@1000 z")
+        y_chain = P.bits(y)
+        # the MoE stage on identical inputs (the oracle's z)
+        y, r = moe.forward(P.to_dev(ref["z"]), want_routing=True)
+        rel = P.logit_rel_rows(r["logits_out"].cpu().numpy(), ref["logits"])
+        print(f"[parity] tiny@1000 logits max row rel-L2 {rel.max():.3e}", flush=True)
+        assert rel.max() <= P.LOGIT_REL_MAX
         g_ids = r["ids_out"].cpu().numpy()
         counts = np.bincount(g_ids.ravel(), minlength=wl.E)
         print(f"[parity] tiny@1000 rows per expert: min {counts.min()} max {counts.max()}",
@@ -232,6 +238,9 @@ def test_prefill_path_ragged_tiles():
         P.check_permutation_valid(g_ids, r["perm_out"].cpu().numpy(),
                                   r["offsets_out"].cpu().numpy(), wl.E)
         P.assert_bf16_close(P.bits(y)[same], ref["y"][same], "tiny@1000 y")
+        ok, st = P.compare_bf16(y_chain[same], ref["y"][same])
+        print(f"[parity] tiny@1000 y composed chain (own z each side): {st}", flush=True)
+        assert st["rel_l2"] < 1e-2
         # replay with the oracle's routing on the oracle's z: the expert path alone
         y2 = moe.forward(P.to_dev(ref["z"]), ids_in=torch.from_numpy(ref["ids"]).cuda(),
                          w_in=torch.from_numpy(ref["w"]).cuda())
