@@ -96,6 +96,7 @@ struct beam_moe_ctx {
   int device = 0;
   // weights (owned)
   float* router_w = nullptr;  // [E, d]
+  uint16_t* router_x3 = nullptr;  // [3][E/16][d/32][64][8]: W = hi + mid + lo, BF16 parts
   float* bias = nullptr;      // [E]
   uint16_t* wgu = nullptr;    // packed gate/up
   uint16_t* wdp = nullptr;    // packed down
@@ -113,6 +114,7 @@ struct beam_moe_ctx {
   int32_t* block_base = nullptr;  // [nb * E]
   uint16_t* act = nullptr;        // [maxT * k, f]
   uint16_t* yk = nullptr;         // [maxT * k, d]
+  int32_t* tile_counter = nullptr;  // [d / 16], zero between calls
   std::vector<void*> allocations;
 };
 
@@ -127,6 +129,9 @@ int validate_config(const beam_moe_config* c) {
   const int gs = c->n_experts / c->n_groups;
   if (c->topk > c->topk_groups * gs) return BEAM_ERR_INVALID_ARG;
   if ((int64_t)c->max_tokens * c->topk >= (1ll << 31)) return BEAM_ERR_INVALID_ARG;
+  // 32-bit element offsets into activations: T * k * max(d, f) < 2^31
+  const int64_t wide = c->hidden > c->d_ff ? c->hidden : c->d_ff;
+  if ((int64_t)c->max_tokens * c->topk * wide >= (1ll << 31)) return BEAM_ERR_UNSUPPORTED;
   if (c->hidden % 256 != 0 || c->hidden > 16384) return BEAM_ERR_UNSUPPORTED;
   if (c->d_ff % 256 != 0 || c->d_ff > 16384) return BEAM_ERR_UNSUPPORTED;
   if (c->n_experts > 256 || c->n_groups > 64 || c->topk > 32) return BEAM_ERR_UNSUPPORTED;
@@ -151,9 +156,15 @@ void free_all(beam_moe_ctx* h) {
   h->allocations.clear();
 }
 
+// Small batches read the FP32 router weight once on the vector ALUs (the bytes are
+// the bound); large batches use the exact three-part BF16 split on the matrix cores.
 int run_router(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, hipStream_t s) {
   const beam_moe_config& c = h->cfg;
   ProfScope ps(K_ROUTER, s);
+  if (T > kStreamMaxT && c.n_experts % 64 == 0) {
+    RouterX3Args ra{T, c.hidden, c.n_experts, z, h->router_x3, logits};
+    return hip_status(launch_router_bf16x3(ra, s));
+  }
   RouterArgs ra{T, c.hidden, c.n_experts, z, h->router_w, logits};
   return hip_status(launch_router_fp32(ra, s));
 }
@@ -210,7 +221,8 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
   const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, k = c.topk, T = c.max_tokens;
   const size_t slots = T * k;
   const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
-  bool ok = dev_alloc(h, &h->router_w, E * d) && dev_alloc(h, &h->bias, E) &&
+  bool ok = dev_alloc(h, &h->router_w, E * d) && dev_alloc(h, &h->router_x3, 3 * E * d) &&
+            dev_alloc(h, &h->bias, E) &&
             dev_alloc(h, &h->wgu, E * 2 * f * d) && dev_alloc(h, &h->wdp, E * d * f) &&
             dev_alloc(h, &h->logits, T * E) && dev_alloc(h, &h->ids, slots) &&
             dev_alloc(h, &h->w, slots) && dev_alloc(h, &h->counts, E) &&
@@ -218,7 +230,7 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
             dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
             dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->block_cnt, nb * E) &&
             dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
-            dev_alloc(h, &h->yk, slots * d);
+            dev_alloc(h, &h->yk, slots * d) && dev_alloc(h, &h->tile_counter, d / 16);
   if (!ok) {
     free_all(h);
     delete h;
@@ -226,10 +238,13 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
   }
   hipError_t e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->tile_counter, 0, (d / 16) * sizeof(int32_t), s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, (int)E, (int)f, (int)d, s);
+  if (e == hipSuccess && E % 64 == 0)
+    e = launch_repack_router(router_w, h->router_x3, (int)E, (int)d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -352,17 +367,16 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk};
+                h->n_active, h->tile_start, w, h->act, h->yk, nullptr, ids, h->tile_counter};
   if (T <= kStreamMaxT) {
     const int max_active = slots < E ? slots : E;
     {
       ProfScope ps(K_GATEUP, s);
       if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
     }
-    {
-      ProfScope ps(K_DOWN, s);
-      if (launch_down_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
+    ProfScope ps(K_DOWN, s);  // down projection + combine
+    ea.y = y_out;
+    return hip_status(launch_down_stream(ea, max_active, s));
   } else {
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
     {

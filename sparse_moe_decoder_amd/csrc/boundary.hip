@@ -71,24 +71,29 @@ __global__ __launch_bounds__(256) void boundary_rows_kernel(BoundaryArgs a) {
   u32x4* ho = (u32x4*)(a.h_out + t * a.d);
   u32x4* zo = (u32x4*)(a.z_out + t * a.d);
 
-  u32x4 xv[NC], hv[NC];
-  float ss = 0.0f;
+  // every load is issued before the first reduction: one memory latency per row
+  u32x4 xv[NC], hv[NC], wo[NC], wr[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     int idx = lane + 64 * c;
     if (idx < nch) {
       xv[c] = ld_u32x4(xr + idx);
       hv[c] = ld_u32x4(hr + idx);
-      ss += sumsq8(xv[c]);
+      wo[c] = ld_u32x4(wpo + idx);
+      wr[c] = ld_u32x4(wpr + idx);
     }
   }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (lane + 64 * c < nch) ss += sumsq8(xv[c]);
   const float r = rms_scale(wave_sum(ss), a.d, a.eps);
   float ss2 = 0.0f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     int idx = lane + 64 * c;
     if (idx < nch) {
-      u32x4 xn = norm8(xv[c], r, ld_u32x4(wpo + idx));
+      u32x4 xn = norm8(xv[c], r, wo[c]);
       hv[c] = residual8(hv[c], xn, a.c1, a.c2, ss2);
       st_u32x4(ho + idx, hv[c]);
     }
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(256) void boundary_rows_kernel(BoundaryArgs a) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     int idx = lane + 64 * c;
-    if (idx < nch) st_u32x4(zo + idx, norm8(hv[c], r2, ld_u32x4(wpr + idx)));
+    if (idx < nch) st_u32x4(zo + idx, norm8(hv[c], r2, wr[c]));
   }
 }
 

@@ -51,14 +51,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 64-bit max over the wave (all lanes get the result); keys are unique per lane.
+// 64-bit max over the wave, returned wave-uniform. Max is associative and
+// commutative, so the reduction order does not matter: DPP moves (quad
+// permutes, row half-mirror, row mirror) give every lane its row's maximum, then
+// the four row maxima are read into scalar registers and compared there.
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint64_t m = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    m = max_u64(m, x);
   }
-  return v;
+  return m;
 }
 
 // Order-preserving map of a finite FP32 value to uint32 (larger value -> larger key).
@@ -80,6 +97,13 @@ __device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: lane l holds A[l % 32][8*(l/32) .. +7],
+// B[8*(l/32) .. +7][l % 32] and D[8*(r/4) + 4*(l/32) + r%4][l % 32] in register r.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 

@@ -22,6 +22,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace beam {
 
 // ---------------------------------------------------------------------------------------------
@@ -161,6 +163,12 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(ExpertArgs a) {
   }
 }
 
+// The down pass also finishes the combine: the last workgroup to finish an output
+// tile (a per-tile arrival counter, device-scope release/acquire fences) sums,
+// for every token, its k expert rows of that tile in slot order (FP32, one
+// rounding, invalid slots skipped) and resets the counter for the next call. The
+// sum reads the rows from memory in a fixed order, so the result does not depend
+// on which workgroup arrives last.
 template <int MT, int U>
 __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
   const int ND = a.d / 16;
@@ -172,6 +180,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
   const int KS = a.f / 32, ksw = KS / 4, ks0 = wv * ksw;
   const uint16_t* bp = a.wdp + (((int64_t)e * ND + nt) * KS + ks0) * 512 + lane * 8;
   __shared__ f32x4 red[3][MT][64];
+  __shared__ int last;
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     f32x4 acc[MT];
     const uint16_t* ap[MT];
@@ -220,6 +229,40 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
     }
     __syncthreads();
   }
+  if (a.y == nullptr) return;
+  // arrival: publish this workgroup's rows, then count it
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&a.tile_counter[nt], 1);
+    last = (prev == *a.n_active - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // combine tile nt for every token: 16 columns = two 8-column chunks per token
+  for (int q = threadIdx.x; q < a.T * 2; q += 256) {
+    const int t = q >> 1, half = q & 1;
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = -0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int id = a.ids[t * a.k + j];
+      if (id < 0 || id >= a.E) continue;
+      const u32x4 v = __builtin_nontemporal_load(
+          (const u32x4*)(a.yk + ((int64_t)t * a.k + j) * a.d + nt * 16 + half * 8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[2 * i] += lo_bf(v[i]);
+        s[2 * i + 1] += hi_bf(v[i]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf2(s[2 * i], s[2 * i + 1]);
+    st_u32x4(a.y + (int64_t)t * a.d + nt * 16 + half * 8, o);
+  }
+  if (threadIdx.x == 0) a.tile_counter[nt] = 0;
 }
 
 template <int MT>
@@ -259,149 +302,264 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prefill path: grouped GEMM on the matrix cores. A workgroup computes a
-// 128-row x 128-column tile of one expert: rows are that expert's assignment
-// rows (gathered through the permutation for gate/up), columns are 4 gate/up
-// tile pairs (gate/up) or 8 output tiles (down). K advances 64 at a time through
-// LDS; the next K block is fetched into registers while the current one is
-// multiplied. The four waves each own a 64 x 64 quarter (4 x 4 MFMA tiles).
-constexpr int GBM = kGemmBM, GBK = 64, GLDA = GBK + 8;
+// Prefill path: grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// A workgroup (4 waves) computes a 256-row x 256-column tile of one expert:
+// rows are that expert's assignment rows (gathered through the permutation for
+// gate/up: the z rows of their tokens), columns are 128 gate + 128 up outputs
+// (gate/up) or 256 outputs (down). Each wave owns a 128 x 128 quarter as 4 x 4
+// MFMA tiles (256 accumulators per lane).
+// K advances 32 at a time through four LDS stages filled by direct
+// global-to-LDS 16-byte loads (global_load_lds_dwordx4: each lane's 16 bytes land
+// at the stage base + 16 * lane), three K blocks ahead of the multiply, with one
+// barrier per K block and no staging registers.
+//   A stage: 256 rows x 32 values, 64 bytes per row; chunk c of row r is stored
+//     in slot c ^ ((r / 4) % 4), so the 16 lanes of a fragment read hit 16
+//     distinct 16-byte bank groups. A lane loads the logical chunk that belongs
+//     in its slot.
+//   B stage: sixteen packed 16x16x32 fragments (1 KB each) copied verbatim; a
+//     32x32x16 fragment reads two adjacent blocks, 256 contiguous bytes per 16 lanes.
+// For gate/up the wave's four N tiles are gate[q0, q0+32), gate[q0+32, q0+64),
+// up[q0, q0+32), up[q0+32, q0+64), so g and u of one output sit in the same lane
+// and register and the SiLU-mul epilogue needs no data movement. Results are
+// staged through LDS and written as 16-byte row chunks.
+constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GSTAGES = 4;
+constexpr int GSTAGE_A = GBM * GBK, GSTAGE_B = GBN * GBK;  // elements per stage
+
+__device__ __forceinline__ int a_slot(int row, int c) { return row * GBK + ((c ^ ((row >> 2) & 3)) << 3); }
+
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16 l (lds must be wave-uniform). Issued as inline assembly so the
+// compiler does not add its own conservative waits on the stage buffers; the
+// kernel waits explicitly (vmcnt) before a stage is read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(ExpertArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[GBM * GLDA];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2 * 8 * 512];
-  const int g = blockIdx.x;
-  const int nb = blockIdx.y;
-  if (g >= a.tile_start[a.E]) return;
+  // four A stages then four B stages (128 KB), reused as the epilogue's staging tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSTAGES * (GSTAGE_A + GSTAGE_B)];
+  __shared__ float w_row[GBM];
+  __shared__ int slot_row[GBM];
+  // XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs
+  // (block b runs on XCD b % 8), so XCD x is given the contiguous m-tile range
+  // [x R, x R + R) of the R = ceil(tiles / 8) it can own, n-tile fastest. The
+  // n-tiles of one m-tile then share its A rows, and an expert's consecutive
+  // m-tiles share its weight tiles, in one L2.
+  const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
+  const int total = a.tile_start[a.E];
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int R = (total + 7) >> 3;
+  const int nb = q % NT;
+  const int mb = q / NT;
+  const int g = xcd * R + mb;
+  if (mb >= R || g >= total) return;
   int lo = 0, hi = a.E;  // largest e with tile_start[e] <= g
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
     if (a.tile_start[mid] <= g) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int row0 = a.offsets[e];
-  const int m0 = (g - a.tile_start[e]) * GBM;
-  const int rows = min(GBM, a.offsets[e + 1] - row0 - m0);
+  const int row0 = a.offsets[e] + (g - a.tile_start[e]) * GBM;
+  const int rows = min(GBM, a.offsets[e + 1] - row0);
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wm = wv >> 1, wn = wv & 1;
   const int K = GATEUP ? a.d : a.f;
   const int KS = K / 32;
 
-  // global sources for this thread's 4 A chunks and 4 B chunks
-  const uint16_t* asrc[4];
-  int adst[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, kc = q & 7;
-    adst[i] = r * GLDA + kc * 8;
-    if (r < rows) {
-      if (GATEUP) {
-        const int tok = a.perm[row0 + m0 + r] / a.k;
-        asrc[i] = a.z + (int64_t)tok * a.d + kc * 8;
-      } else {
-        asrc[i] = a.act + (int64_t)(row0 + m0 + r) * a.f + kc * 8;
-      }
-    } else {
-      asrc[i] = nullptr;
+  if (!GATEUP) {
+    for (int r = tid; r < GBM; r += 256) {
+      const int slot = r < rows ? a.perm[row0 + r] : 0;
+      slot_row[r] = slot;
+      w_row[r] = r < rows ? a.w[slot] : 0.0f;
     }
   }
-  const uint16_t* bsrc[4];
-  int64_t bstep;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + 256 * i, blk = q >> 6, ln = q & 63;
-    const int ksl = blk >> 3, bb = blk & 7;
-    if (GATEUP) {
-      const int NJ = a.f / 16, jj = bb >> 1, gu = bb & 1;
-      bsrc[i] = a.wgu + ((((int64_t)e * NJ + nb * 4 + jj) * KS + ksl) * 2 + gu) * 512 + ln * 8;
-    } else {
-      const int ND = a.d / 16;
-      bsrc[i] = a.wdp + (((int64_t)e * ND + nb * 8 + bb) * KS + ksl) * 512 + ln * 8;
-    }
-  }
-  bstep = GATEUP ? 4 * 512 : 2 * 512;  // elements per 64-wide K block
 
-  f32x4 acc[4][4];
+  // A: wave wv fills rows [64 wv, 64 wv + 64) of a stage with 4 instructions of
+  // 16 rows; lane l covers row 16 i + l / 4, slot l % 4. Rows past the tile's
+  // valid count read row 0 of the tile (finite data, never written back).
+  const uint16_t* abase = GATEUP ? a.z : a.act;
+  int aoff[4];  // element offset of (row, logical chunk) at K block 0
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wv * 64 + i * 16 + (lane >> 2);
+    const int rr = r < rows ? r : 0;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    aoff[i] = (GATEUP ? (a.perm[row0 + rr] / a.k) * a.d : (row0 + rr) * a.f) + c * 8;
+  }
+  // B: wave wv copies blocks 4 wv .. 4 wv + 3 of a stage (block = 64 lanes x 16 B)
+  const uint16_t* bbase;
+  int boff[4];
+  if (GATEUP) {
+    const int NJ = a.f / 16;
+    bbase = a.wgu + ((int64_t)e * NJ + nb * 8) * KS * 2 * 512;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wv * 4 + i, jj = b >> 1, gu = b & 1;  // stage block b = jj * 2 + gu
+      boff[i] = (jj * KS * 2 + gu) * 512 + lane * 8;
+    }
+  } else {
+    const int ND = a.d / 16;
+    bbase = a.wdp + ((int64_t)e * ND + nb * 16) * KS * 512;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wv * 4 + i;  // stage block b = n-tile b
+      boff[i] = b * KS * 512 + lane * 8;
+    }
+  }
+  const int bstep = GATEUP ? 2 * 512 : 512;  // elements per 32-wide K block
+
+  // stage offsets are compile-time constants (the main loop is unrolled by the
+  // stage count)
+  auto stage_a = [&](auto S) -> uint16_t* { return smem + decltype(S)::value * GSTAGE_A; };
+  auto stage_b = [&](auto S) -> uint16_t* {
+    return smem + GSTAGES * GSTAGE_A + decltype(S)::value * GSTAGE_B;
+  };
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
+  auto issue = [&](int kb, auto S) {
+    const uint32_t A = lds_addr(stage_a(S)) + (uint32_t)(wvu * 64 * GBK * 2);
+    const uint32_t B = lds_addr(stage_b(S)) + (uint32_t)(wvu * 4 * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(abase + aoff[i] + kb * GBK, A + i * 16 * GBK * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(bbase + boff[i] + kb * bstep, B + i * 1024);
+  };
+
+  // fragment read offsets (elements within a stage)
+  const int l32 = lane & 31, lh = lane >> 5;
+  int aread[4][2], bread[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) aread[mt][kk] = a_slot(wm * 128 + mt * 32 + l32, kk * 2 + lh);
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int lanep = (lane & 15) + 16 * (kk * 2 + lh);
+      int b;
+      if (GATEUP) {
+        const int mq = nn & 1, gu = nn >> 1;
+        b = (wn * 4 + 2 * mq + ((lane >> 4) & 1)) * 2 + gu;
+      } else {
+        b = wn * 8 + nn * 2 + ((lane >> 4) & 1);
+      }
+      bread[nn][kk] = b * 512 + lanep * 8;
+    }
+  }
+
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[4], rb[4];
-  auto fetch = [&](int kb) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = asrc[i] ? ld_u32x4(asrc[i] + kb * GBK) : u32x4{0u, 0u, 0u, 0u};
-      rb[i] = ld_u32x4(bsrc[i] + (int64_t)kb * bstep);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nkb = K / GBK;  // a multiple of 4 (d, f % 256 == 0)
+  auto step = [&](int kb, auto S) {
+    constexpr int st = decltype(S)::value;
+    const int left = nkb - 1 - kb;  // K blocks issued after this one, at most 2
+    if (left >= 2) wait_vm<16>(); else if (left == 1) wait_vm<8>(); else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    const uint16_t* A = stage_a(S);
+    const uint16_t* B = stage_b(S);
+    // all 16 fragments of this K block are read before the next stage's loads are
+    // issued and before the MFMAs (k16 step 0, then 1)
+    u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) fa[kk][mt] = ld_u32x4(A + aread[mt][kk]);
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn) fb[kk][nn] = ld_u32x4(B + bread[nn][kk]);
     }
+    if (kb + GSTAGES - 1 < nkb) issue(kb + GSTAGES - 1, std::integral_constant<int, (st + 3) & 3>{});
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
   };
-  const int nkb = K / GBK;
-  fetch(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st_u32x4(As + adst[i], ra[i]);
-      st_u32x4(Bs + (tid + 256 * i) * 8, rb[i]);
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) fetch(kb + 1);
-#pragma unroll
-    for (int ksl = 0; ksl < 2; ++ksl) {
-      u32x4 fa[4], fb[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        fa[mt] = ld_u32x4(As + (wm * 64 + mt * 16 + (lane & 15)) * GLDA + ksl * 32 + 8 * (lane >> 4));
-#pragma unroll
-      for (int nn = 0; nn < 4; ++nn) {
-        const int blk = GATEUP ? ksl * 8 + (2 * wn + (nn >> 1)) * 2 + (nn & 1) : ksl * 8 + wn * 4 + nn;
-        fb[nn] = ld_u32x4(Bs + blk * 512 + lane * 8);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nn = 0; nn < 4; ++nn) acc[mt][nn] = mfma16(fa[mt], fb[nn], acc[mt][nn]);
-    }
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+  issue(2, std::integral_constant<int, 2>{});
+  for (int kb = 0; kb < nkb; kb += 4) {
+    step(kb, std::integral_constant<int, 0>{});
+    step(kb + 1, std::integral_constant<int, 1>{});
+    step(kb + 2, std::integral_constant<int, 2>{});
+    step(kb + 3, std::integral_constant<int, 3>{});
   }
+  wait_vm<0>();
+  __syncthreads();
 
-  // epilogue
+  // epilogue through LDS: the 128 KB of stages hold the output tile
+  uint16_t* stage = smem;
+  if (GATEUP) {
+    // act tile [256 rows][128 q]
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
-      if (r >= rows) continue;
-      const int row = row0 + m0 + r;
-      if (GATEUP) {
+      for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const float gv = bf2f(f2bf(acc[mt][2 * jj][i])), uv = bf2f(f2bf(acc[mt][2 * jj + 1][i]));
-          const int col = (nb * 4 + 2 * wn + jj) * 16 + (lane & 15);
-          a.act[(int64_t)row * a.f + col] = f2bf(silu(gv) * uv);
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int q = wn * 64 + mq * 32 + l32;
+          const float gv = bf2f(f2bf(acc[mt][mq][r])), uv = bf2f(f2bf(acc[mt][mq + 2][r]));
+          stage[row * 128 + q] = f2bf(silu(gv) * uv);
         }
-      } else {
-        const int slot = a.perm[row];
-        const float wt = a.w[slot];
+    __syncthreads();
+    for (int c = tid; c < GBM * 16; c += 256) {
+      const int r = c >> 4, ch = c & 15;
+      if (r < rows)
+        st_u32x4(a.act + (int64_t)(row0 + r) * a.f + nb * 128 + ch * 8,
+                 ld_u32x4(&stage[r * 128 + ch * 8]));
+    }
+  } else {
+    // output tile [256 rows][256 cols], weighted and rounded
 #pragma unroll
-        for (int nn = 0; nn < 4; ++nn) {
-          const int col = (nb * 8 + wn * 4 + nn) * 16 + (lane & 15);
-          a.yk[(int64_t)slot * a.d + col] = f2bf(wt * acc[mt][nn][i]);
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int col = wn * 128 + nn * 32 + l32;
+          stage[row * 256 + col] = f2bf(w_row[row] * acc[mt][nn][r]);
         }
-      }
+    __syncthreads();
+    for (int c = tid; c < GBM * 32; c += 256) {
+      const int r = c >> 5, ch = c & 31;
+      if (r < rows)
+        st_u32x4(a.yk + (int64_t)slot_row[r] * a.d + nb * 256 + ch * 8,
+                 ld_u32x4(&stage[r * 256 + ch * 8]));
     }
   }
 }
 
+// 1-D grid of 8 * ceil(max_tiles / 8) * n-tiles workgroups (see the tile order above)
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)max_tiles, (unsigned)(a.f / 64)),
-                     dim3(256), 0, s, a);
+  const unsigned gx = (unsigned)(8 * ((max_tiles + 7) / 8) * (a.f / 128));
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(gx), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)max_tiles, (unsigned)(a.d / 128)),
-                     dim3(256), 0, s, a);
+  const unsigned gx = (unsigned)(8 * ((max_tiles + 7) / 8) * (a.d / 256));
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(gx), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 namespace beam {
 
 constexpr int kPermChunk = 1024;  // slots per permutation block (256 threads x 4 rounds)
-constexpr int kGemmBM = 128;      // rows per grouped-GEMM tile
+constexpr int kGemmBM = 256;      // rows per grouped-GEMM tile
 constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming expert path
 
 struct BoundaryArgs {
@@ -25,6 +25,13 @@ struct RouterArgs {
   const uint16_t* z;  // [T, d] BF16
   const float* W;     // [E, d] FP32
   float* logits;      // [T, E]
+};
+
+struct RouterX3Args {
+  int T, d, E;            // E % 64 == 0, d % 128 == 0
+  const uint16_t* z;      // [T, d] BF16
+  const uint16_t* wx3;    // router weight as 3 BF16 parts, packed fragments
+  float* logits;          // [T, E]
 };
 
 struct TopkArgs {
@@ -69,11 +76,18 @@ struct ExpertArgs {
   const float* w;             // [T*k] routing weight by slot
   uint16_t* act;              // [T*k, f] by row (expert-grouped order)
   uint16_t* yk;               // [T*k, d] by slot t*k+j
+  // fused combine (weight-streaming path): output, routing ids and per-tile
+  // arrival counters (zero between calls); y == nullptr skips the combine
+  uint16_t* y;                // [T, d]
+  const int32_t* ids;         // [T, k]
+  int32_t* tile_counter;      // [d / 16]
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_repack_router(const float* W, uint16_t* out, int E, int d, hipStream_t s);
+hipError_t launch_router_bf16x3(const RouterX3Args& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 // grouped top-k + permutation in one launch; needs T * k <= kPermChunk
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s);

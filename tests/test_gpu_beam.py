@@ -104,7 +104,7 @@ def gpu_run(d, moe, wl, T, ref_z):
 def compare_front(g, ref, wl, what):
     """Boundary outputs, then routing and grouping on identical z."""
     P.assert_bf16_close(g["h_out"], ref["h_out"], f"{what} h'")
-    P.assert_bf16_close(g["z"], ref["z"], f"{what} z")
+    P.assert_bf16_close(g["z"], ref["z"], f"{what} z", two_ulp=g["h_out"] != ref["h_out"])
     rel = P.logit_rel_rows(g["logits_out"], ref["logits"])
     print(f"[parity] {what} logits max row rel-L2 {rel.max():.3e}", flush=True)
     assert rel.max() <= P.LOGIT_REL_MAX
