@@ -43,7 +43,23 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run plain device-to-device copies of BYTES (for scaling HBM "
+                        "counter readings) and exit")
     return p.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int = 5):
+    """Plain device copies of a known size: what FETCH_SIZE / WRITE_SIZE read per
+    dispatch for nbytes read + nbytes written gives the counters' scale."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def log(msg):
@@ -81,6 +97,9 @@ def read_traffic(kernel: str, workload: str, src_hash: str):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has "
               "no multi-GPU path; the per-GPU kernels are what one GPU shows.", file=sys.stderr)

@@ -114,7 +114,6 @@ struct beam_moe_ctx {
   int32_t* block_base = nullptr;  // [nb * E]
   uint16_t* act = nullptr;        // [maxT * k, f]
   uint16_t* yk = nullptr;         // [maxT * k, d]
-  int32_t* tile_counter = nullptr;  // [d / 16], zero between calls
   std::vector<void*> allocations;
 };
 
@@ -230,7 +229,7 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
             dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
             dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->block_cnt, nb * E) &&
             dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
-            dev_alloc(h, &h->yk, slots * d) && dev_alloc(h, &h->tile_counter, d / 16);
+            dev_alloc(h, &h->yk, slots * d);
   if (!ok) {
     free_all(h);
     delete h;
@@ -238,7 +237,6 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
   }
   hipError_t e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float),
                                 hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemsetAsync(h->tile_counter, 0, (d / 16) * sizeof(int32_t), s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
@@ -367,16 +365,19 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk, nullptr, ids, h->tile_counter};
+                h->n_active, h->tile_start, w, h->act, h->yk, y_out, ids};
   if (T <= kStreamMaxT) {
     const int max_active = slots < E ? slots : E;
     {
       ProfScope ps(K_GATEUP, s);
       if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
     }
-    ProfScope ps(K_DOWN, s);  // down projection + combine
-    ea.y = y_out;
-    return hip_status(launch_down_stream(ea, max_active, s));
+    if (T == 1 && k <= 16) {
+      ProfScope ps(K_DOWN, s);  // down projection + combine in one pass
+      return hip_status(launch_down_combine_t1(ea, s));
+    }
+    ProfScope ps(K_DOWN, s);
+    if (launch_down_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
   } else {
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
     {

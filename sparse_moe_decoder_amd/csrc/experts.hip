@@ -163,24 +163,20 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(ExpertArgs a) {
   }
 }
 
-// The down pass also finishes the combine: the last workgroup to finish an output
-// tile (a per-tile arrival counter, device-scope release/acquire fences) sums,
-// for every token, its k expert rows of that tile in slot order (FP32, one
-// rounding, invalid slots skipped) and resets the counter for the next call. The
-// sum reads the rows from memory in a fixed order, so the result does not depend
-// on which workgroup arrives last.
+// Down projection for the weight-streaming path: a workgroup covers 4 output
+// tiles of 16 columns of one expert, one wave per tile accumulating the full K in
+// order (the same per-output accumulation as the single-token kernel, so a token's
+// result does not depend on the batch it is in).
 template <int MT, int U>
 __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
-  const int ND = a.d / 16;
-  const int nt = blockIdx.x % ND;
-  int row0, cnt;
-  const int e = expert_of_block(a, blockIdx.x / ND, row0, cnt);
-  if (e < 0) return;
+  const int ND = a.d / 16, NB = ND / 4;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int KS = a.f / 32, ksw = KS / 4, ks0 = wv * ksw;
-  const uint16_t* bp = a.wdp + (((int64_t)e * ND + nt) * KS + ks0) * 512 + lane * 8;
-  __shared__ f32x4 red[3][MT][64];
-  __shared__ int last;
+  const int nt = (blockIdx.x % NB) * 4 + wv;
+  int row0, cnt;
+  const int e = expert_of_block(a, blockIdx.x / NB, row0, cnt);
+  if (e < 0) return;
+  const int KS = a.f / 32;
+  const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     f32x4 acc[MT];
     const uint16_t* ap[MT];
@@ -190,9 +186,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
       acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = m0 + mt * 16 + (lane & 15);
       av[mt] = r < cnt;
-      ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + ks0 * 32 + 8 * (lane >> 4);
+      ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + 8 * (lane >> 4);
     }
-    for (int ks = 0; ks < ksw; ks += U) {
+    for (int ks = 0; ks < KS; ks += U) {
       u32x4 b[U], x[MT][U];
 #pragma unroll
       for (int u = 0; u < U; ++u) b[u] = ld_stream_u32x4(bp + (int64_t)(ks + u) * 512);
@@ -206,63 +202,74 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
     }
-    if (wv > 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[wv - 1][mt][lane] = acc[mt];
-    }
-    __syncthreads();
-    if (wv == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 c = acc[mt];
-#pragma unroll
-        for (int w = 0; w < 3; ++w) c += red[w][mt][lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
-          if (r < cnt) {
-            const int slot = a.perm[row0 + r];
-            a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * c[i]);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (a.y == nullptr) return;
-  // arrival: publish this workgroup's rows, then count it
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.tile_counter[nt], 1);
-    last = (prev == *a.n_active - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // combine tile nt for every token: 16 columns = two 8-column chunks per token
-  for (int q = threadIdx.x; q < a.T * 2; q += 256) {
-    const int t = q >> 1, half = q & 1;
-    float s[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = -0.0f;
-    for (int j = 0; j < a.k; ++j) {
-      const int id = a.ids[t * a.k + j];
-      if (id < 0 || id >= a.E) continue;
-      const u32x4 v = __builtin_nontemporal_load(
-          (const u32x4*)(a.yk + ((int64_t)t * a.k + j) * a.d + nt * 16 + half * 8));
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[2 * i] += lo_bf(v[i]);
-        s[2 * i + 1] += hi_bf(v[i]);
+        const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+        if (r < cnt) {
+          const int slot = a.perm[row0 + r];
+          a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * acc[mt][i]);
+        }
       }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf2(s[2 * i], s[2 * i + 1]);
-    st_u32x4(a.y + (int64_t)t * a.d + nt * 16 + half * 8, o);
   }
-  if (threadIdx.x == 0) a.tile_counter[nt] = 0;
+}
+
+// Single token: down projection and combine in one pass with no cross-workgroup
+// traffic. A workgroup owns 16 output columns; its wave j streams slot j's expert
+// tile (16 x f) and keeps the token's row as the MFMA A operand. Each wave rounds
+// its weighted row (bf16(w_j * acc)), and the workgroup sums the k rows in slot
+// order in FP32 from -0.0 and rounds once, as the combine defines.
+template <int U>
+__global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
+  __shared__ float part[32][16];
+  const int ND = a.d / 16;
+  const int nt = blockIdx.x;
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KS = a.f / 32;
+  const int e = a.ids[j];
+  const bool valid = e >= 0 && e < a.E;
+  if (valid) {
+    // this slot's row in the expert-grouped order (slots ascend within an expert)
+    int row = a.offsets[e];
+    for (int jj = 0; jj < j; ++jj) row += (a.ids[jj] == e) ? 1 : 0;
+    const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
+    const bool arow = (lane & 15) == 0;
+    const uint16_t* ap = a.act + (int64_t)row * a.f + 8 * (lane >> 4);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ks += U) {
+      u32x4 b[U], x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = ld_stream_u32x4(bp + (int64_t)(ks + u) * 512);
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = arow ? ld_u32x4(ap + (ks + u) * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = mfma16(x[u], b[u], acc);
+    }
+    // row 0 of D sits in register 0 of lanes 0..15
+    if (lane < 16) part[j][lane] = bf2f(f2bf(a.w[j] * acc[0]));
+  }
+  __syncthreads();
+  if (j == 0 && lane < 16) {
+    float sum = -0.0f;
+    for (int jj = 0; jj < a.k; ++jj) {
+      const int ej = a.ids[jj];
+      if (ej >= 0 && ej < a.E) sum += part[jj][lane];
+    }
+    a.y[nt * 16 + lane] = f2bf(sum);
+  }
+}
+
+hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s) {
+  const int KS = a.f / 32;
+  dim3 g((unsigned)(a.d / 16)), blk((unsigned)(64 * a.k));
+  if (KS % 8 == 0)
+    hipLaunchKernelGGL(down_combine_t1_kernel<8>, g, blk, 0, s, a);
+  else if (KS % 4 == 0)
+    hipLaunchKernelGGL(down_combine_t1_kernel<4>, g, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL(down_combine_t1_kernel<2>, g, blk, 0, s, a);
+  return hipGetLastError();
 }
 
 template <int MT>
@@ -280,8 +287,8 @@ hipError_t launch_gateup_stream_mt(const ExpertArgs& a, int max_active, hipStrea
 
 template <int MT>
 hipError_t launch_down_stream_mt(const ExpertArgs& a, int max_active, hipStream_t s) {
-  const int ksw = a.f / 32 / 4;
-  dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
+  const int ksw = a.f / 32;  // every wave runs the full K
+  dim3 g((unsigned)(max_active * (a.d / 64))), blk(256);
   if (ksw % 8 == 0)
     hipLaunchKernelGGL((down_stream_kernel<MT, 8>), g, blk, 0, s, a);
   else if (ksw % 4 == 0)
@@ -304,11 +311,13 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 // ---------------------------------------------------------------------------------------------
 // Prefill path: grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// A workgroup (4 waves) computes a 256-row x 256-column tile of one expert:
-// rows are that expert's assignment rows (gathered through the permutation for
+// A workgroup (4 waves) computes up to 256 rows x 256 columns of one expert: rows
+// are that expert's assignment rows (gathered through the permutation for
 // gate/up: the z rows of their tokens), columns are 128 gate + 128 up outputs
-// (gate/up) or 256 outputs (down). Each wave owns a 128 x 128 quarter as 4 x 4
-// MFMA tiles (256 accumulators per lane).
+// (gate/up) or 256 outputs (down). Wave w owns all rows x columns [64 w, 64 w + 64)
+// as 8 x 2 MFMA tiles (256 accumulators per lane); the body is instantiated for
+// the number of 32-row tiles that hold rows (1..8), so an expert's last, partial
+// tile skips the empty ones.
 // K advances 32 at a time through four LDS stages filled by direct
 // global-to-LDS 16-byte loads (global_load_lds_dwordx4: each lane's 16 bytes land
 // at the stage base + 16 * lane), three K blocks ahead of the multiply, with one
@@ -316,13 +325,18 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 //   A stage: 256 rows x 32 values, 64 bytes per row; chunk c of row r is stored
 //     in slot c ^ ((r / 4) % 4), so the 16 lanes of a fragment read hit 16
 //     distinct 16-byte bank groups. A lane loads the logical chunk that belongs
-//     in its slot.
+//     in its slot. Rows past the tile's count load row 0 again (L2 hits).
 //   B stage: sixteen packed 16x16x32 fragments (1 KB each) copied verbatim; a
 //     32x32x16 fragment reads two adjacent blocks, 256 contiguous bytes per 16 lanes.
-// For gate/up the wave's four N tiles are gate[q0, q0+32), gate[q0+32, q0+64),
-// up[q0, q0+32), up[q0+32, q0+64), so g and u of one output sit in the same lane
-// and register and the SiLU-mul epilogue needs no data movement. Results are
-// staged through LDS and written as 16-byte row chunks.
+// For gate/up, wave w's two N tiles are gate[32 w, 32 w + 32) and up of the same
+// outputs, so g and u of one output sit in the same lane and register and the
+// SiLU-mul epilogue needs no data movement. Results are staged through LDS and
+// written as 16-byte row chunks.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs (block b runs
+// on XCD b % 8), so XCD x is given a contiguous range of the tile list, which is
+// ordered (expert, n-tile, m-tile): an expert's m-tiles read each weight tile at
+// the same time from one L2, and consecutive n-tiles share the expert's rows.
 constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GSTAGES = 4;
 constexpr int GSTAGE_A = GBM * GBK, GSTAGE_B = GBN * GBK;  // elements per stage
 
@@ -349,217 +363,228 @@ __device__ __forceinline__ void wait_vm() {
   else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(ExpertArgs a) {
-  // four A stages then four B stages (128 KB), reused as the epilogue's staging tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSTAGES * (GSTAGE_A + GSTAGE_B)];
-  __shared__ float w_row[GBM];
-  __shared__ int slot_row[GBM];
-  // XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs
-  // (block b runs on XCD b % 8), so XCD x is given the contiguous m-tile range
-  // [x R, x R + R) of the R = ceil(tiles / 8) it can own, n-tile fastest. The
-  // n-tiles of one m-tile then share its A rows, and an expert's consecutive
-  // m-tiles share its weight tiles, in one L2.
-  const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
-  const int total = a.tile_start[a.E];
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int R = (total + 7) >> 3;
-  const int nb = q % NT;
-  const int mb = q / NT;
-  const int g = xcd * R + mb;
-  if (mb >= R || g >= total) return;
-  int lo = 0, hi = a.E;  // largest e with tile_start[e] <= g
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.tile_start[mid] <= g) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int row0 = a.offsets[e] + (g - a.tile_start[e]) * GBM;
-  const int rows = min(GBM, a.offsets[e + 1] - row0);
+struct GemmTile {
+  int e, row0, rows, nb;
+};
+
+// Eight waves: wave w = 4 wm + wn owns the 32-row tiles 2 mt + wm (mt < MW) x
+// columns [64 wn, 64 wn + 64) as MW x 2 MFMA tiles (up to 128 accumulators), two
+// waves per SIMD. MW = ceil(tiles holding rows / 2), the same for every wave, so a
+// partial tile costs in 64-row steps.
+template <bool GATEUP, int MW>
+__device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTile& t,
+                                               uint16_t* smem, const float* w_row,
+                                               const int* slot_row) {
+  constexpr int NW = 8;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
+  const int wm = wvu >> 2, wn = wvu & 3;
   const int K = GATEUP ? a.d : a.f;
   const int KS = K / 32;
+  const int e = t.e, row0 = t.row0, rows = t.rows, nb = t.nb;
 
-  if (!GATEUP) {
-    for (int r = tid; r < GBM; r += 256) {
-      const int slot = r < rows ? a.perm[row0 + r] : 0;
-      slot_row[r] = slot;
-      w_row[r] = r < rows ? a.w[slot] : 0.0f;
-    }
-  }
-
-  // A: wave wv fills rows [64 wv, 64 wv + 64) of a stage with 4 instructions of
-  // 16 rows; lane l covers row 16 i + l / 4, slot l % 4. Rows past the tile's
-  // valid count read row 0 of the tile (finite data, never written back).
+  // A: wave w fills rows [32 w, 32 w + 32) of a stage with 2 instructions of 16
+  // rows; lane l covers row 16 i + l / 4, slot l % 4.
   const uint16_t* abase = GATEUP ? a.z : a.act;
-  int aoff[4];  // element offset of (row, logical chunk) at K block 0
+  int aoff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wv * 64 + i * 16 + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wv * 32 + i * 16 + (lane >> 2);
     const int rr = r < rows ? r : 0;
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     aoff[i] = (GATEUP ? (a.perm[row0 + rr] / a.k) * a.d : (row0 + rr) * a.f) + c * 8;
   }
-  // B: wave wv copies blocks 4 wv .. 4 wv + 3 of a stage (block = 64 lanes x 16 B)
+  // B: wave w copies blocks 2 w, 2 w + 1 of a stage (block = 64 lanes x 16 B)
   const uint16_t* bbase;
-  int boff[4];
+  int boff[2];
   if (GATEUP) {
     const int NJ = a.f / 16;
     bbase = a.wgu + ((int64_t)e * NJ + nb * 8) * KS * 2 * 512;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wv * 4 + i, jj = b >> 1, gu = b & 1;  // stage block b = jj * 2 + gu
+    for (int i = 0; i < 2; ++i) {
+      const int b = wv * 2 + i, jj = b >> 1, gu = b & 1;  // stage block b = jj * 2 + gu
       boff[i] = (jj * KS * 2 + gu) * 512 + lane * 8;
     }
   } else {
     const int ND = a.d / 16;
     bbase = a.wdp + ((int64_t)e * ND + nb * 16) * KS * 512;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wv * 4 + i;  // stage block b = n-tile b
+    for (int i = 0; i < 2; ++i) {
+      const int b = wv * 2 + i;  // stage block b = n-tile b
       boff[i] = b * KS * 512 + lane * 8;
     }
   }
   const int bstep = GATEUP ? 2 * 512 : 512;  // elements per 32-wide K block
 
-  // stage offsets are compile-time constants (the main loop is unrolled by the
-  // stage count)
-  auto stage_a = [&](auto S) -> uint16_t* { return smem + decltype(S)::value * GSTAGE_A; };
-  auto stage_b = [&](auto S) -> uint16_t* {
-    return smem + GSTAGES * GSTAGE_A + decltype(S)::value * GSTAGE_B;
-  };
-  const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
-  auto issue = [&](int kb, auto S) {
-    const uint32_t A = lds_addr(stage_a(S)) + (uint32_t)(wvu * 64 * GBK * 2);
-    const uint32_t B = lds_addr(stage_b(S)) + (uint32_t)(wvu * 4 * 1024);
+  auto stage_a = [&](int st) -> uint16_t* { return smem + st * GSTAGE_A; };
+  auto stage_b = [&](int st) -> uint16_t* { return smem + GSTAGES * GSTAGE_A + st * GSTAGE_B; };
+  auto issue = [&](int kb, int st) {
+    const uint32_t A = lds_addr(stage_a(st)) + (uint32_t)(wvu * 32 * GBK * 2);
+    const uint32_t B = lds_addr(stage_b(st)) + (uint32_t)(wvu * 2 * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(abase + aoff[i] + kb * GBK, A + i * 16 * GBK * 2);
+    for (int i = 0; i < 2; ++i) lds_dma16(abase + aoff[i] + kb * GBK, A + i * 16 * GBK * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(bbase + boff[i] + kb * bstep, B + i * 1024);
+    for (int i = 0; i < 2; ++i) lds_dma16(bbase + boff[i] + kb * bstep, B + i * 1024);
   };
 
-  // fragment read offsets (elements within a stage)
   const int l32 = lane & 31, lh = lane >> 5;
-  int aread[4][2], bread[4][2];
+  int aread[2], bread[2][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
+    // (row / 4) % 4 does not change across 32-row tiles: this wave's tile mt (rows
+    // 32 (2 mt + wm) ..) is at + mt * 64 * GBK
+    aread[kk] = a_slot(wm * 32 + l32, kk * 2 + lh);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) aread[mt][kk] = a_slot(wm * 128 + mt * 32 + l32, kk * 2 + lh);
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
+    for (int nn = 0; nn < 2; ++nn) {
       const int lanep = (lane & 15) + 16 * (kk * 2 + lh);
-      int b;
-      if (GATEUP) {
-        const int mq = nn & 1, gu = nn >> 1;
-        b = (wn * 4 + 2 * mq + ((lane >> 4) & 1)) * 2 + gu;
-      } else {
-        b = wn * 8 + nn * 2 + ((lane >> 4) & 1);
-      }
+      const int b = GATEUP ? (2 * wn + ((lane >> 4) & 1)) * 2 + nn : wn * 4 + nn * 2 + ((lane >> 4) & 1);
       bread[nn][kk] = b * 512 + lanep * 8;
     }
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[MW][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute = [&](int st) {
+    const uint16_t* A = stage_a(st);
+    const uint16_t* B = stage_b(st);
+    u32x4 fa[2][MW], fb[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) fb[kk][nn] = ld_u32x4(B + bread[nn][kk]);
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
+  };
 
   const int nkb = K / GBK;  // a multiple of 4 (d, f % 256 == 0)
   auto step = [&](int kb, auto S) {
     constexpr int st = decltype(S)::value;
     const int left = nkb - 1 - kb;  // K blocks issued after this one, at most 2
-    if (left >= 2) wait_vm<16>(); else if (left == 1) wait_vm<8>(); else wait_vm<0>();
+    if (left >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (left == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    const uint16_t* A = stage_a(S);
-    const uint16_t* B = stage_b(S);
-    // all 16 fragments of this K block are read before the next stage's loads are
-    // issued and before the MFMAs (k16 step 0, then 1)
-    u32x4 fa[2][4], fb[2][4];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) fa[kk][mt] = ld_u32x4(A + aread[mt][kk]);
-#pragma unroll
-      for (int nn = 0; nn < 4; ++nn) fb[kk][nn] = ld_u32x4(B + bread[nn][kk]);
-    }
-    if (kb + GSTAGES - 1 < nkb) issue(kb + GSTAGES - 1, std::integral_constant<int, (st + 3) & 3>{});
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nn = 0; nn < 4; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
+    if (kb + GSTAGES - 1 < nkb) issue(kb + GSTAGES - 1, (st + 3) & 3);
+    compute(st);
   };
-  issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
-  issue(2, std::integral_constant<int, 2>{});
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
   for (int kb = 0; kb < nkb; kb += 4) {
     step(kb, std::integral_constant<int, 0>{});
     step(kb + 1, std::integral_constant<int, 1>{});
     step(kb + 2, std::integral_constant<int, 2>{});
     step(kb + 3, std::integral_constant<int, 3>{});
   }
-  wait_vm<0>();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // epilogue through LDS: the 128 KB of stages hold the output tile
   uint16_t* stage = smem;
   if (GATEUP) {
-    // act tile [256 rows][128 q]
+    // act tile [256 rows][128 q]; wave (wm, wn) holds 32-row tiles 2 mt + wm, q [32 wn, +32)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
-      for (int mq = 0; mq < 2; ++mq)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int q = wn * 64 + mq * 32 + l32;
-          const float gv = bf2f(f2bf(acc[mt][mq][r])), uv = bf2f(f2bf(acc[mt][mq + 2][r]));
-          stage[row * 128 + q] = f2bf(silu(gv) * uv);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = (2 * mt + wm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int q = wn * 32 + l32;
+        const float gv = bf2f(f2bf(acc[mt][0][r])), uv = bf2f(f2bf(acc[mt][1][r]));
+        stage[row * 128 + q] = f2bf(silu(gv) * uv);
+      }
+    }
     __syncthreads();
-    for (int c = tid; c < GBM * 16; c += 256) {
+    for (int c = tid; c < rows * 16; c += 64 * NW) {
       const int r = c >> 4, ch = c & 15;
-      if (r < rows)
-        st_u32x4(a.act + (int64_t)(row0 + r) * a.f + nb * 128 + ch * 8,
-                 ld_u32x4(&stage[r * 128 + ch * 8]));
+      st_u32x4(a.act + (int64_t)(row0 + r) * a.f + nb * 128 + ch * 8,
+               ld_u32x4(&stage[r * 128 + ch * 8]));
     }
   } else {
     // output tile [256 rows][256 cols], weighted and rounded
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
+      for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int col = wn * 128 + nn * 32 + l32;
+          const int row = (2 * mt + wm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int col = wn * 64 + nn * 32 + l32;
           stage[row * 256 + col] = f2bf(w_row[row] * acc[mt][nn][r]);
         }
+    }
     __syncthreads();
-    for (int c = tid; c < GBM * 32; c += 256) {
+    for (int c = tid; c < rows * 32; c += 64 * NW) {
       const int r = c >> 5, ch = c & 31;
-      if (r < rows)
-        st_u32x4(a.yk + (int64_t)slot_row[r] * a.d + nb * 256 + ch * 8,
-                 ld_u32x4(&stage[r * 256 + ch * 8]));
+      st_u32x4(a.yk + (int64_t)slot_row[r] * a.d + nb * 256 + ch * 8,
+               ld_u32x4(&stage[r * 256 + ch * 8]));
     }
   }
 }
 
-// 1-D grid of 8 * ceil(max_tiles / 8) * n-tiles workgroups (see the tile order above)
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
+  // four A stages then four B stages (128 KB), reused as the epilogue's staging tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSTAGES * (GSTAGE_A + GSTAGE_B)];
+  __shared__ float w_row[GBM];
+  __shared__ int slot_row[GBM];
+  const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
+  const int total = a.tile_start[a.E] * NT;        // (expert, n-tile, m-tile) triples
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int R = (total + 7) >> 3;
+  const int L = xcd * R + q;
+  if (q >= R || L >= total) return;
+  // expert: largest e with tile_start[e] * NT <= L
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a.tile_start[mid] * NT <= L) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int mtiles = a.tile_start[e + 1] - a.tile_start[e];
+  const int within = L - a.tile_start[e] * NT;
+  GemmTile t;
+  t.e = e;
+  t.nb = within / mtiles;
+  t.row0 = a.offsets[e] + (within % mtiles) * GBM;
+  t.rows = min(GBM, a.offsets[e + 1] - t.row0);
+  if (!GATEUP) {
+    for (int r = threadIdx.x; r < GBM; r += blockDim.x) {
+      const int slot = r < t.rows ? a.perm[t.row0 + r] : 0;
+      slot_row[r] = slot;
+      w_row[r] = r < t.rows ? a.w[slot] : 0.0f;
+    }
+  }
+  switch ((t.rows + 63) >> 6) {  // 64-row steps: tiles per wave
+    case 1: gemm_tile_body<GATEUP, 1>(a, t, smem, w_row, slot_row); break;
+    case 2: gemm_tile_body<GATEUP, 2>(a, t, smem, w_row, slot_row); break;
+    case 3: gemm_tile_body<GATEUP, 3>(a, t, smem, w_row, slot_row); break;
+    default: gemm_tile_body<GATEUP, 4>(a, t, smem, w_row, slot_row); break;
+  }
+}
+
+// 1-D grid of 8 * ceil(max_tiles * n-tiles / 8) workgroups (see the tile order above)
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s) {
-  const unsigned gx = (unsigned)(8 * ((max_tiles + 7) / 8) * (a.f / 128));
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(gx), dim3(256), 0, s, a);
+  const unsigned gx = (unsigned)(8 * ((max_tiles * (a.f / 128) + 7) / 8));
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(gx), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s) {
-  const unsigned gx = (unsigned)(8 * ((max_tiles + 7) / 8) * (a.d / 256));
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(gx), dim3(256), 0, s, a);
+  const unsigned gx = (unsigned)(8 * ((max_tiles * (a.d / 256) + 7) / 8));
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(gx), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -76,11 +76,9 @@ struct ExpertArgs {
   const float* w;             // [T*k] routing weight by slot
   uint16_t* act;              // [T*k, f] by row (expert-grouped order)
   uint16_t* yk;               // [T*k, d] by slot t*k+j
-  // fused combine (weight-streaming path): output, routing ids and per-tile
-  // arrival counters (zero between calls); y == nullptr skips the combine
+  // single-token down + combine: output and routing ids
   uint16_t* y;                // [T, d]
   const int32_t* ids;         // [T, k]
-  int32_t* tile_counter;      // [d / 16]
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
@@ -95,6 +93,8 @@ hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t*
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);
 hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s);
+// T == 1, k <= 16: down projection and combine in one pass
+hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,

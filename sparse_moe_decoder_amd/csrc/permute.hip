@@ -195,7 +195,6 @@ __global__ __launch_bounds__(256) void perm_single_kernel(PermArgs a) {
 // token per wave at a time), then the histogram, offsets and stable scatter from
 // LDS, all in one launch.
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, PermArgs a) {
-  __shared__ float s_lds[16][256];
   __shared__ float c_lds[16][256];
   __shared__ int32_t sel[16][32];
   __shared__ int32_t ids_lds[1024];
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, 
   for (int e = tid; e < 256; e += 1024) cnt[e] = 0;
   for (int i = tid; i < 16 * 256; i += 1024) (&wave_cnt[0][0])[i] = 0;
   for (int64_t t = wv; t < ta.T; t += 16) {
-    topk_token(ta, t, s_lds[wv], c_lds[wv], sel[wv], lane);
+    topk_token(ta, t, c_lds[wv], sel[wv], lane);
     if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
   }
   __syncthreads();
@@ -239,8 +238,93 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, 
   }
 }
 
+// Tiny batches (T*k <= 64): the waves route one token each, then wave 0 holds one
+// slot per lane and computes everything by counting over the wave: a slot's row
+// is the number of valid slots ordered before it by (expert, slot); lane l owns
+// experts 4l .. 4l+3 for counts, offsets, the active list and the tile table.
+__global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, PermArgs a) {
+  __shared__ float c_lds[16][256];
+  __shared__ int32_t sel[16][32];
+  __shared__ int32_t ids_lds[64];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int nw = blockDim.x >> 6;
+  for (int64_t t = wv; t < ta.T; t += nw) {
+    topk_token(ta, t, c_lds[wv], sel[wv], lane);
+    if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  const int n = a.n, E = a.E;
+  const int e_mine = lane < n ? ids_lds[lane] : -1;
+  const bool v = valid_id(e_mine, E);
+  int pos = 0, c4[4] = {0, 0, 0, 0}, below4[4] = {0, 0, 0, 0};
+  for (int s2 = 0; s2 < n; ++s2) {
+    const int e2 = __builtin_amdgcn_readlane(e_mine, s2);
+    if (!valid_id(e2, E)) continue;
+    pos += (e2 < e_mine || (e2 == e_mine && s2 < lane)) ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c4[i] += (e2 == 4 * lane + i) ? 1 : 0;
+      below4[i] += (e2 < 4 * lane + i) ? 1 : 0;
+    }
+  }
+  if (v) {
+    a.perm[pos] = lane;
+    if (a.perm2) a.perm2[pos] = lane;
+  }
+  // active-list index and tile table: exclusive scans over experts (4 per lane)
+  int act4 = 0, tiles4 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    act4 += c4[i] > 0 ? 1 : 0;
+    tiles4 += (c4[i] + a.bm - 1) / a.bm;
+  }
+  int ia = act4, it = tiles4;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int xa = __shfl_up(ia, off, 64), xt = __shfl_up(it, off, 64);
+    if (lane >= off) {
+      ia += xa;
+      it += xt;
+    }
+  }
+  int aidx = ia - act4, tidx = it - tiles4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (e < E) {
+      a.counts[e] = c4[i];
+      a.offsets[e] = below4[i];
+      if (a.offsets2) a.offsets2[e] = below4[i];
+      a.tile_start[e] = tidx;
+      if (c4[i] > 0) a.active[aidx++] = e;
+      tidx += (c4[i] + a.bm - 1) / a.bm;
+    }
+  }
+  // totals (lane 63's inclusive scans), read with every lane active
+  const int n_act = __builtin_amdgcn_readlane(ia, 63);
+  const int n_tiles = __builtin_amdgcn_readlane(it, 63);
+  int nvalid = 0;
+  for (int s2 = 0; s2 < n; ++s2) nvalid += valid_id(__builtin_amdgcn_readlane(e_mine, s2), E) ? 1 : 0;
+  if (lane == 0) {
+    a.offsets[E] = nvalid;
+    if (a.offsets2) a.offsets2[E] = nvalid;
+    a.tile_start[E] = n_tiles;
+    *a.n_active = n_act;
+  }
+  if (lane >= nvalid && lane < n) {
+    a.perm[lane] = -1;
+    if (a.perm2) a.perm2[lane] = -1;
+  }
+}
+
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(1024), 0, s, t, a);
+  if (a.n <= 64) {
+    const int waves = t.T < 16 ? t.T : 16;
+    hipLaunchKernelGGL(route_permute_tiny_kernel, dim3(1), dim3(64 * waves), 0, s, t, a);
+  } else {
+    hipLaunchKernelGGL(route_permute_small_kernel, dim3(1), dim3(1024), 0, s, t, a);
+  }
   return hipGetLastError();
 }
 

@@ -298,13 +298,12 @@ hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s) {
 // Selection uses 64-bit keys (order-preserving value bits << 32 | ~index), so one
 // wave max picks the winner and breaks ties toward the lower index.
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  __shared__ float s_lds[4][256];
   __shared__ float c_lds[4][256];
   __shared__ int32_t sel_ids[4][32];
   const int wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= a.T) return;
-  topk_token(a, t, s_lds[wv], c_lds[wv], sel_ids[wv], threadIdx.x & 63);
+  topk_token(a, t, c_lds[wv], sel_ids[wv], threadIdx.x & 63);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {

@@ -29,72 +29,101 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// s, c: this wave's E-entry LDS scratch; sel: its k-entry LDS scratch. Writes
-// ids/w (and the optional copies) for token t; leaves the selected ids in sel.
-__device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* s, float* c,
-                                           int32_t* sel, int lane) {
+// Token t's grouped top-k by one wavefront, in registers: lane l holds experts
+// 4l .. 4l+3 (E <= 256). A group of gs experts spans gs/4 lanes when gs is a
+// multiple of 4 and gs/4 a power of two up to 16 (then the group's two largest
+// biased scores are merged across its lanes with shuffles); other group sizes go
+// through LDS scratch `c_lds` (E floats). Selected ids land in sel[0..k) (LDS) and
+// in ids/w (and the optional copies).
+__device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float o2) {
+  const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
+  m2 = fmaxf(lo, fmaxf(m2, o2));
+  m1 = hi;
+}
+
+__device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* c_lds, int32_t* sel,
+                                           int lane) {
   const int E = a.E, G = a.G, gs = E / G;
-  for (int e = lane; e < E; e += 64) {
-    float l = a.logits[t * E + e];
-    float sv = (float)(1.0 / (1.0 + exp(-(double)l)));
-    s[e] = sv;
-    c[e] = sv + a.bias[e];
-  }
-  wave_lds_sync();
-  // group scores: lane j < G scans its group
-  uint64_t gkey = 0;
-  if (lane < G) {
-    float m1 = -INFINITY, m2 = -INFINITY;
-    for (int q = 0; q < gs; ++q) {
-      float v = c[lane * gs + q];
-      if (v > m1) {
-        m2 = m1;
-        m1 = v;
-      } else if (v > m2) {
-        m2 = v;
-      }
+  float s[4], c[4];
+  const int e0 = 4 * lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const float l = a.logits[t * E + e];
+      s[i] = (float)(1.0 / (1.0 + exp(-(double)l)));
+      c[i] = s[i] + a.bias[e];
+    } else {
+      s[i] = 0.0f;
+      c[i] = -INFINITY;
     }
-    gkey = make_key(gs >= 2 ? m1 + m2 : m1, lane);
+  }
+  // group score: sum of the two largest biased scores of the group
+  uint64_t gkey = 0;
+  const int lpg = gs >> 2;  // lanes per group
+  const bool lane_groups = (gs & 3) == 0 && lpg <= 16 && (lpg & (lpg - 1)) == 0;
+  if (lane_groups) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) top2_merge(m1, m2, c[i], -INFINITY);
+    for (int off = 1; off < lpg; off <<= 1) {
+      const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
+      top2_merge(m1, m2, o1, o2);
+    }
+    const int j = lane / lpg;
+    if (j < G && (lane % lpg) == 0) gkey = make_key(gs >= 2 ? m1 + m2 : m1, j);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e0 + i < E) c_lds[e0 + i] = c[i];
+    wave_lds_sync();
+    if (lane < G) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int q = 0; q < gs; ++q) top2_merge(m1, m2, c_lds[lane * gs + q], -INFINITY);
+      gkey = make_key(gs >= 2 ? m1 + m2 : m1, lane);
+    }
   }
   // keep the kg best groups
   uint64_t kept = 0;  // bit j set: group j kept
   for (int r = 0; r < a.kg; ++r) {
-    uint64_t best = wave_max_u64(gkey);
-    int j = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    const uint64_t best = wave_max_u64(gkey);
+    const int j = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
     kept |= 1ull << (j & 63);
-    if (lane == j) gkey = 0;
+    if (gkey == best) gkey = 0;
   }
-  // candidate keys: each lane owns experts lane, lane + 64, lane + 128, lane + 192
   uint64_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
-    key[i] = (e < E && ((kept >> (e / gs)) & 1)) ? make_key(c[e], e) : 0;
+    const int e = e0 + i;
+    key[i] = (e < E && ((kept >> (e / gs)) & 1)) ? make_key(c[i], e) : 0;
   }
+  // k rounds of wave max; the winner's score is read from its owner lane
+  float my_s = 0.0f, den = 0.0f;
+  int my_e = 0;
   for (int j = 0; j < a.k; ++j) {
     uint64_t m = key[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i) m = key[i] > m ? key[i] : m;
-    uint64_t best = wave_max_u64(m);
-    int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    const uint64_t best = wave_max_u64(m);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (key[i] == best) key[i] = 0;
-    if (lane == 0) sel[j] = e;
-  }
-  wave_lds_sync();
-  // denominator in slot order (every lane computes the same sequential sum)
-  float den = 0.0f;
-  for (int j = 0; j < a.k; ++j) {
-    float sj = s[sel[j]];
-    den = (j == 0) ? sj : den + sj;
+    const int q = e & 3;
+    const float sv_local = q == 0 ? s[0] : q == 1 ? s[1] : q == 2 ? s[2] : s[3];
+    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv_local), e >> 2));
+    den = (j == 0) ? sv : den + sv;  // slot order
+    if (lane == j) {
+      my_s = sv;
+      my_e = e;
+    }
   }
   if (lane < a.k) {
-    int e = sel[lane];
-    float wj = (s[e] / den) * a.scale;
-    a.ids[t * a.k + lane] = e;
+    const float wj = (my_s / den) * a.scale;
+    sel[lane] = my_e;
+    a.ids[t * a.k + lane] = my_e;
     a.w[t * a.k + lane] = wj;
-    if (a.ids2) a.ids2[t * a.k + lane] = e;
+    if (a.ids2) a.ids2[t * a.k + lane] = my_e;
     if (a.w2) a.w2[t * a.k + lane] = wj;
   }
   wave_lds_sync();
