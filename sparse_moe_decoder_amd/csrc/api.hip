@@ -110,6 +110,7 @@ struct beam_moe_ctx {
   int32_t* n_active = nullptr; // [1]
   int32_t* tile_start = nullptr;  // [E + 1]
   int32_t* perm = nullptr;        // [maxT * k]
+  uint32_t* route_done = nullptr;  // [1] workgroup counter of the fused small-batch routing
   int32_t* block_cnt = nullptr;   // [nb * E]
   int32_t* block_base = nullptr;  // [nb * E]
   uint16_t* act = nullptr;        // [maxT * k, f]
@@ -227,7 +228,8 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
             dev_alloc(h, &h->w, slots) && dev_alloc(h, &h->counts, E) &&
             dev_alloc(h, &h->offsets, E + 1) && dev_alloc(h, &h->active, E) &&
             dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
-            dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->block_cnt, nb * E) &&
+            dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->route_done, 1) &&
+            dev_alloc(h, &h->block_cnt, nb * E) &&
             dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
             dev_alloc(h, &h->yk, slots * d);
   if (!ok) {
@@ -239,6 +241,7 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
                                 hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->route_done, 0, sizeof(uint32_t), s);
   if (e == hipSuccess)
     e = launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, (int)E, (int)f, (int)d, s);
   if (e == hipSuccess && E % 64 == 0)
@@ -336,16 +339,22 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
               h->tile_start, perm_out, offsets_out};
   if (!ids_in) {
     float* lg = logits_out ? logits_out : h->logits;
-    int st = run_router(h, T, z, lg, s);
-    if (st != BEAM_OK) return st;
     ids = h->ids;
     w = h->w;
     pa.ids = ids;
     TopkArgs ta = topk_args(h, T, lg, ids_out, w_out);
-    if (slots <= kPermChunk) {
+    if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
+      ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
+      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
+      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else if (slots <= kPermChunk) {
+      int st = run_router(h, T, z, lg, s);
+      if (st != BEAM_OK) return st;
       ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
       if (launch_route_permute_small(ta, pa, s) != hipSuccess) return BEAM_ERR_HIP;
     } else {
+      int st = run_router(h, T, z, lg, s);
+      if (st != BEAM_OK) return st;
       {
         ProfScope ps(K_TOPK, s);
         if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
@@ -372,7 +381,7 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
       ProfScope ps(K_GATEUP, s);
       if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
     }
-    if (T == 1 && k <= 16) {
+    if (T == 1 && k <= 16 && down_combine_t1_lds(k, c.d_ff) <= 61440) {
       ProfScope ps(K_DOWN, s);  // down projection + combine in one pass
       return hip_status(launch_down_combine_t1(ea, s));
     }

@@ -7,11 +7,11 @@
 // [SGLang "SGLang 支撑编程模型 Beam 生产部署", §三明治归一化与深度缩放残差]
 //   both scaled operands are rounded to BF16 before the add.
 //
-// One wavefront per token row. A row of d BF16 values is read as 16-byte
-// chunks, chunk c of the row going to lane c % 64 (consecutive lanes read
-// consecutive 16 bytes). For d <= 8192 the row stays in registers between the
-// three phases (sum of squares of x; scaled add and sum of squares of h';
-// pre-norm), so each row costs 2 reads and 2 writes of d BF16 values.
+// A row of d BF16 values is read as 16-byte chunks (consecutive lanes read
+// consecutive 16 bytes) and stays in registers between the three phases (sum of
+// squares of x; scaled add and sum of squares of h'; pre-norm), so each row costs
+// 2 reads and 2 writes of d BF16 values. Rows up to 8192 wide get a workgroup
+// each (one chunk per lane); wider rows one wavefront each.
 #include "common.h"
 #include "kernels.h"
 
@@ -57,7 +57,42 @@ __device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
   return 1.0f / sqrtf(ss / (float)d + eps);
 }
 
-// Register-resident variant: NC = max 16-byte chunks per lane.
+// One workgroup per row (rows up to 8192 wide): one 16-byte chunk per lane, W =
+// ceil(d / 512) waves. Each sum of squares is a per-lane sum of its chunk, a wave
+// sum, then the W wave sums added in wave order through LDS; every lane forms the
+// same total. The whole row is in flight after one round of loads.
+__global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a) {
+  __shared__ float red[2][16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int64_t t = blockIdx.x;
+  const int nch = a.d >> 3;
+  const int idx = threadIdx.x;
+  const bool ok = idx < nch;
+  const int li = ok ? idx : 0;
+  const u32x4 xv = ld_u32x4((const u32x4*)(a.x + t * a.d) + li);
+  u32x4 hv = ld_u32x4((const u32x4*)(a.h + t * a.d) + li);
+  const u32x4 wo = ld_u32x4((const u32x4*)a.w_post + li);
+  const u32x4 wr = ld_u32x4((const u32x4*)a.w_pre + li);
+  float ss = wave_sum(ok ? sumsq8(xv) : 0.0f);
+  if (lane == 0) red[0][wv] = ss;
+  __syncthreads();
+  ss = 0.0f;
+  for (int w = 0; w < nw; ++w) ss += red[0][w];
+  const float r = rms_scale(ss, a.d, a.eps);
+  float ss2 = 0.0f;
+  const u32x4 xn = norm8(xv, r, wo);
+  hv = residual8(hv, xn, a.c1, a.c2, ss2);
+  if (ok) st_u32x4((u32x4*)(a.h_out + t * a.d) + idx, hv);
+  ss2 = wave_sum(ok ? ss2 : 0.0f);
+  if (lane == 0) red[1][wv] = ss2;
+  __syncthreads();
+  ss2 = 0.0f;
+  for (int w = 0; w < nw; ++w) ss2 += red[1][w];
+  const float r2 = rms_scale(ss2, a.d, a.eps);
+  if (ok) st_u32x4((u32x4*)(a.z_out + t * a.d) + idx, norm8(hv, r2, wr));
+}
+
+// Register-resident variant (one wave per row): NC = max 16-byte chunks per lane.
 template <int NC>
 __global__ __launch_bounds__(256) void boundary_rows_kernel(BoundaryArgs a) {
   const int lane = threadIdx.x & 63;
@@ -135,6 +170,10 @@ __global__ __launch_bounds__(256) void boundary_rows_wide_kernel(BoundaryArgs a)
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s) {
   const int nch = a.d >> 3;
   const int nc = (nch + 63) / 64;
+  if (nc <= 16) {  // the choice depends on d only, so a row's result does not depend on T
+    hipLaunchKernelGGL(boundary_row_wg_kernel, dim3((unsigned)a.T), dim3(64 * nc), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
   if (nc <= 1)
     hipLaunchKernelGGL(boundary_rows_kernel<1>, grid, block, 0, s, a);

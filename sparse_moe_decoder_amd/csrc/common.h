@@ -95,6 +95,18 @@ __device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
+// Buffer loads: a raw buffer resource over `bytes` bytes from `base` (gfx9-family
+// resource word); a 16-byte load at a byte offset at or past `bytes` returns zeros
+// without touching memory, so rows that do not exist can issue the same
+// instruction as rows that do.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 ld_buf_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -26,6 +26,21 @@
 
 namespace beam {
 
+// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16 l (lds must be wave-uniform). Issued as inline assembly so the
+// compiler does not add its own conservative waits on the stage buffers; the
+// kernel waits explicitly (vmcnt) before a stage is read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+
 // ---------------------------------------------------------------------------------------------
 // Repack (init only)
 
@@ -81,8 +96,10 @@ hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t*
 
 __device__ __forceinline__ int expert_of_block(const ExpertArgs& a, int slot, int& row0,
                                                int& cnt) {
-  if (slot >= *a.n_active) return -1;
-  const int e = a.active[slot];
+  // slot < E, so active[slot] is in bounds: both loads are issued before either is used
+  const int na = *a.n_active, e = a.active[slot];
+  asm volatile("" ::"s"(na), "s"(e));
+  if (slot >= na) return -1;
   row0 = a.offsets[e];
   cnt = a.offsets[e + 1] - row0;
   return e;
@@ -98,40 +115,74 @@ __global__ __launch_bounds__(256) void gateup_stream_kernel(ExpertArgs a) {
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KS = a.d / 32, ksw = KS / 4, ks0 = wv * ksw;
   const uint16_t* bp = a.wgu + ((((int64_t)e * NJ + j) * KS + ks0) * 2) * 512 + lane * 8;
+  // the expert's rows are read through a buffer resource: rows past its count read
+  // zeros without memory traffic, so every k-step issues the same loads
+  const uint32_t zbytes = (uint32_t)a.T * a.d * 2;
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, zbytes);
   __shared__ f32x4 red[3][2 * MT][64];
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     f32x4 ag[MT], au[MT];
-    const uint16_t* ap[MT];
-    bool av[MT];
+    // the rows' slots are loaded first and used only after the weight prologue is
+    // issued: older than the weight loads, they never make those wait
+    int pv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       au[mt] = ag[mt];
       const int r = m0 + mt * 16 + (lane & 15);
-      av[mt] = r < cnt;
-      const int tok = av[mt] ? a.perm[row0 + r] / a.k : 0;
-      ap[mt] = a.z + (int64_t)tok * a.d + ks0 * 32 + 8 * (lane >> 4);
+      pv[mt] = a.perm[row0 + (r < cnt ? r : cnt - 1)];
     }
-    for (int ks = 0; ks < ksw; ks += U) {
-      u32x4 bg[U], bu[U], x[MT][U];
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t xo[MT];  // byte offsets of the rows' fragments in z; past the end for no row
+    // ring of U k-steps in flight: slot u is consumed, then refilled with the
+    // k-step U ahead, so the stream never drains until its last U steps
+    u32x4 bg[U], bu[U], x[MT][U];
+    auto load_b = [&](int u, int ks) {
+      bg[u] = ld_stream_u32x4(bp + (int64_t)ks * 1024);
+      bu[u] = ld_stream_u32x4(bp + (int64_t)ks * 1024 + 512);
+    };
+    auto load_x = [&](int u, int ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) x[mt][u] = ld_buf_u32x4(zr, xo[mt] + ks * 64);
+    };
+    auto load = [&](int u, int ks) {
+      load_b(u, ks);
+      load_x(u, ks);
+    };
+    auto use = [&](int u) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        ag[mt] = mfma16(x[mt][u], bg[u], ag[mt]);
+        au[mt] = mfma16(x[mt][u], bu[u], au[mt]);
+      }
+    };
+    // prologue: all U weight k-steps first (their addresses need only the expert),
+    // then the rows (which wait for the permutation)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_b(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = m0 + mt * 16 + (lane & 15);
+      xo[mt] = r < cnt ? 2u * (uint32_t)((pv[mt] / a.k) * a.d + ks0 * 32 + 8 * (lane >> 4)) : zbytes;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_x(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int ks = 0; ks < ksw - U; ks += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        bg[u] = ld_stream_u32x4(bp + ((int64_t)(ks + u) * 2 + 0) * 512);
-        bu[u] = ld_stream_u32x4(bp + ((int64_t)(ks + u) * 2 + 1) * 512);
+        use(u);
+        load(u, ks + U + u);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads in ring order
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          x[mt][u] = av[mt] ? ld_u32x4(ap[mt] + (ks + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          ag[mt] = mfma16(x[mt][u], bg[u], ag[mt]);
-          au[mt] = mfma16(x[mt][u], bu[u], au[mt]);
-        }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) use(u);
     if (wv > 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -177,31 +228,42 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
   if (e < 0) return;
   const int KS = a.f / 32;
   const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
+  const uint32_t abytes = (uint32_t)a.T * a.k * a.f * 2;  // rows past the count read zeros
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.act, abytes);
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     f32x4 acc[MT];
-    const uint16_t* ap[MT];
-    bool av[MT];
+    uint32_t xo[MT];  // byte offsets of the rows' fragments in act; past the end for no row
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = m0 + mt * 16 + (lane & 15);
-      av[mt] = r < cnt;
-      ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + 8 * (lane >> 4);
+      xo[mt] = r < cnt ? 2u * (uint32_t)((row0 + r) * a.f + 8 * (lane >> 4)) : abytes;
     }
-    for (int ks = 0; ks < KS; ks += U) {
-      u32x4 b[U], x[MT][U];
+    u32x4 b[U], x[MT][U];
+    auto load = [&](int u, int ks) {
+      b[u] = ld_stream_u32x4(bp + (int64_t)ks * 512);
 #pragma unroll
-      for (int u = 0; u < U; ++u) b[u] = ld_stream_u32x4(bp + (int64_t)(ks + u) * 512);
+      for (int mt = 0; mt < MT; ++mt) x[mt][u] = ld_buf_u32x4(ar, xo[mt] + ks * 64);
+    };
+    auto use = [&](int u) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
+    };
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          x[mt][u] = av[mt] ? ld_u32x4(ap[mt] + (ks + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    for (int ks = 0; ks < KS - U; ks += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        use(u);
+        load(u, ks + U + u);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads in ring order
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) use(u);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -220,34 +282,67 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
 // tile (16 x f) and keeps the token's row as the MFMA A operand. Each wave rounds
 // its weighted row (bf16(w_j * acc)), and the workgroup sums the k rows in slot
 // order in FP32 from -0.0 and rounds once, as the combine defines.
+// Each wave first copies its slot's activation row (f values) into LDS with
+// direct-to-LDS loads, then keeps only weight fragments in its register ring (U
+// k-steps deep); the A fragment (the row in lanes 0, 16, 32, 48, zeros elsewhere)
+// is read from LDS, so the row loads do not queue behind the weight stream.
+// Dynamic LDS: k * f * 2 bytes, plus 16 zero bytes.
 template <int U>
 __global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
-  __shared__ float part[32][16];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [k][f] rows, then 8 zeros
+  __shared__ float part[16][16];
   const int ND = a.d / 16;
   const int nt = blockIdx.x;
   const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int jw = __builtin_amdgcn_readfirstlane(j);
   const int KS = a.f / 32;
-  const int e = a.ids[j];
+  uint16_t* zero = xs + a.k * a.f;
+  if (threadIdx.x < 8) zero[threadIdx.x] = 0;
+  __syncthreads();
+  const int e = a.ids[jw];
   const bool valid = e >= 0 && e < a.E;
   if (valid) {
     // this slot's row in the expert-grouped order (slots ascend within an expert)
     int row = a.offsets[e];
-    for (int jj = 0; jj < j; ++jj) row += (a.ids[jj] == e) ? 1 : 0;
+    for (int jj = 0; jj < jw; ++jj) row += (a.ids[jj] == e) ? 1 : 0;
+    const uint16_t* src = a.act + (int64_t)row * a.f + lane * 8;
+    const uint32_t dst = lds_addr(xs + jw * a.f);
+    for (int c = 0; c < a.f; c += 512)  // lanes past the row's end stay idle
+      if (c + lane * 8 < a.f) lds_dma16(src + c, dst + c * 2);
     const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
-    const bool arow = (lane & 15) == 0;
-    const uint16_t* ap = a.act + (int64_t)row * a.f + 8 * (lane >> 4);
+    u32x4 b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b[u] = ld_stream_u32x4(bp + (int64_t)u * 512);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the row copies were issued before the U weight loads: wait for them only
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(U) : "memory");
+    const uint16_t* xrow = (lane & 15) == 0 ? xs + jw * a.f + 8 * (lane >> 4) : zero;
+    const int xstep = (lane & 15) == 0 ? 32 : 0;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < KS; ks += U) {
-      u32x4 b[U], x[U];
+    // the A fragment is read one k-step ahead; scheduling barriers keep the weight
+    // loads in ring order, so waiting for slot u never waits for a later refill
+    u32x4 xa = ld_u32x4(xrow);
+    for (int ks = 0; ks < KS - U; ks += U) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) b[u] = ld_stream_u32x4(bp + (int64_t)(ks + u) * 512);
+      for (int u = 0; u < U; ++u) {
+        const u32x4 xn = ld_u32x4(xrow + (ks + u + 1) * xstep);
+        acc = mfma16(xa, b[u], acc);
+        b[u] = ld_stream_u32x4(bp + (int64_t)(ks + U + u) * 512);
+        xa = xn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = arow ? ld_u32x4(ap + (ks + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < U; ++u) acc = mfma16(x[u], b[u], acc);
+    for (int u = 0; u < U; ++u) {
+      const int kn = KS - U + u + 1 < KS ? KS - U + u + 1 : KS - 1;
+      const u32x4 xn = ld_u32x4(xrow + kn * xstep);
+      acc = mfma16(xa, b[u], acc);
+      xa = xn;
     }
     // row 0 of D sits in register 0 of lanes 0..15
-    if (lane < 16) part[j][lane] = bf2f(f2bf(a.w[j] * acc[0]));
+    if (lane < 16) part[jw][lane] = bf2f(f2bf(a.w[jw] * acc[0]));
   }
   __syncthreads();
   if (j == 0 && lane < 16) {
@@ -260,15 +355,16 @@ __global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
   }
 }
 
+size_t down_combine_t1_lds(int k, int f) { return (size_t)k * f * 2 + 16; }
+
 hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s) {
   const int KS = a.f / 32;
   dim3 g((unsigned)(a.d / 16)), blk((unsigned)(64 * a.k));
-  if (KS % 8 == 0)
-    hipLaunchKernelGGL(down_combine_t1_kernel<8>, g, blk, 0, s, a);
-  else if (KS % 4 == 0)
-    hipLaunchKernelGGL(down_combine_t1_kernel<4>, g, blk, 0, s, a);
+  const size_t lds = down_combine_t1_lds(a.k, a.f);
+  if (KS % 16 == 0)
+    hipLaunchKernelGGL(down_combine_t1_kernel<16>, g, blk, lds, s, a);
   else
-    hipLaunchKernelGGL(down_combine_t1_kernel<2>, g, blk, 0, s, a);
+    hipLaunchKernelGGL(down_combine_t1_kernel<8>, g, blk, lds, s, a);
   return hipGetLastError();
 }
 
@@ -341,20 +437,6 @@ constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GSTAGES = 4;
 constexpr int GSTAGE_A = GBM * GBK, GSTAGE_B = GBN * GBK;  // elements per stage
 
 __device__ __forceinline__ int a_slot(int row, int c) { return row * GBK + ((c ^ ((row >> 2) & 3)) << 3); }
-
-// Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds + 16 l (lds must be wave-uniform). Issued as inline assembly so the
-// compiler does not add its own conservative waits on the stage buffers; the
-// kernel waits explicitly (vmcnt) before a stage is read.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds)
-               : "memory", "m0");
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {

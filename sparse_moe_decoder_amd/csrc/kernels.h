@@ -8,6 +8,8 @@ namespace beam {
 constexpr int kPermChunk = 1024;  // slots per permutation block (256 threads x 4 rounds)
 constexpr int kGemmBM = 256;      // rows per grouped-GEMM tile
 constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming expert path
+constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
+constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
 
 struct BoundaryArgs {
   int T, d;
@@ -89,11 +91,17 @@ hipError_t launch_router_bf16x3(const RouterX3Args& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 // grouped top-k + permutation in one launch; needs T * k <= kPermChunk
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s);
+// Router + grouped top-k + grouping in one launch for T <= 16 and T * k <= 64 (E
+// workgroups; `done` is a zeroed device counter owned by the caller, left zeroed).
+hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
+                                   uint32_t* done, hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);
 hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s);
 // T == 1, k <= 16: down projection and combine in one pass
+// dynamic LDS bytes the single-token down kernel needs (the api keeps it <= 60 KB)
+size_t down_combine_t1_lds(int k, int f);
 hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);

@@ -11,6 +11,7 @@
 // every run.
 #include "common.h"
 #include "kernels.h"
+#include "router_device.h"
 #include "topk_device.h"
 
 namespace beam {
@@ -238,22 +239,12 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, 
   }
 }
 
-// Tiny batches (T*k <= 64): the waves route one token each, then wave 0 holds one
-// slot per lane and computes everything by counting over the wave: a slot's row
+// Grouping of at most 64 slots by one wave, from the slot ids in LDS (one slot per
+// lane), everything by counting over the wave: a slot's row
 // is the number of valid slots ordered before it by (expert, slot); lane l owns
 // experts 4l .. 4l+3 for counts, offsets, the active list and the tile table.
-__global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, PermArgs a) {
-  __shared__ float c_lds[16][256];
-  __shared__ int32_t sel[16][32];
-  __shared__ int32_t ids_lds[64];
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int nw = blockDim.x >> 6;
-  for (int64_t t = wv; t < ta.T; t += nw) {
-    topk_token(ta, t, c_lds[wv], sel[wv], lane);
-    if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
-  }
-  __syncthreads();
-  if (wv != 0) return;
+__device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_t* ids_lds,
+                                                 int lane) {
   const int n = a.n, E = a.E;
   const int e_mine = lane < n ? ids_lds[lane] : -1;
   const bool v = valid_id(e_mine, E);
@@ -316,6 +307,66 @@ __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, P
     a.perm[lane] = -1;
     if (a.perm2) a.perm2[lane] = -1;
   }
+}
+
+// Tiny batches (T*k <= 64): the waves route one token each, then wave 0 groups.
+__global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, PermArgs a) {
+  __shared__ float c_lds[16][256];
+  __shared__ int32_t sel[16][32];
+  __shared__ int32_t ids_lds[64];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int nw = blockDim.x >> 6;
+  for (int64_t t = wv; t < ta.T; t += nw) {
+    topk_token(ta, t, c_lds[wv], sel[wv], lane);
+    if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  group_slots_wave(a, ids_lds, lane);
+}
+
+// Router, grouped top-k and grouping of a small batch (T <= 16 tokens, T * k <= 64
+// slots) in one launch: one workgroup per expert computes its logits exactly as the
+// stand-alone small-batch router does and publishes them with device-coherent
+// (write-through) stores, waits for those stores to complete, then counts itself
+// done on `done`. The workgroup that counts last (every other one has published)
+// resets the counter for the next launch and runs the top-k (one wave per token,
+// coherent loads) and the grouping. No workgroup waits on another.
+__global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, TopkArgs ta,
+                                                               PermArgs pa, uint32_t* done) {
+  __shared__ float part[3][kRouterRT];
+  __shared__ float c_lds[4][256];
+  __shared__ int32_t sel[4][32];
+  __shared__ int32_t ids_lds[64];
+  __shared__ int is_last;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.x;
+  const float v = router_small_dot(ra, e, 0, ra.T, part);
+  if (tid < ra.T)
+    __hip_atomic_store(ra.logits + (int64_t)tid * ra.E + e, v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = prev == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int t = wv; t < ta.T; t += 4) {
+    topk_token<true>(ta, t, c_lds[wv], sel[wv], lane);
+    if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
+  }
+  __syncthreads();
+  if (wv == 0) group_slots_wave(pa, ids_lds, lane);
+}
+
+hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
+                                   uint32_t* done, hipStream_t s) {
+  hipLaunchKernelGGL(route_fused_tiny_kernel, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a, done);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s) {

@@ -9,6 +9,7 @@
 //   FP32 routing coefficients, scale folded into the weights.
 #include "common.h"
 #include "kernels.h"
+#include "router_device.h"
 #include "topk_device.h"
 
 #include <type_traits>
@@ -20,7 +21,7 @@ namespace beam {
 // One wavefront per (expert, block of RT tokens): each lane walks 16-byte chunks
 // of W's row (chunk c -> lane c % 64) and keeps one FP32 partial per token; the
 // partials are then summed across the wave. W's row is read once per token block.
-constexpr int RT = 16;
+constexpr int RT = kRouterRT;
 
 __global__ __launch_bounds__(256) void router_fp32_kernel(RouterArgs a) {
   const int lane = threadIdx.x & 63;
@@ -56,50 +57,14 @@ __global__ __launch_bounds__(256) void router_fp32_kernel(RouterArgs a) {
 }
 
 // Small batches: one workgroup per (expert, block of RT tokens); its four waves
-// split d, so a W row is fetched by 256 lanes at once. Partials from the four
-// waves are added in wave order.
+// split d, so a W row is fetched by 256 lanes at once.
 __global__ __launch_bounds__(256) void router_fp32_small_kernel(RouterArgs a) {
-  __shared__ float part[3][RT];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ float part[3][kRouterRT];
   const int e = blockIdx.x;
-  const int t0 = blockIdx.y * RT;
-  const int nt = min(RT, a.T - t0);
-  const int nch = a.d >> 2, per = nch >> 2;  // 4-float chunks; d % 256 == 0
-  const f32x4* wr = (const f32x4*)(a.W + (int64_t)e * a.d) + wv * per;
-  float acc[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = 0.0f;
-  for (int c = lane; c < per; c += 64) {
-    f32x4 w = *(wr + c);
-    const int col = 4 * (wv * per + c);
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if (t < nt) {
-        const uint2 zz = *(const uint2*)(a.z + (int64_t)(t0 + t) * a.d + col);
-        acc[t] += lo_bf(zz.x) * w[0];
-        acc[t] += hi_bf(zz.x) * w[1];
-        acc[t] += lo_bf(zz.y) * w[2];
-        acc[t] += hi_bf(zz.y) * w[3];
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    if (t < nt) {
-      float v = wave_sum(acc[t]);
-      if (wv > 0 && lane == 0) part[wv - 1][t] = v;
-      acc[t] = v;
-    }
-  }
-  __syncthreads();
-  if (wv == 0 && lane < nt) {
-    float v = 0.0f;
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-      if (t == lane) v = acc[t];
-    v = ((v + part[0][lane]) + part[1][lane]) + part[2][lane];
-    a.logits[(int64_t)(t0 + lane) * a.E + e] = v;
-  }
+  const int t0 = blockIdx.y * kRouterRT;
+  const int nt = min(kRouterRT, a.T - t0);
+  const float v = router_small_dot(a, e, t0, nt, part);
+  if (threadIdx.x < nt) a.logits[(int64_t)(t0 + threadIdx.x) * a.E + e] = v;
 }
 
 // ---------------------------------------------------------------------------------------------

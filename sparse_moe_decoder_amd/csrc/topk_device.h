@@ -41,6 +41,9 @@ __device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float
   m1 = hi;
 }
 
+// COHERENT: read the logits with device-coherent loads (they were published within
+// the same launch by other workgroups' write-through stores).
+template <bool COHERENT = false>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* c_lds, int32_t* sel,
                                            int lane) {
   const int E = a.E, G = a.G, gs = E / G;
@@ -50,7 +53,9 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* 
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + i;
     if (e < E) {
-      const float l = a.logits[t * E + e];
+      const float l = COHERENT ? __hip_atomic_load(a.logits + t * E + e, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : a.logits[t * E + e];
       s[i] = (float)(1.0 / (1.0 + exp(-(double)l)));
       c[i] = s[i] + a.bias[e];
     } else {
