@@ -55,27 +55,34 @@ __device__ __forceinline__ float wave_sum(float v) {
 // commutative, so the reduction order does not matter: DPP moves (quad
 // permutes, row half-mirror, row mirror) give every lane its row's maximum, then
 // the four row maxima are read into scalar registers and compared there.
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Wave-wide maximum of a uint32, identical in every lane: DPP max within each row
+// of 16 lanes, then the four row results through SGPRs.
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
-  v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  uint64_t m = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-    m = max_u64(m, x);
-  }
-  return m;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_u32(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u32(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u32(v, dpp_u32<0x141>(v));  // row_half_mirror
+  v = max_u32(v, dpp_u32<0x140>(v));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max_u32(max_u32(r0, r1), max_u32(r2, r3));
+}
+
+// Lowest lane whose predicate holds (the predicate must hold somewhere).
+__device__ __forceinline__ int first_lane(bool pred) {
+  return __builtin_ctzll((unsigned long long)__ballot(pred));
+}
+
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // Order-preserving map of a finite FP32 value to uint32 (larger value -> larger key).

@@ -228,42 +228,33 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
   if (e < 0) return;
   const int KS = a.f / 32;
   const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
-  const uint32_t abytes = (uint32_t)a.T * a.k * a.f * 2;  // rows past the count read zeros
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.act, abytes);
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
     f32x4 acc[MT];
-    uint32_t xo[MT];  // byte offsets of the rows' fragments in act; past the end for no row
+    const uint16_t* ap[MT];
+    bool av[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = m0 + mt * 16 + (lane & 15);
-      xo[mt] = r < cnt ? 2u * (uint32_t)((row0 + r) * a.f + 8 * (lane >> 4)) : abytes;
+      av[mt] = r < cnt;
+      ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + 8 * (lane >> 4);
     }
-    u32x4 b[U], x[MT][U];
-    auto load = [&](int u, int ks) {
-      b[u] = ld_stream_u32x4(bp + (int64_t)ks * 512);
+    // U k-steps per batch; rows past the count are not loaded (masked lanes move no
+    // bytes), which measured faster here than a ring with zero-filling buffer loads
+    for (int ks = 0; ks < KS; ks += U) {
+      u32x4 b[U], x[MT][U];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) x[mt][u] = ld_buf_u32x4(ar, xo[mt] + ks * 64);
-    };
-    auto use = [&](int u) {
+      for (int u = 0; u < U; ++u) b[u] = ld_stream_u32x4(bp + (int64_t)(ks + u) * 512);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
-    };
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      load(u, u);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < U; ++u)
+          x[mt][u] = av[mt] ? ld_u32x4(ap[mt] + (ks + u) * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
     }
-    for (int ks = 0; ks < KS - U; ks += U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        use(u);
-        load(u, ks + U + u);
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads in ring order
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) use(u);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -243,15 +243,17 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, 
 // lane), everything by counting over the wave: a slot's row
 // is the number of valid slots ordered before it by (expert, slot); lane l owns
 // experts 4l .. 4l+3 for counts, offsets, the active list and the tile table.
+static_assert(kGemmBM >= 64, "the one-wave grouping assumes at most one tile per expert");
 __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_t* ids_lds,
                                                  int lane) {
   const int n = a.n, E = a.E;
   const int e_mine = lane < n ? ids_lds[lane] : -1;
   const bool v = valid_id(e_mine, E);
-  int pos = 0, c4[4] = {0, 0, 0, 0}, below4[4] = {0, 0, 0, 0};
+  int pos = 0, nvalid = 0, c4[4] = {0, 0, 0, 0}, below4[4] = {0, 0, 0, 0};
   for (int s2 = 0; s2 < n; ++s2) {
     const int e2 = __builtin_amdgcn_readlane(e_mine, s2);
     if (!valid_id(e2, E)) continue;
+    ++nvalid;
     pos += (e2 < e_mine || (e2 == e_mine && s2 < lane)) ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -263,23 +265,24 @@ __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_
     a.perm[pos] = lane;
     if (a.perm2) a.perm2[pos] = lane;
   }
-  // active-list index and tile table: exclusive scans over experts (4 per lane)
+  // active-list index and tile table: exclusive scans over experts (4 per lane). A
+  // lane's own counts are below 8 (at most 4 experts, one tile each: n <= bm), so
+  // each scan is three bit planes: ballot, then count the set lanes below.
   int act4 = 0, tiles4 = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     act4 += c4[i] > 0 ? 1 : 0;
     tiles4 += (c4[i] + a.bm - 1) / a.bm;
   }
-  int ia = act4, it = tiles4;
+  int aidx = 0, tidx = 0, n_act = 0, n_tiles = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int xa = __shfl_up(ia, off, 64), xt = __shfl_up(it, off, 64);
-    if (lane >= off) {
-      ia += xa;
-      it += xt;
-    }
+  for (int b = 0; b < 3; ++b) {
+    const uint64_t ba = __ballot((act4 >> b) & 1), bt = __ballot((tiles4 >> b) & 1);
+    aidx += lanes_below(ba) << b;
+    tidx += lanes_below(bt) << b;
+    n_act += __popcll(ba) << b;
+    n_tiles += __popcll(bt) << b;
   }
-  int aidx = ia - act4, tidx = it - tiles4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * lane + i;
@@ -292,11 +295,6 @@ __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_
       tidx += (c4[i] + a.bm - 1) / a.bm;
     }
   }
-  // totals (lane 63's inclusive scans), read with every lane active
-  const int n_act = __builtin_amdgcn_readlane(ia, 63);
-  const int n_tiles = __builtin_amdgcn_readlane(it, 63);
-  int nvalid = 0;
-  for (int s2 = 0; s2 < n; ++s2) nvalid += valid_id(__builtin_amdgcn_readlane(e_mine, s2), E) ? 1 : 0;
   if (lane == 0) {
     a.offsets[E] = nvalid;
     if (a.offsets2) a.offsets2[E] = nvalid;

@@ -11,17 +11,16 @@
 //   group score = sum of the two largest c of the group (the c itself if E/G = 1)
 //   keep kg groups, then k experts, each by (value desc, index asc)
 //   w_j = (s_j / den) * scale, den summed over the slots in order
-// Selection uses 64-bit keys (order-preserving value bits << 32 | ~index), so one
-// wave max picks the winner and breaks ties toward the lower index.
+// Selection: each candidate's value becomes an order-preserving 32-bit key; a
+// round takes the wave maximum of the lanes' best keys and the lowest lane that
+// holds it. Lane l holds experts 4l .. 4l+3 and prefers its lowest index among
+// equal keys, so the winner is the lowest index of the largest value: the order is
+// (value desc, index asc) exactly.
 #pragma once
 #include "common.h"
 #include "kernels.h"
 
 namespace beam {
-
-__device__ __forceinline__ uint64_t make_key(float v, int idx) {
-  return ((uint64_t)f32_order_key(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
@@ -63,8 +62,10 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* 
       c[i] = -INFINITY;
     }
   }
-  // group score: sum of the two largest biased scores of the group
-  uint64_t gkey = 0;
+  // group score: sum of the two largest biased scores of the group; the group's
+  // key sits in the lowest lane of the group (groups ascend with lanes)
+  uint32_t gkey = 0;
+  int gof = 0;  // group held by this lane
   const int lpg = gs >> 2;  // lanes per group
   const bool lane_groups = (gs & 3) == 0 && lpg <= 16 && (lpg & (lpg - 1)) == 0;
   if (lane_groups) {
@@ -75,48 +76,57 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* 
       const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
       top2_merge(m1, m2, o1, o2);
     }
-    const int j = lane / lpg;
-    if (j < G && (lane % lpg) == 0) gkey = make_key(gs >= 2 ? m1 + m2 : m1, j);
+    gof = lane / lpg;
+    if (gof < G && (lane % lpg) == 0) gkey = f32_order_key(gs >= 2 ? m1 + m2 : m1);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (e0 + i < E) c_lds[e0 + i] = c[i];
     wave_lds_sync();
+    gof = lane;
     if (lane < G) {
       float m1 = -INFINITY, m2 = -INFINITY;
       for (int q = 0; q < gs; ++q) top2_merge(m1, m2, c_lds[lane * gs + q], -INFINITY);
-      gkey = make_key(gs >= 2 ? m1 + m2 : m1, lane);
+      gkey = f32_order_key(gs >= 2 ? m1 + m2 : m1);
     }
   }
-  // keep the kg best groups
+  // keep the kg best groups (ties: lower group)
   uint64_t kept = 0;  // bit j set: group j kept
   for (int r = 0; r < a.kg; ++r) {
-    const uint64_t best = wave_max_u64(gkey);
-    const int j = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    const uint32_t best = wave_max_u32(gkey);
+    const int L = first_lane(gkey == best);
+    const int j = __builtin_amdgcn_readlane(gof, L);
     kept |= 1ull << (j & 63);
-    if (gkey == best) gkey = 0;
+    if (lane == L) gkey = 0;
   }
-  uint64_t key[4];
+  uint32_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + i;
-    key[i] = (e < E && ((kept >> (e / gs)) & 1)) ? make_key(c[i], e) : 0;
+    key[i] = (e < E && ((kept >> (e / gs)) & 1)) ? f32_order_key(c[i]) : 0u;
   }
-  // k rounds of wave max; the winner's score is read from its owner lane
+  // k rounds: the lane's best candidate (lowest index among equal keys), the wave's
+  // best key, the lowest lane holding it; the winner's score comes from that lane
   float my_s = 0.0f, den = 0.0f;
   int my_e = 0;
   for (int j = 0; j < a.k; ++j) {
-    uint64_t m = key[0];
+    uint32_t lm = key[0];
+    int li = 0;
 #pragma unroll
-    for (int i = 1; i < 4; ++i) m = key[i] > m ? key[i] : m;
-    const uint64_t best = wave_max_u64(m);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    for (int i = 1; i < 4; ++i)
+      if (key[i] > lm) {
+        lm = key[i];
+        li = i;
+      }
+    const uint32_t best = wave_max_u32(lm);
+    const int L = first_lane(lm == best);
+    const int q = __builtin_amdgcn_readlane(li, L);
+    const int e = 4 * L + q;
+    const float sl = li == 0 ? s[0] : li == 1 ? s[1] : li == 2 ? s[2] : s[3];
+    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sl), L));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (key[i] == best) key[i] = 0;
-    const int q = e & 3;
-    const float sv_local = q == 0 ? s[0] : q == 1 ? s[1] : q == 2 ? s[2] : s[3];
-    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv_local), e >> 2));
+      if (lane == L && i == li) key[i] = 0u;
     den = (j == 0) ? sv : den + sv;  // slot order
     if (lane == j) {
       my_s = sv;
