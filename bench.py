@@ -224,8 +224,8 @@ def main():
         # token rows in, the activations out
         bytes_gu = mean_distinct * 2 * wl.f * wl.d * 2 + T * wl.d * 2 + T * wl.k * wl.f * 2
         achieved = bytes_gu / (gu_us * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4))
+        roof = dict(kernel="gate_up", bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4))
         traffic = read_traffic("gate_up", wl.name, src)
         roof["traffic"] = traffic
         step_bytes = (mean_distinct * 3 * wl.f * wl.d * 2 + wl.E * wl.d * 4
@@ -235,8 +235,9 @@ def main():
     else:
         flops_gu = 2.0 * T * wl.k * (2 * wl.f) * wl.d
         achieved = flops_gu / (gu_us * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / BF16_PEAK_TFLOPS, 4))
+        roof = dict(kernel="gate_up", bound="mfma", achieved=round(achieved, 1),
+                    peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4))
         roof["traffic"] = read_traffic("gate_up", wl.name, src)
         step_flops = 2.0 * T * wl.k * 3 * wl.f * wl.d
         whole = dict(expert_flops=step_flops, mfma_frac=round(

@@ -282,6 +282,7 @@ template <int U>
 __global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [k][f] rows, then 8 zeros
   __shared__ float part[16][16];
+  __shared__ int sid[16];
   const int ND = a.d / 16;
   const int nt = blockIdx.x;
   const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -289,13 +290,14 @@ __global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
   const int KS = a.f / 32;
   uint16_t* zero = xs + a.k * a.f;
   if (threadIdx.x < 8) zero[threadIdx.x] = 0;
+  if (threadIdx.x < a.k) sid[threadIdx.x] = a.ids[threadIdx.x];  // all slot ids, one load
   __syncthreads();
-  const int e = a.ids[jw];
+  const int e = sid[jw];
   const bool valid = e >= 0 && e < a.E;
   if (valid) {
     // this slot's row in the expert-grouped order (slots ascend within an expert)
     int row = a.offsets[e];
-    for (int jj = 0; jj < jw; ++jj) row += (a.ids[jj] == e) ? 1 : 0;
+    for (int jj = 0; jj < jw; ++jj) row += (sid[jj] == e) ? 1 : 0;
     const uint16_t* src = a.act + (int64_t)row * a.f + lane * 8;
     const uint32_t dst = lds_addr(xs + jw * a.f);
     for (int c = 0; c < a.f; c += 512)  // lanes past the row's end stay idle
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
   if (j == 0 && lane < 16) {
     float sum = -0.0f;
     for (int jj = 0; jj < a.k; ++jj) {
-      const int ej = a.ids[jj];
+      const int ej = sid[jj];
       if (ej >= 0 && ej < a.E) sum += part[jj][lane];
     }
     a.y[nt * 16 + lane] = f2bf(sum);

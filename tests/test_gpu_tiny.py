@@ -175,6 +175,31 @@ def test_batch_invariance(gpu, host):
         assert np.array_equal(one[0], full[t])
 
 
+def test_single_token_paths_agree(gpu, host):
+    """One token: the single-token down-and-combine pass equals the batched path
+    (separate down and combine) on the same token, routing replayed so both see
+    the same ids and weights, over repeated calls; the grouping tables of a
+    single-token call are valid."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    moe = gpu["moe"]
+    z = P.to_dev(host["z"])
+    T = z.shape[0]
+    _, ids, w = moe.router_topk(z, want_logits=False)
+    full = P.bits(moe.forward(z, ids_in=ids, w_in=w))
+    for rep in range(3):
+        for t in range(T):
+            one = P.bits(moe.forward(z[t:t + 1].contiguous(), ids_in=ids[t:t + 1].contiguous(),
+                                     w_in=w[t:t + 1].contiguous()))
+            assert np.array_equal(one[0], full[t]), (rep, t)
+    k = ids.shape[1]
+    y1 = torch.empty((1, z.shape[1]), dtype=torch.bfloat16, device="cuda")
+    perm = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    offs = torch.full((WL.E + 1,), -7, dtype=torch.int32, device="cuda")
+    beam.beam_moe_forward(moe.handle, z[:1].contiguous(), y1, perm_out=perm, offsets_out=offs)
+    P.check_permutation_valid(ids[:1].cpu().numpy(), perm.cpu().numpy(), offs.cpu().numpy(), WL.E)
+
+
 def test_edge_sizes(gpu, host):
     """T = 0 is a no-op; T = max_tokens works; T > max_tokens is rejected up front."""
     import torch
