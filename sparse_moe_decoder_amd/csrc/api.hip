@@ -374,19 +374,19 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk, y_out, ids};
+                h->n_active, h->tile_start, w, h->act, h->yk};
   if (T <= kStreamMaxT) {
     const int max_active = slots < E ? slots : E;
     {
       ProfScope ps(K_GATEUP, s);
       if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
     }
-    if (T == 1 && k <= 16 && down_combine_t1_lds(k, c.d_ff) <= 61440) {
-      ProfScope ps(K_DOWN, s);  // down projection + combine in one pass
-      return hip_status(launch_down_combine_t1(ea, s));
-    }
     ProfScope ps(K_DOWN, s);
-    if (launch_down_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    if (T <= kSplitDownMaxT) {
+      if (launch_down_split(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else if (launch_down_stream(ea, max_active, s) != hipSuccess) {
+      return BEAM_ERR_HIP;
+    }
   } else {
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
     {

@@ -268,97 +268,87 @@ __global__ __launch_bounds__(256) void down_stream_kernel(ExpertArgs a) {
   }
 }
 
-// Single token: down projection and combine in one pass with no cross-workgroup
-// traffic. A workgroup owns 16 output columns; its wave j streams slot j's expert
-// tile (16 x f) and keeps the token's row as the MFMA A operand. Each wave rounds
-// its weighted row (bf16(w_j * acc)), and the workgroup sums the k rows in slot
-// order in FP32 from -0.0 and rounds once, as the combine defines.
-// Each wave first copies its slot's activation row (f values) into LDS with
-// direct-to-LDS loads, then keeps only weight fragments in its register ring (U
-// k-steps deep); the A fragment (the row in lanes 0, 16, 32, 48, zeros elsewhere)
-// is read from LDS, so the row loads do not queue behind the weight stream.
-// Dynamic LDS: k * f * 2 bytes, plus 16 zero bytes.
-template <int U>
-__global__ __launch_bounds__(1024) void down_combine_t1_kernel(ExpertArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [k][f] rows, then 8 zeros
-  __shared__ float part[16][16];
-  __shared__ int sid[16];
+// Down projection for batches of up to 16 tokens, split like gate/up: one
+// workgroup per (active expert, 16 output columns); its four waves split K (f) into
+// quarters, each streaming its stretch of the packed weights through a ring of U
+// k-steps (16-byte non-temporal loads), with the expert's rows (at most 16 per
+// pass; rows past the count are not loaded) as the MFMA A operand. The quarters are
+// added in wave order, then bf16(w * sum) is written to the row's slot; the combine
+// pass sums the slots. Small batches give few experts, so this spreads the weight
+// stream over many small workgroups (2560 for one token: ten per CU, evenly) where
+// one workgroup per 16 columns and all slots would leave some CUs with twice the
+// work of others. Every T served here uses this same order, so a token's result
+// does not depend on the batch.
+template <int MT, int U>
+__global__ __launch_bounds__(256) void down_split_kernel(ExpertArgs a) {
   const int ND = a.d / 16;
-  const int nt = blockIdx.x;
-  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int jw = __builtin_amdgcn_readfirstlane(j);
-  const int KS = a.f / 32;
-  uint16_t* zero = xs + a.k * a.f;
-  if (threadIdx.x < 8) zero[threadIdx.x] = 0;
-  if (threadIdx.x < a.k) sid[threadIdx.x] = a.ids[threadIdx.x];  // all slot ids, one load
-  __syncthreads();
-  const int e = sid[jw];
-  const bool valid = e >= 0 && e < a.E;
-  if (valid) {
-    // this slot's row in the expert-grouped order (slots ascend within an expert)
-    int row = a.offsets[e];
-    for (int jj = 0; jj < jw; ++jj) row += (sid[jj] == e) ? 1 : 0;
-    const uint16_t* src = a.act + (int64_t)row * a.f + lane * 8;
-    const uint32_t dst = lds_addr(xs + jw * a.f);
-    for (int c = 0; c < a.f; c += 512)  // lanes past the row's end stay idle
-      if (c + lane * 8 < a.f) lds_dma16(src + c, dst + c * 2);
-    const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + lane * 8;
-    u32x4 b[U];
+  const int nt = blockIdx.x % ND;
+  int row0, cnt;
+  const int e = expert_of_block(a, blockIdx.x / ND, row0, cnt);
+  if (e < 0) return;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KS = a.f / 32, ksw = KS / 4, ks0 = wv * ksw;
+  const uint16_t* bp = a.wdp + ((int64_t)e * ND + nt) * KS * 512 + (int64_t)ks0 * 512 + lane * 8;
+  const uint32_t abytes = (uint32_t)a.T * a.k * a.f * 2;
+  __shared__ f32x4 red[3][MT][64];
+  for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+    f32x4 acc[MT];
+    uint32_t xo[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = m0 + mt * 16 + (lane & 15);
+      xo[mt] = r < cnt ? 2u * (uint32_t)((row0 + r) * a.f + ks0 * 32 + 8 * (lane >> 4)) : abytes;
+    }
+    u32x4 b[U], x[MT][U];
+    auto load = [&](int u, int ks) {
+      b[u] = ld_stream_u32x4(bp + (int64_t)ks * 512);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        x[mt][u] = xo[mt] < abytes ? ld_u32x4((const char*)a.act + xo[mt] + ks * 64)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      b[u] = ld_stream_u32x4(bp + (int64_t)u * 512);
+      load(u, u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the row copies were issued before the U weight loads: wait for them only
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(U) : "memory");
-    const uint16_t* xrow = (lane & 15) == 0 ? xs + jw * a.f + 8 * (lane >> 4) : zero;
-    const int xstep = (lane & 15) == 0 ? 32 : 0;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the A fragment is read one k-step ahead; scheduling barriers keep the weight
-    // loads in ring order, so waiting for slot u never waits for a later refill
-    u32x4 xa = ld_u32x4(xrow);
-    for (int ks = 0; ks < KS - U; ks += U) {
+    for (int ks = 0; ks < ksw - U; ks += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const u32x4 xn = ld_u32x4(xrow + (ks + u + 1) * xstep);
-        acc = mfma16(xa, b[u], acc);
-        b[u] = ld_stream_u32x4(bp + (int64_t)(ks + U + u) * 512);
-        xa = xn;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
+        load(u, ks + U + u);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kn = KS - U + u + 1 < KS ? KS - U + u + 1 : KS - 1;
-      const u32x4 xn = ld_u32x4(xrow + kn * xstep);
-      acc = mfma16(xa, b[u], acc);
-      xa = xn;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u], b[u], acc[mt]);
+    if (wv > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[wv - 1][mt][lane] = acc[mt];
     }
-    // row 0 of D sits in register 0 of lanes 0..15
-    if (lane < 16) part[jw][lane] = bf2f(f2bf(a.w[jw] * acc[0]));
-  }
-  __syncthreads();
-  if (j == 0 && lane < 16) {
-    float sum = -0.0f;
-    for (int jj = 0; jj < a.k; ++jj) {
-      const int ej = sid[jj];
-      if (ej >= 0 && ej < a.E) sum += part[jj][lane];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 v = acc[mt];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) v += red[w][mt][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+          if (r < cnt) {
+            const int slot = a.perm[row0 + r];
+            a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * v[i]);
+          }
+        }
+      }
     }
-    a.y[nt * 16 + lane] = f2bf(sum);
+    __syncthreads();
   }
-}
-
-size_t down_combine_t1_lds(int k, int f) { return (size_t)k * f * 2 + 16; }
-
-hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s) {
-  const int KS = a.f / 32;
-  dim3 g((unsigned)(a.d / 16)), blk((unsigned)(64 * a.k));
-  const size_t lds = down_combine_t1_lds(a.k, a.f);
-  if (KS % 16 == 0)
-    hipLaunchKernelGGL(down_combine_t1_kernel<16>, g, blk, lds, s, a);
-  else
-    hipLaunchKernelGGL(down_combine_t1_kernel<8>, g, blk, lds, s, a);
-  return hipGetLastError();
 }
 
 template <int MT>
@@ -384,6 +374,18 @@ hipError_t launch_down_stream_mt(const ExpertArgs& a, int max_active, hipStream_
     hipLaunchKernelGGL((down_stream_kernel<MT, 4>), g, blk, 0, s, a);
   else
     hipLaunchKernelGGL((down_stream_kernel<MT, 2>), g, blk, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_split(const ExpertArgs& a, int max_active, hipStream_t s) {
+  const int ksw = a.f / 32 / 4;  // k-steps per wave (f % 256 == 0: a multiple of 2)
+  dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
+  if (ksw % 10 == 0)
+    hipLaunchKernelGGL((down_split_kernel<1, 10>), g, blk, 0, s, a);
+  else if (ksw % 5 == 0)
+    hipLaunchKernelGGL((down_split_kernel<1, 5>), g, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL((down_split_kernel<1, 2>), g, blk, 0, s, a);
   return hipGetLastError();
 }
 

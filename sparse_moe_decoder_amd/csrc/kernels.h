@@ -8,6 +8,7 @@ namespace beam {
 constexpr int kPermChunk = 1024;  // slots per permutation block (256 threads x 4 rounds)
 constexpr int kGemmBM = 256;      // rows per grouped-GEMM tile
 constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming expert path
+constexpr int kSplitDownMaxT = 16;  // largest T whose down pass splits K over four waves
 constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
 constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
 
@@ -78,9 +79,6 @@ struct ExpertArgs {
   const float* w;             // [T*k] routing weight by slot
   uint16_t* act;              // [T*k, f] by row (expert-grouped order)
   uint16_t* yk;               // [T*k, d] by slot t*k+j
-  // single-token down + combine: output and routing ids
-  uint16_t* y;                // [T, d]
-  const int32_t* ids;         // [T, k]
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
@@ -98,11 +96,10 @@ hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);
+// down for T <= kSplitDownMaxT with K split over four waves (then launch_combine)
+hipError_t launch_down_split(const ExpertArgs& a, int max_active, hipStream_t s);
 hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s);
 // T == 1, k <= 16: down projection and combine in one pass
-// dynamic LDS bytes the single-token down kernel needs (the api keeps it <= 60 KB)
-size_t down_combine_t1_lds(int k, int f);
-hipError_t launch_down_combine_t1(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,

@@ -176,10 +176,9 @@ def test_batch_invariance(gpu, host):
 
 
 def test_single_token_paths_agree(gpu, host):
-    """One token: the single-token down-and-combine pass equals the batched path
-    (separate down and combine) on the same token, routing replayed so both see
-    the same ids and weights, over repeated calls; the grouping tables of a
-    single-token call are valid."""
+    """One token alone equals the same token inside a batch (routing replayed, so
+    both see the same ids and weights), over repeated calls; the grouping tables
+    of a single-token call are valid."""
     import torch
     import sparse_moe_decoder_amd as beam
     moe = gpu["moe"]
