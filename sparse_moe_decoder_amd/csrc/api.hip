@@ -111,6 +111,7 @@ struct beam_moe_ctx {
   int32_t* tile_start = nullptr;  // [E + 1]
   int32_t* perm = nullptr;        // [maxT * k]
   uint32_t* route_done = nullptr;  // [1] workgroup counter of the fused small-batch routing
+  uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
   int32_t* block_cnt = nullptr;   // [nb * E]
   int32_t* block_base = nullptr;  // [nb * E]
   uint16_t* act = nullptr;        // [maxT * k, f]
@@ -229,6 +230,7 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
             dev_alloc(h, &h->offsets, E + 1) && dev_alloc(h, &h->active, E) &&
             dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
             dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->route_done, 1) &&
+            dev_alloc(h, &h->route_sc, (size_t)kFusedRouteMaxT * E) &&
             dev_alloc(h, &h->block_cnt, nb * E) &&
             dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
             dev_alloc(h, &h->yk, slots * d);
@@ -346,7 +348,8 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
       ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
       RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, s) != hipSuccess) return BEAM_ERR_HIP;
+      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
+        return BEAM_ERR_HIP;
     } else if (slots <= kPermChunk) {
       int st = run_router(h, T, z, lg, s);
       if (st != BEAM_OK) return st;

@@ -90,9 +90,10 @@ hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 // grouped top-k + permutation in one launch; needs T * k <= kPermChunk
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s);
 // Router + grouped top-k + grouping in one launch for T <= 16 and T * k <= 64 (E
-// workgroups; `done` is a zeroed device counter owned by the caller, left zeroed).
+// workgroups; `done` is a zeroed device counter owned by the caller, left zeroed;
+// `sc` is caller-owned scratch of T * E 64-bit words for the published scores).
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
-                                   uint32_t* done, hipStream_t s);
+                                   uint32_t* done, uint64_t* sc, hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);

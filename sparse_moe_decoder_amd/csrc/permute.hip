@@ -325,13 +325,16 @@ __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, P
 
 // Router, grouped top-k and grouping of a small batch (T <= 16 tokens, T * k <= 64
 // slots) in one launch: one workgroup per expert computes its logits exactly as the
-// stand-alone small-batch router does and publishes them with device-coherent
-// (write-through) stores, waits for those stores to complete, then counts itself
-// done on `done`. The workgroup that counts last (every other one has published)
-// resets the counter for the next launch and runs the top-k (one wave per token,
-// coherent loads) and the grouping. No workgroup waits on another.
+// stand-alone small-batch router does, writes them out, and publishes each token's
+// (score, biased score) pair for its expert (computed as the top-k computes them)
+// with device-coherent (write-through) stores; it waits for those stores to
+// complete, then counts itself done on `done`. The workgroup that counts last
+// (every other one has published) resets the counter for the next launch and runs
+// the top-k (one wave per token, coherent loads of the pairs) and the grouping. No
+// workgroup waits on another.
 __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, TopkArgs ta,
-                                                               PermArgs pa, uint32_t* done) {
+                                                               PermArgs pa, uint32_t* done,
+                                                               uint64_t* sc) {
   __shared__ float part[3][kRouterRT];
   __shared__ float c_lds[4][256];
   __shared__ int32_t sel[4][32];
@@ -339,10 +342,15 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   __shared__ int is_last;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
+  const float bias = ta.bias[e];
   const float v = router_small_dot(ra, e, 0, ra.T, part);
-  if (tid < ra.T)
-    __hip_atomic_store(ra.logits + (int64_t)tid * ra.E + e, v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < ra.T) {
+    ra.logits[(int64_t)tid * ra.E + e] = v;
+    const float sv = routing_score(v), cv = sv + bias;
+    __hip_atomic_store(sc + (int64_t)tid * ra.E + e,
+                       (uint64_t)__float_as_uint(sv) | ((uint64_t)__float_as_uint(cv) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's stores are complete
   __syncthreads();
   if (tid == 0) {
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int t = wv; t < ta.T; t += 4) {
-    topk_token<true>(ta, t, c_lds[wv], sel[wv], lane);
+    topk_token<true>(ta, t, c_lds[wv], sel[wv], lane, sc);
     if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
   }
   __syncthreads();
@@ -362,8 +370,9 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
 }
 
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
-                                   uint32_t* done, hipStream_t s) {
-  hipLaunchKernelGGL(route_fused_tiny_kernel, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a, done);
+                                   uint32_t* done, uint64_t* sc, hipStream_t s) {
+  hipLaunchKernelGGL(route_fused_tiny_kernel, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a, done,
+                     sc);
   return hipGetLastError();
 }
 

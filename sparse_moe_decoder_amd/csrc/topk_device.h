@@ -40,11 +40,17 @@ __device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float
   m1 = hi;
 }
 
-// COHERENT: read the logits with device-coherent loads (they were published within
-// the same launch by other workgroups' write-through stores).
-template <bool COHERENT = false>
+// The routing score of a logit: sigmoid in double, rounded once to FP32.
+__device__ __forceinline__ float routing_score(float l) {
+  return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
+// SCORES: instead of logits, read each expert's (score s, biased score c) pair from
+// `sc` [T, E] (s in the low 32 bits) with device-coherent loads: the pairs were
+// published within the same launch by other workgroups' write-through stores.
+template <bool SCORES = false>
 __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* c_lds, int32_t* sel,
-                                           int lane) {
+                                           int lane, const uint64_t* sc = nullptr) {
   const int E = a.E, G = a.G, gs = E / G;
   float s[4], c[4];
   const int e0 = 4 * lane;
@@ -52,11 +58,14 @@ __device__ __forceinline__ void topk_token(const TopkArgs& a, int64_t t, float* 
   for (int i = 0; i < 4; ++i) {
     const int e = e0 + i;
     if (e < E) {
-      const float l = COHERENT ? __hip_atomic_load(a.logits + t * E + e, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : a.logits[t * E + e];
-      s[i] = (float)(1.0 / (1.0 + exp(-(double)l)));
-      c[i] = s[i] + a.bias[e];
+      if constexpr (SCORES) {
+        const uint64_t p = __hip_atomic_load(sc + t * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s[i] = __uint_as_float((uint32_t)p);
+        c[i] = __uint_as_float((uint32_t)(p >> 32));
+      } else {
+        s[i] = routing_score(a.logits[t * E + e]);
+        c[i] = s[i] + a.bias[e];
+      }
     } else {
       s[i] = 0.0f;
       c[i] = -INFINITY;
