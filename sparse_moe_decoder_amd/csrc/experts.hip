@@ -680,15 +680,27 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int d, int E
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[t * k + j];
-    if (e < 0 || e >= E) continue;
-    const u32x4 v = ld_u32x4(yk + ((t * k + j) * d) + c * 8);
+  // slots in chunks of eight: all ids, then all rows in flight, then the adds in order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    bool ok[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += lo_bf(v[i]);
-      acc[2 * i + 1] += hi_bf(v[i]);
+    for (int u = 0; u < 8; ++u) {
+      const int e = j0 + u < k ? ids[t * k + j0 + u] : -1;
+      ok[u] = e >= 0 && e < E;
     }
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = ld_u32x4(yk + ((t * k + (ok[u] ? j0 + u : 0)) * d) + c * 8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (ok[u]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += lo_bf(v[u][i]);
+          acc[2 * i + 1] += hi_bf(v[u][i]);
+        }
+      }
   }
   u32x4 o;
 #pragma unroll
