@@ -402,24 +402,30 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 // ---------------------------------------------------------------------------------------------
 // Prefill path: grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// A workgroup (4 waves) computes up to 256 rows x 256 columns of one expert: rows
-// are that expert's assignment rows (gathered through the permutation for
-// gate/up: the z rows of their tokens), columns are 128 gate + 128 up outputs
-// (gate/up) or 256 outputs (down). Wave w owns all rows x columns [64 w, 64 w + 64)
-// as 8 x 2 MFMA tiles (256 accumulators per lane); the body is instantiated for
-// the number of 32-row tiles that hold rows (1..8), so an expert's last, partial
-// tile skips the empty ones.
-// K advances 32 at a time through four LDS stages filled by direct
-// global-to-LDS 16-byte loads (global_load_lds_dwordx4: each lane's 16 bytes land
-// at the stage base + 16 * lane), three K blocks ahead of the multiply, with one
-// barrier per K block and no staging registers.
+// A workgroup (8 waves, two per SIMD) computes up to 256 rows x 256 columns of one
+// expert: rows are that expert's assignment rows (gathered through the permutation
+// for gate/up: the z rows of their tokens), columns are 128 gate + 128 up outputs
+// (gate/up) or 256 outputs (down). Wave w = 4 wm + wn owns the 32-row tiles
+// 2 mt + wm (mt < MW) x columns [64 wn, 64 wn + 64) as MW x 2 MFMA tiles; MW =
+// ceil(rows / 64), the same for every wave, so a partial tile costs in 64-row steps.
+// An expert's rows are cut into ceil(rows / 256) tiles of equal size (a multiple of
+// 64), so the tiles that share one weight tile take the same time.
+//
+// K advances 32 at a time through NS LDS stages (NS = 5 when K / 32 is a multiple
+// of 5, else 4) filled by direct global-to-LDS 16-byte loads (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the stage base + 16 * lane), NS - 1 K blocks ahead of
+// the multiply, with one barrier per K block and no staging registers. Loads take
+// a few microseconds under this traffic, so the depth of the ring (up to 128 KB in
+// flight per CU) sets the speed more than any other choice here. A wave's four
+// copies of a K block are spread between its MFMAs, so a full memory queue stalls
+// one MFMA group instead of the fragment reads of the whole block.
 //   A stage: 256 rows x 32 values, 64 bytes per row; chunk c of row r is stored
 //     in slot c ^ ((r / 4) % 4), so the 16 lanes of a fragment read hit 16
 //     distinct 16-byte bank groups. A lane loads the logical chunk that belongs
 //     in its slot. Rows past the tile's count load row 0 again (L2 hits).
 //   B stage: sixteen packed 16x16x32 fragments (1 KB each) copied verbatim; a
 //     32x32x16 fragment reads two adjacent blocks, 256 contiguous bytes per 16 lanes.
-// For gate/up, wave w's two N tiles are gate[32 w, 32 w + 32) and up of the same
+// For gate/up, wave w's two N tiles are gate[32 wn, 32 wn + 32) and up of the same
 // outputs, so g and u of one output sit in the same lane and register and the
 // SiLU-mul epilogue needs no data movement. Results are staged through LDS and
 // written as 16-byte row chunks.
@@ -427,37 +433,38 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (block b runs
 // on XCD b % 8), so XCD x is given a contiguous range of the tile list, which is
 // ordered (expert, n-tile, m-tile): an expert's m-tiles read each weight tile at
-// the same time from one L2, and consecutive n-tiles share the expert's rows.
-constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GSTAGES = 4;
+// about the same time from one L2, and consecutive n-tiles share the expert's rows.
+constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GMAXST = 5;
 constexpr int GSTAGE_A = GBM * GBK, GSTAGE_B = GBN * GBK;  // elements per stage
+constexpr int GSMEM = GMAXST * (GSTAGE_A + GSTAGE_B);      // 160 KB
+static_assert(GSMEM * 2 <= 160 * 1024, "LDS");
+static_assert(GBM * 256 * 2 + GBM * 8 <= GSMEM * 2, "down epilogue: output tile, weights and slots");
 
 __device__ __forceinline__ int a_slot(int row, int c) { return row * GBK + ((c ^ ((row >> 2) & 3)) << 3); }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+// s_waitcnt vmcnt(4 n): at most n K blocks of this wave's copies still in flight
+__device__ __forceinline__ void wait_blocks(int n) {
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 struct GemmTile {
   int e, row0, rows, nb;
 };
 
-// Eight waves: wave w = 4 wm + wn owns the 32-row tiles 2 mt + wm (mt < MW) x
-// columns [64 wn, 64 wn + 64) as MW x 2 MFMA tiles (up to 128 accumulators), two
-// waves per SIMD. MW = ceil(tiles holding rows / 2), the same for every wave, so a
-// partial tile costs in 64-row steps.
-template <bool GATEUP, int MW>
+template <bool GATEUP, int MW, int NS>
 __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTile& t,
-                                               uint16_t* smem, const float* w_row,
-                                               const int* slot_row) {
+                                               uint16_t* smem) {
   constexpr int NW = 8;
+  static_assert(NS >= 3 && NS <= GMAXST && NS - 2 <= 3, "stages");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
   const int wm = wvu >> 2, wn = wvu & 3;
   const int K = GATEUP ? a.d : a.f;
   const int KS = K / 32;
+  const int nkb = K / GBK;  // a multiple of NS
   const int e = t.e, row0 = t.row0, rows = t.rows, nb = t.nb;
 
   // A: wave w fills rows [32 w, 32 w + 32) of a stage with 2 instructions of 16
@@ -492,16 +499,25 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
     }
   }
   const int bstep = GATEUP ? 2 * 512 : 512;  // elements per 32-wide K block
+  // down: thread r < 256 holds row r's slot and routing weight for the epilogue
+  // (loaded now, so the loads are long done when the K loop ends)
+  int my_slot = 0;
+  float my_w = 0.0f;
+  if (!GATEUP && tid < GBM && tid < rows) {
+    my_slot = a.perm[row0 + tid];
+    my_w = a.w[my_slot];
+  }
 
   auto stage_a = [&](int st) -> uint16_t* { return smem + st * GSTAGE_A; };
-  auto stage_b = [&](int st) -> uint16_t* { return smem + GSTAGES * GSTAGE_A + st * GSTAGE_B; };
-  auto issue = [&](int kb, int st) {
-    const uint32_t A = lds_addr(stage_a(st)) + (uint32_t)(wvu * 32 * GBK * 2);
-    const uint32_t B = lds_addr(stage_b(st)) + (uint32_t)(wvu * 2 * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(abase + aoff[i] + kb * GBK, A + i * 16 * GBK * 2);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(bbase + boff[i] + kb * bstep, B + i * 1024);
+  auto stage_b = [&](int st) -> uint16_t* { return smem + NS * GSTAGE_A + st * GSTAGE_B; };
+  // copy p (0, 1: A rows; 2, 3: B blocks) of K block kb into stage st
+  auto issue = [&](int kb, int st, int p) {
+    if (p < 2)
+      lds_dma16(abase + aoff[p] + kb * GBK,
+                lds_addr(stage_a(st)) + (uint32_t)(wvu * 32 * GBK * 2) + p * 16 * GBK * 2);
+    else
+      lds_dma16(bbase + boff[p - 2] + kb * bstep,
+                lds_addr(stage_b(st)) + (uint32_t)(wvu * 2 * 1024) + (p - 2) * 1024);
   };
 
   const int l32 = lane & 31, lh = lane >> 5;
@@ -527,7 +543,9 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](int st) {
+  // fragments of stage st, then the MFMAs with the copies of K block kb + NS - 1
+  // placed after MFMA groups (one copy per MW / 2 groups of two)
+  auto compute = [&](int st, int kb) {
     const uint16_t* A = stage_a(st);
     const uint16_t* B = stage_b(st);
     u32x4 fa[2][MW], fb[2][2];
@@ -538,38 +556,55 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
 #pragma unroll
       for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
     }
+    const bool more = kb + NS - 1 < nkb;
+    const int kn = kb + NS - 1, sn = (st + NS - 1) % NS;
+    constexpr int EVERY = MW >= 2 ? MW / 2 : 1;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int mt = 0; mt < MW; ++mt)
+      for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
+        const int q = kk * MW + mt;
+        if (q % EVERY == 0 && q / EVERY < 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) issue(kn, sn, q / EVERY);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    if (MW == 1) {  // two MFMA groups: the last two copies go after them
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        issue(kn, sn, 2);
+        issue(kn, sn, 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  const int nkb = K / GBK;  // a multiple of 4 (d, f % 256 == 0)
+  // step kb: blocks kb + 1 .. kb + NS - 2 may still be in flight behind block kb
   auto step = [&](int kb, auto S) {
     constexpr int st = decltype(S)::value;
-    const int left = nkb - 1 - kb;  // K blocks issued after this one, at most 2
-    if (left >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (left == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int later = nkb - 1 - kb;
+    wait_blocks(later < NS - 2 ? later : NS - 2);
     __builtin_amdgcn_s_barrier();
-    if (kb + GSTAGES - 1 < nkb) issue(kb + GSTAGES - 1, (st + 3) & 3);
-    compute(st);
+    compute(st, kb);
   };
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  for (int kb = 0; kb < nkb; kb += 4) {
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue(j, j, p);
+  for (int kb = 0; kb < nkb; kb += NS) {
     step(kb, std::integral_constant<int, 0>{});
     step(kb + 1, std::integral_constant<int, 1>{});
     step(kb + 2, std::integral_constant<int, 2>{});
-    step(kb + 3, std::integral_constant<int, 3>{});
+    step(kb + 3, std::integral_constant<int, 3 % NS>{});
+    if constexpr (NS == 5) step(kb + 4, std::integral_constant<int, 4>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // epilogue through LDS: the 128 KB of stages hold the output tile
+  // epilogue through LDS: the stages hold the output tile
   uint16_t* stage = smem;
   if (GATEUP) {
     // act tile [256 rows][128 q]; wave (wm, wn) holds 32-row tiles 2 mt + wm, q [32 wn, +32)
@@ -590,7 +625,15 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
                ld_u32x4(&stage[r * 128 + ch * 8]));
     }
   } else {
-    // output tile [256 rows][256 cols], weighted and rounded
+    // output tile [256 rows][256 cols] in the first 128 KB, weighted and rounded;
+    // the rows' weights and slots behind it (rows past the count: weight 0)
+    float* w_row = reinterpret_cast<float*>(smem + GBM * 256);
+    int* slot_row = reinterpret_cast<int*>(w_row + GBM);
+    if (tid < GBM) {
+      w_row[tid] = my_w;
+      slot_row[tid] = my_slot;
+    }
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
@@ -611,12 +654,20 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   }
 }
 
+template <bool GATEUP, int NS>
+__device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile& t, uint16_t* smem) {
+  switch ((t.rows + 63) >> 6) {  // 64-row steps: tiles per wave
+    case 1: gemm_tile_body<GATEUP, 1, NS>(a, t, smem); break;
+    case 2: gemm_tile_body<GATEUP, 2, NS>(a, t, smem); break;
+    case 3: gemm_tile_body<GATEUP, 3, NS>(a, t, smem); break;
+    default: gemm_tile_body<GATEUP, 4, NS>(a, t, smem); break;
+  }
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
-  // four A stages then four B stages (128 KB), reused as the epilogue's staging tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSTAGES * (GSTAGE_A + GSTAGE_B)];
-  __shared__ float w_row[GBM];
-  __shared__ int slot_row[GBM];
+  // the stages, reused as the epilogue's staging tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSMEM];
   const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
   const int total = a.tile_start[a.E] * NT;        // (expert, n-tile, m-tile) triples
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
@@ -632,24 +683,18 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
   const int e = lo;
   const int mtiles = a.tile_start[e + 1] - a.tile_start[e];
   const int within = L - a.tile_start[e] * NT;
+  const int cnt = a.offsets[e + 1] - a.offsets[e];
+  // equal tiles, a multiple of 64 rows each (at most GBM; the last one is not empty)
+  const int per = (((cnt + mtiles - 1) / mtiles) + 63) & ~63;
   GemmTile t;
   t.e = e;
   t.nb = within / mtiles;
-  t.row0 = a.offsets[e] + (within % mtiles) * GBM;
-  t.rows = min(GBM, a.offsets[e + 1] - t.row0);
-  if (!GATEUP) {
-    for (int r = threadIdx.x; r < GBM; r += blockDim.x) {
-      const int slot = r < t.rows ? a.perm[t.row0 + r] : 0;
-      slot_row[r] = slot;
-      w_row[r] = r < t.rows ? a.w[slot] : 0.0f;
-    }
-  }
-  switch ((t.rows + 63) >> 6) {  // 64-row steps: tiles per wave
-    case 1: gemm_tile_body<GATEUP, 1>(a, t, smem, w_row, slot_row); break;
-    case 2: gemm_tile_body<GATEUP, 2>(a, t, smem, w_row, slot_row); break;
-    case 3: gemm_tile_body<GATEUP, 3>(a, t, smem, w_row, slot_row); break;
-    default: gemm_tile_body<GATEUP, 4>(a, t, smem, w_row, slot_row); break;
-  }
+  t.row0 = a.offsets[e] + (within % mtiles) * per;
+  t.rows = min(per, a.offsets[e + 1] - t.row0);
+  if (((GATEUP ? a.d : a.f) / GBK) % 5 == 0)
+    gemm_tile_mw<GATEUP, 5>(a, t, smem);
+  else
+    gemm_tile_mw<GATEUP, 4>(a, t, smem);
 }
 
 // 1-D grid of 8 * ceil(max_tiles * n-tiles / 8) workgroups (see the tile order above)
