@@ -664,16 +664,8 @@ __device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile
   }
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
-  // the stages, reused as the epilogue's staging tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSMEM];
-  const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
-  const int total = a.tile_start[a.E] * NT;        // (expert, n-tile, m-tile) triples
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int R = (total + 7) >> 3;
-  const int L = xcd * R + q;
-  if (q >= R || L >= total) return;
+// Tile (expert, n-tile, m-tile) number L of the list above
+__device__ __forceinline__ GemmTile decode_tile(const ExpertArgs& a, int NT, int L) {
   // expert: largest e with tile_start[e] * NT <= L
   int lo = 0, hi = a.E;
   while (hi - lo > 1) {
@@ -691,6 +683,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
   t.nb = within / mtiles;
   t.row0 = a.offsets[e] + (within % mtiles) * per;
   t.rows = min(per, a.offsets[e + 1] - t.row0);
+  return t;
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
+  // the stages, reused as the epilogue's staging tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSMEM];
+  const int NT = GATEUP ? a.f / 128 : a.d / 256;  // n-tiles per m-tile
+  const int total = a.tile_start[a.E] * NT;        // (expert, n-tile, m-tile) triples
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int R = (total + 7) >> 3;
+  const int L = xcd * R + q;
+  if (q >= R || L >= total) return;
+  const GemmTile t = decode_tile(a, NT, L);
   if (((GATEUP ? a.d : a.f) / GBK) % 5 == 0)
     gemm_tile_mw<GATEUP, 5>(a, t, smem);
   else
