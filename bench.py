@@ -1,9 +1,11 @@
 """Benchmark: one Beam MoE sublayer step (fused boundary + routed MoE FFN) on one MI355X.
 
-A step is one pass of the whole path over one batch of T tokens:
-beam_sublayer_norm_residual (post-norm, depth-scaled residual, pre-norm) then
-beam_moe_forward (FP32 router, grouped top-k, expert grouping, BF16 SwiGLU
-experts, weighted combine). Inputs are seeded synthetic tensors already resident
+A step is one pass of the whole path over one batch of T tokens through
+beam_sublayer_forward: the boundary (post-norm, depth-scaled residual, pre-norm)
+then the MoE FFN (FP32 router, grouped top-k, expert grouping, BF16 SwiGLU
+experts, weighted combine) — the same results as beam_sublayer_norm_residual
+followed by beam_moe_forward, with the boundary inside the routing launch for one
+token. Inputs are seeded synthetic tensors already resident
 in HBM when the timed region starts; decode steps rotate over distinct token sets
 so the experts touched change from step to step.
 
@@ -140,9 +142,8 @@ def main():
 
     def step(i):
         s = i % R
-        beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps, h_out=h_out,
-                                         z_out=z)
-        beam.beam_moe_forward(moe.handle, z, y)
+        beam.beam_sublayer_forward(moe.handle, hs[s], xs[s], wpost, wpre, wl.n, wl.eps, y,
+                                   h_out=h_out, z_out=z)
 
     # distinct experts per token set (for the algorithmic byte count)
     distinct = []

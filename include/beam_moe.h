@@ -162,6 +162,25 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
                      int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
                      void* stream);
 
+/*
+ * beam_sublayer_forward — one sublayer step: the boundary of beam_sublayer_norm_residual
+ * on (h_in, x) writing h_out and z_out, then beam_moe_forward on z_out with computed
+ * routing writing y_out. The results are bit-identical to those two calls in sequence.
+ * For one token (d <= 8192, k <= 64) the boundary runs inside the routing launch —
+ * every routing workgroup forms z itself while its router weights load, which saves
+ * the boundary's launch — as [vLLM §Agentengetriebene Optimierung, change 1] fuses the
+ * boundary into its neighbours and [vLLM §Der fusionierte Graph] runs the routing
+ * kernels right after it.
+ * Arguments as in those calls: h_in, x [T, d] BF16; w_post, w_pre [d] BF16; n >= 1;
+ * eps >= 0. h_out may be h_in itself; z_out and y_out must not overlap each other or
+ * any input. Optional outputs (NULL to skip): logits_out [T, E] FP32, ids_out [T, k],
+ * w_out [T, k]. T <= max_tokens.
+ */
+int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, const uint16_t* x,
+                          const uint16_t* w_post, const uint16_t* w_pre, int32_t n, float eps,
+                          uint16_t* h_out, uint16_t* z_out, uint16_t* y_out, float* logits_out,
+                          int32_t* ids_out, float* w_out, void* stream);
+
 /* beam_status_string — a static description of a status code. */
 const char* beam_status_string(int status);
 

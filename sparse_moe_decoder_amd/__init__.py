@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     beam_moe_forward,
     beam_moe_init,
     beam_router_topk,
+    beam_sublayer_forward,
     beam_sublayer_norm_residual,
     kernel_names,
     lib,

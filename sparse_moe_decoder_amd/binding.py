@@ -43,6 +43,8 @@ def lib():
         L.beam_router_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.beam_grouped_topk.argtypes = [vp, i32, vp, vp, vp, vp]
         L.beam_moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.beam_sublayer_forward.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp,
+                                            vp, vp]
         L.beam_status_string.argtypes = [ctypes.c_int]
         L.beam_status_string.restype = ctypes.c_char_p
         L.beam_profile_enable.argtypes = [ctypes.c_int]
@@ -53,6 +55,7 @@ def lib():
         L.beam_kernel_name.restype = ctypes.c_char_p
         for name in ("beam_moe_init", "beam_moe_destroy", "beam_sublayer_norm_residual",
                      "beam_router_topk", "beam_grouped_topk", "beam_moe_forward",
+                     "beam_sublayer_forward",
                      "beam_profile_enable", "beam_profile_reset", "beam_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -149,6 +152,25 @@ def beam_moe_forward(handle, z, y_out, ids_in=None, w_in=None, logits_out=None, 
         _ptr(ids_out, name="ids_out"), _ptr(w_out, name="w_out"),
         _ptr(perm_out, name="perm_out"), _ptr(offsets_out, name="offsets_out"),
         _stream(stream)))
+
+
+def beam_sublayer_forward(handle, h, x, w_post, w_pre, n, eps, y_out, h_out=None, z_out=None,
+                          logits_out=None, ids_out=None, w_out=None, stream=None):
+    """Boundary then MoE in one call; returns (h_out, z_out). h_out may be h itself."""
+    import torch
+    T, d = h.shape
+    if h_out is None:
+        h_out = torch.empty_like(h)
+    if z_out is None:
+        z_out = torch.empty_like(h)
+    bf = torch.bfloat16
+    _check("beam_sublayer_forward", lib().beam_sublayer_forward(
+        handle, T, _ptr(h, bf, (T, d), "h"), _ptr(x, bf, (T, d), "x"),
+        _ptr(w_post, bf, (d,), "w_post"), _ptr(w_pre, bf, (d,), "w_pre"), int(n), float(eps),
+        _ptr(h_out, bf, (T, d), "h_out"), _ptr(z_out, bf, (T, d), "z_out"),
+        _ptr(y_out, bf, (T, d), "y_out"), _ptr(logits_out, name="logits_out"),
+        _ptr(ids_out, name="ids_out"), _ptr(w_out, name="w_out"), _stream(stream)))
+    return h_out, z_out
 
 
 # ---- measurement hooks ------------------------------------------------------------------

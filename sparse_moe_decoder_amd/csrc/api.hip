@@ -185,6 +185,97 @@ int route(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, int32_t* ids
   return hip_status(launch_topk(topk_args(h, T, logits, ids_copy, w_copy), s));
 }
 
+bool overlaps(const void* a, const void* b, int64_t bytes) {
+  return (const char*)a < (const char*)b + bytes && (const char*)b < (const char*)a + bytes;
+}
+
+// The MoE forward after validation. bnd (computed routing, T = 1, d <=
+// kBoundaryWgMaxD, k <= kFusedRouteMaxSlots only): the boundary of the token runs
+// inside the routing launch and writes z (= bnd->z_out, the z read here) and h'.
+int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, const int32_t* ids_in,
+                 const float* w_in, float* logits_out, int32_t* ids_out, float* w_out,
+                 int32_t* perm_out, int32_t* offsets_out, hipStream_t s, const BoundaryArgs* bnd) {
+  const beam_moe_config& c = h->cfg;
+  const int k = c.topk, E = c.n_experts;
+  const int slots = T * k;
+
+  const int32_t* ids = ids_in;
+  const float* w = w_in;
+  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, h->counts,
+              h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
+              h->tile_start, perm_out, offsets_out};
+  if (!ids_in) {
+    float* lg = logits_out ? logits_out : h->logits;
+    ids = h->ids;
+    w = h->w;
+    pa.ids = ids;
+    TopkArgs ta = topk_args(h, T, lg, ids_out, w_out);
+    if (bnd) {
+      ProfScope ps(K_ROUTER, s);  // boundary, router, top-k and grouping in one launch
+      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
+      if (launch_boundary_route_fused(*bnd, ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
+        return BEAM_ERR_HIP;
+    } else if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
+      ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
+      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
+      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
+        return BEAM_ERR_HIP;
+    } else if (slots <= kPermChunk) {
+      int st = run_router(h, T, z, lg, s);
+      if (st != BEAM_OK) return st;
+      ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
+      if (launch_route_permute_small(ta, pa, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else {
+      int st = run_router(h, T, z, lg, s);
+      if (st != BEAM_OK) return st;
+      {
+        ProfScope ps(K_TOPK, s);
+        if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
+      }
+      ProfScope ps(K_PERMUTE, s);
+      if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+  } else {
+    if (ids_out &&
+        hipMemcpyAsync(ids_out, ids_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    if (w_out &&
+        hipMemcpyAsync(w_out, w_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    pa.ids = ids;
+    ProfScope ps(K_PERMUTE, s);
+    if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
+                h->n_active, h->tile_start, w, h->act, h->yk};
+  if (T <= kStreamMaxT) {
+    const int max_active = slots < E ? slots : E;
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    ProfScope ps(K_DOWN, s);
+    if (T <= kSplitDownMaxT) {
+      if (launch_down_split(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else if (launch_down_stream(ea, max_active, s) != hipSuccess) {
+      return BEAM_ERR_HIP;
+    }
+  } else {
+    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    {
+      ProfScope ps(K_DOWN, s);
+      if (launch_down_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+  }
+  ProfScope ps(K_COMBINE, s);
+  return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -327,82 +418,50 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
   for (const void* p : ptrs4)
     if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
   const beam_moe_config& c = h->cfg;
-  const int64_t bytes_z = (int64_t)T * c.hidden * 2;
-  if ((const char*)y_out < (const char*)z + bytes_z && (const char*)z < (const char*)y_out + bytes_z)
-    return BEAM_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  const int k = c.topk, E = c.n_experts;
-  const int slots = T * k;
+  if (overlaps(y_out, z, (int64_t)T * c.hidden * 2)) return BEAM_ERR_INVALID_ARG;
+  return forward_impl(h, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
+                      offsets_out, (hipStream_t)stream, nullptr);
+}
 
-  const int32_t* ids = ids_in;
-  const float* w = w_in;
-  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, h->counts,
-              h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
-              h->tile_start, perm_out, offsets_out};
-  if (!ids_in) {
-    float* lg = logits_out ? logits_out : h->logits;
-    ids = h->ids;
-    w = h->w;
-    pa.ids = ids;
-    TopkArgs ta = topk_args(h, T, lg, ids_out, w_out);
-    if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
-      ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
-      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
-        return BEAM_ERR_HIP;
-    } else if (slots <= kPermChunk) {
-      int st = run_router(h, T, z, lg, s);
-      if (st != BEAM_OK) return st;
-      ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
-      if (launch_route_permute_small(ta, pa, s) != hipSuccess) return BEAM_ERR_HIP;
-    } else {
-      int st = run_router(h, T, z, lg, s);
-      if (st != BEAM_OK) return st;
-      {
-        ProfScope ps(K_TOPK, s);
-        if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
-      }
-      ProfScope ps(K_PERMUTE, s);
-      if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
-  } else {
-    if (ids_out &&
-        hipMemcpyAsync(ids_out, ids_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return BEAM_ERR_HIP;
-    if (w_out &&
-        hipMemcpyAsync(w_out, w_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return BEAM_ERR_HIP;
-    pa.ids = ids;
-    ProfScope ps(K_PERMUTE, s);
-    if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, const uint16_t* x,
+                          const uint16_t* w_post, const uint16_t* w_pre, int32_t n, float eps,
+                          uint16_t* h_out, uint16_t* z_out, uint16_t* y_out, float* logits_out,
+                          int32_t* ids_out, float* w_out, void* stream) {
+  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  const beam_moe_config& c = h->cfg;
+  const int d = c.hidden;
+  if (n < 1 || !(eps >= 0.0f) || !isfinite(eps)) return BEAM_ERR_INVALID_ARG;
+  if (!h_in || !x || !w_post || !w_pre || !h_out || !z_out || !y_out) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(h_in) || !aligned16(x) || !aligned16(w_post) || !aligned16(w_pre) ||
+      !aligned16(h_out) || !aligned16(z_out) || !aligned16(y_out))
+    return BEAM_ERR_INVALID_ARG;
+  const void* ptrs4[] = {logits_out, ids_out, w_out};
+  for (const void* p : ptrs4)
+    if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
+  const int64_t bytes = (int64_t)T * d * 2;
+  // z_out and y_out are written while the inputs are still read; only h_out may be h_in
+  const void* ins[] = {h_in, x};
+  for (const void* p : ins)
+    if (overlaps(p, z_out, bytes) || overlaps(p, y_out, bytes)) return BEAM_ERR_INVALID_ARG;
+  if (overlaps(z_out, y_out, bytes) || overlaps(h_out, z_out, bytes) ||
+      overlaps(h_out, y_out, bytes) || (h_out != h_in && overlaps(h_out, h_in, bytes)) ||
+      overlaps(h_out, x, bytes))
+    return BEAM_ERR_INVALID_ARG;
+  const float c1 = (float)sqrt((double)(n - 1) / (double)n);
+  const float c2 = (float)(1.0 / sqrt((double)n));
+  hipStream_t s = (hipStream_t)stream;
+  BoundaryArgs ba{T, d, h_in, x, w_post, w_pre, h_out, z_out, c1, c2, eps};
+  if (T == 1 && d <= kBoundaryWgMaxD && c.topk <= kFusedRouteMaxSlots)
+    return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
+                        nullptr, s, &ba);
+  {
+    ProfScope ps(K_BOUNDARY, s);
+    if (launch_boundary(ba, s) != hipSuccess) return BEAM_ERR_HIP;
   }
-  ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk};
-  if (T <= kStreamMaxT) {
-    const int max_active = slots < E ? slots : E;
-    {
-      ProfScope ps(K_GATEUP, s);
-      if (launch_gateup_stream(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
-    ProfScope ps(K_DOWN, s);
-    if (T <= kSplitDownMaxT) {
-      if (launch_down_split(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
-    } else if (launch_down_stream(ea, max_active, s) != hipSuccess) {
-      return BEAM_ERR_HIP;
-    }
-  } else {
-    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
-    {
-      ProfScope ps(K_GATEUP, s);
-      if (launch_gateup_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
-    {
-      ProfScope ps(K_DOWN, s);
-      if (launch_down_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
-  }
-  ProfScope ps(K_COMBINE, s);
-  return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+  return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
+                      nullptr, s, nullptr);
 }
 
 int beam_profile_enable(int enable) {

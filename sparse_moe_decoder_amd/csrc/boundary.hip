@@ -12,52 +12,11 @@
 // squares of x; scaled add and sum of squares of h'; pre-norm), so each row costs
 // 2 reads and 2 writes of d BF16 values. Rows up to 8192 wide get a workgroup
 // each (one chunk per lane); wider rows one wavefront each.
-#include "common.h"
-#include "kernels.h"
+#include "boundary_device.h"
 
 namespace beam {
 
-__device__ __forceinline__ float sumsq8(const u32x4& v) {
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float a = lo_bf(v[i]), b = hi_bf(v[i]);
-    s += a * a;
-    s += b * b;
-  }
-  return s;
-}
-
-// (v * r) * w, rounded, for 8 packed values
-__device__ __forceinline__ u32x4 norm8(const u32x4& v, float r, const u32x4& w) {
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = pack_bf2((lo_bf(v[i]) * r) * lo_bf(w[i]), (hi_bf(v[i]) * r) * hi_bf(w[i]));
-  return o;
-}
-
-// h' = bf16(bf16(c1 h) + bf16(c2 xn)) for 8 packed values; accumulates sum of h'^2
-__device__ __forceinline__ u32x4 residual8(const u32x4& h, const u32x4& xn, float c1, float c2,
-                                           float& ss) {
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float a0 = bf2f(f2bf(c1 * lo_bf(h[i]))), a1 = bf2f(f2bf(c1 * hi_bf(h[i])));
-    float b0 = bf2f(f2bf(c2 * lo_bf(xn[i]))), b1 = bf2f(f2bf(c2 * hi_bf(xn[i])));
-    float s0 = bf2f(f2bf(a0 + b0)), s1 = bf2f(f2bf(a1 + b1));
-    ss += s0 * s0;
-    ss += s1 * s1;
-    o[i] = (uint32_t)f2bf(s0) | ((uint32_t)f2bf(s1) << 16);
-  }
-  return o;
-}
-
-__device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
-  return 1.0f / sqrtf(ss / (float)d + eps);
-}
-
-// One workgroup per row (rows up to 8192 wide): one 16-byte chunk per lane, W =
+// One workgroup per row (rows up to kBoundaryWgMaxD wide): one 16-byte chunk per lane, W =
 // ceil(d / 512) waves. Each sum of squares is a per-lane sum of its chunk, a wave
 // sum, then the W wave sums added in wave order through LDS; every lane forms the
 // same total. The whole row is in flight after one round of loads.
@@ -92,56 +51,8 @@ __global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a) {
   if (ok) st_u32x4((u32x4*)(a.z_out + t * a.d) + idx, norm8(hv, r2, wr));
 }
 
-// Register-resident variant (one wave per row): NC = max 16-byte chunks per lane.
-template <int NC>
-__global__ __launch_bounds__(256) void boundary_rows_kernel(BoundaryArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int nch = a.d >> 3;
-  const u32x4* xr = (const u32x4*)(a.x + t * a.d);
-  const u32x4* hr = (const u32x4*)(a.h + t * a.d);
-  const u32x4* wpo = (const u32x4*)a.w_post;
-  const u32x4* wpr = (const u32x4*)a.w_pre;
-  u32x4* ho = (u32x4*)(a.h_out + t * a.d);
-  u32x4* zo = (u32x4*)(a.z_out + t * a.d);
-
-  // every load is issued before the first reduction: one memory latency per row
-  u32x4 xv[NC], hv[NC], wo[NC], wr[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    int idx = lane + 64 * c;
-    if (idx < nch) {
-      xv[c] = ld_u32x4(xr + idx);
-      hv[c] = ld_u32x4(hr + idx);
-      wo[c] = ld_u32x4(wpo + idx);
-      wr[c] = ld_u32x4(wpr + idx);
-    }
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (lane + 64 * c < nch) ss += sumsq8(xv[c]);
-  const float r = rms_scale(wave_sum(ss), a.d, a.eps);
-  float ss2 = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    int idx = lane + 64 * c;
-    if (idx < nch) {
-      u32x4 xn = norm8(xv[c], r, wo[c]);
-      hv[c] = residual8(hv[c], xn, a.c1, a.c2, ss2);
-      st_u32x4(ho + idx, hv[c]);
-    }
-  }
-  const float r2 = rms_scale(wave_sum(ss2), a.d, a.eps);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    int idx = lane + 64 * c;
-    if (idx < nch) st_u32x4(zo + idx, norm8(hv[c], r2, wr[c]));
-  }
-}
-
-// Any-width variant: re-reads x and h' instead of keeping the row in registers.
+// Wider rows: one wavefront per row, re-reading x and h' instead of keeping the row
+// in registers.
 __global__ __launch_bounds__(256) void boundary_rows_wide_kernel(BoundaryArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -168,27 +79,13 @@ __global__ __launch_bounds__(256) void boundary_rows_wide_kernel(BoundaryArgs a)
 }
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s) {
-  const int nch = a.d >> 3;
-  const int nc = (nch + 63) / 64;
-  if (nc <= 16) {  // the choice depends on d only, so a row's result does not depend on T
-    hipLaunchKernelGGL(boundary_row_wg_kernel, dim3((unsigned)a.T), dim3(64 * nc), 0, s, a);
-    return hipGetLastError();
+  // the choice depends on d only, so a row's result does not depend on T
+  if (a.d <= kBoundaryWgMaxD) {
+    const int nv = ((a.d >> 3) + 63) / 64;
+    hipLaunchKernelGGL(boundary_row_wg_kernel, dim3((unsigned)a.T), dim3(64 * nv), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(boundary_rows_wide_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
   }
-  dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
-  if (nc <= 1)
-    hipLaunchKernelGGL(boundary_rows_kernel<1>, grid, block, 0, s, a);
-  else if (nc <= 2)
-    hipLaunchKernelGGL(boundary_rows_kernel<2>, grid, block, 0, s, a);
-  else if (nc <= 4)
-    hipLaunchKernelGGL(boundary_rows_kernel<4>, grid, block, 0, s, a);
-  else if (nc <= 8)
-    hipLaunchKernelGGL(boundary_rows_kernel<8>, grid, block, 0, s, a);
-  else if (nc <= 10)
-    hipLaunchKernelGGL(boundary_rows_kernel<10>, grid, block, 0, s, a);
-  else if (nc <= 16)
-    hipLaunchKernelGGL(boundary_rows_kernel<16>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(boundary_rows_wide_kernel, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

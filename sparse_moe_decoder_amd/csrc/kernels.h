@@ -11,6 +11,7 @@ constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming ex
 constexpr int kSplitDownMaxT = 16;  // largest T whose down pass splits K over four waves
 constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
 constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
+constexpr int kBoundaryWgMaxD = 8192;   // boundary rows up to this width: a workgroup per row
 
 struct BoundaryArgs {
   int T, d;
@@ -94,6 +95,11 @@ hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipS
 // `sc` is caller-owned scratch of T * E 64-bit words for the published scores).
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
                                    uint32_t* done, uint64_t* sc, hipStream_t s);
+// one token (d <= 8192): the boundary of that token inside the same launch; z goes to
+// b.z_out and the router reads it, h' to b.h_out (which may be b.h)
+hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
+                                       const PermArgs& a, uint32_t* done, uint64_t* sc,
+                                       hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);

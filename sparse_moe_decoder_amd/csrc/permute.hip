@@ -11,6 +11,7 @@
 // every run.
 #include "common.h"
 #include "kernels.h"
+#include "boundary_device.h"
 #include "router_device.h"
 #include "topk_device.h"
 
@@ -332,9 +333,15 @@ __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, P
 // (every other one has published) resets the counter for the next launch and runs
 // the top-k (one wave per token, coherent loads of the pairs) and the grouping. No
 // workgroup waits on another.
+// BOUNDARY (one token): the sublayer boundary runs inside the same launch. Each
+// workgroup forms the token's z from h and x itself, in the boundary kernel's exact
+// order (see boundary_row_4waves_finish), into LDS, with its router weights in
+// flight; workgroup 0 writes z out, and the last workgroup writes h' (by then every
+// workgroup has read h, so h_out may alias h).
+template <bool BOUNDARY>
 __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, TopkArgs ta,
                                                                PermArgs pa, uint32_t* done,
-                                                               uint64_t* sc) {
+                                                               uint64_t* sc, BoundaryArgs ba) {
   __shared__ float part[3][kRouterRT];
   __shared__ float c_lds[4][256];
   __shared__ int32_t sel[4][32];
@@ -343,7 +350,25 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
   const float bias = ta.bias[e];
-  const float v = router_small_dot(ra, e, 0, ra.T, part);
+  float v;
+  BoundaryRow4 brow;  // BOUNDARY: the token row; its h' is stored by the last workgroup
+  if constexpr (BOUNDARY) {
+    // one token: the row's loads (L2 hits after the first workgroup) go out first,
+    // then this expert's router weights (HBM); loads complete in order, so the
+    // boundary arithmetic runs while the weights are in flight. Every workgroup forms
+    // z itself (workgroup 0 writes it out).
+    __shared__ float red[2][16];
+    __shared__ __attribute__((aligned(16))) uint16_t zl[kBoundaryWgMaxD];
+    f32x4 w[kRouterPreChunks];
+    boundary_row_4waves_load(ba, 0, brow);
+    __builtin_amdgcn_sched_barrier(0);
+    router_load_w(ra, e, w);
+    __builtin_amdgcn_sched_barrier(0);
+    boundary_row_4waves_finish(ba, 0, brow, zl, e == 0 ? ba.z_out : nullptr, red);
+    v = router_dot_1_lds(ra, w, zl, part);
+  } else {
+    v = router_small_dot(ra, e, 0, ra.T, part);
+  }
   if (tid < ra.T) {
     ra.logits[(int64_t)tid * ra.E + e] = v;
     const float sv = routing_score(v), cv = sv + bias;
@@ -361,6 +386,8 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every workgroup has read h by now, so h_out may be h itself
+  if constexpr (BOUNDARY) boundary_row_4waves_store_h(ba, 0, brow);
   for (int t = wv; t < ta.T; t += 4) {
     topk_token<true>(ta, t, c_lds[wv], sel[wv], lane, sc);
     if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
@@ -371,8 +398,16 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
 
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
                                    uint32_t* done, uint64_t* sc, hipStream_t s) {
-  hipLaunchKernelGGL(route_fused_tiny_kernel, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a, done,
-                     sc);
+  hipLaunchKernelGGL(route_fused_tiny_kernel<false>, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a,
+                     done, sc, BoundaryArgs{});
+  return hipGetLastError();
+}
+
+hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
+                                       const PermArgs& a, uint32_t* done, uint64_t* sc,
+                                       hipStream_t s) {
+  hipLaunchKernelGGL(route_fused_tiny_kernel<true>, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a,
+                     done, sc, b);
   return hipGetLastError();
 }
 

@@ -87,6 +87,48 @@ __device__ __forceinline__ float router_small_dot_t(const RouterArgs& a, int e, 
   return v;
 }
 
+// One token, with the weights already in registers and z in LDS. d <= 8192: each
+// wave's quarter has at most 8 chunks per lane. The lane's terms, the wave sum and
+// the quarter sums are formed in the order of router_small_dot, so the logit is
+// bit-identical to it.
+constexpr int kRouterPreChunks = 8;
+
+// Expert e's weight chunks of this lane (chunks past the quarter read chunk 0).
+__device__ __forceinline__ void router_load_w(const RouterArgs& a, int e, f32x4 (&w)[kRouterPreChunks]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (a.d >> 2) >> 2;
+  const f32x4* wr = (const f32x4*)(a.W + (int64_t)e * a.d) + wv * per;
+#pragma unroll
+  for (int i = 0; i < kRouterPreChunks; ++i) {
+    const int c = lane + 64 * i;
+    w[i] = wr[c < per ? c : 0];
+  }
+}
+
+__device__ __forceinline__ float router_dot_1_lds(const RouterArgs& a, const f32x4 (&w)[kRouterPreChunks],
+                                                  const uint16_t* zl, float (*part)[kRouterRT]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (a.d >> 2) >> 2;
+  const uint16_t* zq = zl + 4 * wv * per;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRouterPreChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c < per) {
+      const uint2 zz = *(const uint2*)(zq + 4 * c);
+      acc += lo_bf(zz.x) * w[i][0];
+      acc += hi_bf(zz.x) * w[i][1];
+      acc += lo_bf(zz.y) * w[i][2];
+      acc += hi_bf(zz.y) * w[i][3];
+    }
+  }
+  float v = wave_sum(acc);
+  if (wv > 0 && lane == 0) part[wv - 1][0] = v;
+  __syncthreads();
+  if (wv == 0 && lane == 0) return ((v + part[0][0]) + part[1][0]) + part[2][0];
+  return 0.0f;
+}
+
 // nt <= kRouterRT tokens; the token-slot count is the next power of two >= nt.
 __device__ __forceinline__ float router_small_dot(const RouterArgs& a, int e, int t0, int nt,
                                                   float (*part)[kRouterRT]) {

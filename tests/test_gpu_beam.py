@@ -142,6 +142,37 @@ def test_decode_full(beam_gpu, experts, T):
     report_chain(g["y_chain"][same], y[same], f"decode T={T} y")
 
 
+def test_sublayer_forward_decode1(beam_gpu):
+    """Beam shapes, one token (boundary inside the routing launch, d = 5120): the one-call
+    path equals the boundary call followed by the MoE forward bit for bit, over several
+    token sets and with h updated in place."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    moe = beam_gpu["moe"]
+    E, k = BASE.E, BASE.k
+    for s in range(4):
+        print(f"[beam] sublayer forward token set {s}", flush=True)
+        h, x = sd.tokens(BASE, "h", T=1, token_set=s), sd.tokens(BASE, "x", T=1, token_set=s)
+        h_ref, z_ref = beam.beam_sublayer_norm_residual(h, x, beam_gpu["wpost"], beam_gpu["wpre"],
+                                                        BASE.n, BASE.eps)
+        y_ref = torch.empty_like(h)
+        lg_ref = torch.empty((1, E), dtype=torch.float32, device="cuda")
+        ids_ref = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        beam.beam_moe_forward(moe.handle, z_ref, y_ref, logits_out=lg_ref, ids_out=ids_ref)
+        hh = h.clone()
+        y = torch.empty_like(h)
+        lg = torch.empty_like(lg_ref)
+        ids = torch.empty_like(ids_ref)
+        _, z = beam.beam_sublayer_forward(moe.handle, hh, x, beam_gpu["wpost"], beam_gpu["wpre"],
+                                          BASE.n, BASE.eps, y, h_out=hh, logits_out=lg, ids_out=ids)
+        assert torch.equal(hh.view(torch.int16), h_ref.view(torch.int16))
+        assert torch.equal(z.view(torch.int16), z_ref.view(torch.int16))
+        assert torch.equal(lg.view(torch.int32), lg_ref.view(torch.int32))
+        assert torch.equal(ids, ids_ref)
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+
+
 def sampled_tokens(ids, T, hot=(), n_rand=32, seed=0):
     rng = np.random.default_rng(seed)
     pick = set(range(8)) | set(range(T - 8, T)) | set(rng.choice(T, n_rand, replace=False).tolist())

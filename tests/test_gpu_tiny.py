@@ -199,6 +199,70 @@ def test_single_token_paths_agree(gpu, host):
     P.check_permutation_valid(ids[:1].cpu().numpy(), perm.cpu().numpy(), offs.cpu().numpy(), WL.E)
 
 
+def _two_calls(moe, h, x, wpost, wpre, n, eps):
+    """The reference sequence: boundary, then the MoE forward on its z."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    T, d = h.shape
+    E, k = moe.cfg["n_experts"], moe.cfg["topk"]
+    h_out, z = beam.beam_sublayer_norm_residual(h, x, wpost, wpre, n, eps)
+    y = torch.empty_like(z)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    beam.beam_moe_forward(moe.handle, z, y, logits_out=lg, ids_out=ids, w_out=w)
+    return [P.bits(h_out), P.bits(z), P.bits(y), lg.cpu().numpy(), ids.cpu().numpy(),
+            w.cpu().numpy()]
+
+
+def _one_call(moe, h, x, wpost, wpre, n, eps, in_place=False):
+    import torch
+    import sparse_moe_decoder_amd as beam
+    T, d = h.shape
+    E, k = moe.cfg["n_experts"], moe.cfg["topk"]
+    y = torch.empty_like(h)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    hh = h.clone() if in_place else h
+    h_out, z = beam.beam_sublayer_forward(moe.handle, hh, x, wpost, wpre, n, eps, y,
+                                          h_out=hh if in_place else None, logits_out=lg,
+                                          ids_out=ids, w_out=w)
+    return [P.bits(h_out), P.bits(z), P.bits(y), lg.cpu().numpy(), ids.cpu().numpy(),
+            w.cpu().numpy()]
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_sublayer_forward_equals_two_calls(gpu, T, in_place):
+    """beam_sublayer_forward (boundary inside the routing launch at T = 1) gives the
+    same h', z, y, logits, ids and weights bit for bit as the boundary call followed
+    by the MoE forward; h_out may be h itself. Repeated, so the launch's counter
+    reset is exercised."""
+    print(f"[tiny] sublayer forward T={T} in_place={in_place}", flush=True)
+    h, x = gpu["h"][:T].contiguous(), gpu["x"][:T].contiguous()
+    ref = _two_calls(gpu["moe"], h, x, gpu["wpost"], gpu["wpre"], WL.n, WL.eps)
+    names = ["h'", "z", "y", "logits", "ids", "w"]
+    for rep in range(3):
+        got = _one_call(gpu["moe"], h, x, gpu["wpost"], gpu["wpre"], WL.n, WL.eps, in_place)
+        for nm, a, b in zip(names, got, ref):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (nm, rep)
+
+
+def test_sublayer_forward_matches_oracle(gpu, host):
+    """Single token through the one-call path against the oracle's sublayer."""
+    got = _one_call(gpu["moe"], gpu["h"][:1].contiguous(), gpu["x"][:1].contiguous(),
+                    gpu["wpost"], gpu["wpre"], WL.n, WL.eps)
+    P.assert_bf16_close(got[0], host["h_out"][:1], "tiny h' (one call)")
+    P.assert_bf16_close(got[1], host["z"][:1], "tiny z (one call)")
+    rel = P.logit_rel_rows(got[3], host["logits"][:1])
+    assert rel.max() <= P.LOGIT_REL_MAX
+    o_ids, o_w, _, _ = oracle.topk(got[3], synth.router_bias(WL), WL.G, WL.kg, WL.k, WL.scale)
+    assert np.array_equal(got[4], o_ids)
+    o_y, _ = oracle.moe_experts(got[1], o_ids, o_w, WL.E, host["experts"].__getitem__)
+    P.assert_bf16_close(got[2], o_y, "tiny y (one call)")
+
+
 def test_edge_sizes(gpu, host):
     """T = 0 is a no-op; T = max_tokens works; T > max_tokens is rejected up front."""
     import torch
