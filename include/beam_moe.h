@@ -163,6 +163,28 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
                      void* stream);
 
 /*
+ * beam_moe_forward_boundary — beam_moe_forward on z, then the NEXT sublayer's
+ * boundary with the MoE output as its branch: the result is bit-identical to
+ *   beam_moe_forward(h, T, z, y, ids_in, w_in, logits_out, ids_out, w_out, ...)
+ *   beam_sublayer_norm_residual(T, d, h_in, y, w_post, w_pre, n, eps, h_out, z_out)
+ * but the combine of the top-k expert rows and the boundary run as one kernel, so
+ * y does not pass through HBM ([vLLM §Agentengetriebene Optimierung, changes 1 and
+ * 3]: after the MoE, the post-norm kernel of the boundary also combines the top-8
+ * expert outputs).
+ * Arguments: z [T, d] BF16 (the MoE input); h_in [T, d] the residual stream; w_post,
+ * w_pre [d]; n >= 1; eps >= 0; outputs h_out, z_out [T, d] (the next sublayer's
+ * residual and input). y_out [T, d] or NULL (required when d > 8192). Routing replay
+ * (ids_in, w_in) and the optional routing outputs as in beam_moe_forward.
+ * Aliasing: h_out may be h_in; z_out may be z (the experts have read z before the
+ * boundary writes); nothing else may overlap.
+ */
+int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
+                              const uint16_t* h_in, const uint16_t* w_post, const uint16_t* w_pre,
+                              int32_t n, float eps, uint16_t* h_out, uint16_t* z_out,
+                              uint16_t* y_out, const int32_t* ids_in, const float* w_in,
+                              float* logits_out, int32_t* ids_out, float* w_out, void* stream);
+
+/*
  * beam_sublayer_forward — one sublayer step: the boundary of beam_sublayer_norm_residual
  * on (h_in, x) writing h_out and z_out, then beam_moe_forward on z_out with computed
  * routing writing y_out. The results are bit-identical to those two calls in sequence.

@@ -192,9 +192,13 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
 // The MoE forward after validation. bnd (computed routing, T = 1, d <=
 // kBoundaryWgMaxD, k <= kFusedRouteMaxSlots only): the boundary of the token runs
 // inside the routing launch and writes z (= bnd->z_out, the z read here) and h'.
+// post: the next sublayer's boundary with x = the MoE output runs in the combine
+// launch (d <= kBoundaryWgMaxD; y_out may then be null) or after it (wider rows,
+// through y_out).
 int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, const int32_t* ids_in,
                  const float* w_in, float* logits_out, int32_t* ids_out, float* w_out,
-                 int32_t* perm_out, int32_t* offsets_out, hipStream_t s, const BoundaryArgs* bnd) {
+                 int32_t* perm_out, int32_t* offsets_out, hipStream_t s, const BoundaryArgs* bnd,
+                 const BoundaryArgs* post) {
   const beam_moe_config& c = h->cfg;
   const int k = c.topk, E = c.n_experts;
   const int slots = T * k;
@@ -272,7 +276,13 @@ int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, con
     }
   }
   ProfScope ps(K_COMBINE, s);
-  return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+  if (!post) return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+  if (c.hidden <= kBoundaryWgMaxD)
+    return hip_status(launch_combine_boundary(*post, CombineArgs{k, E, ids, h->yk, y_out}, s));
+  if (launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s) != hipSuccess) return BEAM_ERR_HIP;
+  BoundaryArgs pb = *post;
+  pb.x = y_out;
+  return hip_status(launch_boundary(pb, s));
 }
 
 
@@ -420,7 +430,48 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
   const beam_moe_config& c = h->cfg;
   if (overlaps(y_out, z, (int64_t)T * c.hidden * 2)) return BEAM_ERR_INVALID_ARG;
   return forward_impl(h, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
-                      offsets_out, (hipStream_t)stream, nullptr);
+                      offsets_out, (hipStream_t)stream, nullptr, nullptr);
+}
+
+int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
+                              const uint16_t* h_in, const uint16_t* w_post, const uint16_t* w_pre,
+                              int32_t n, float eps, uint16_t* h_out, uint16_t* z_out,
+                              uint16_t* y_out, const int32_t* ids_in, const float* w_in,
+                              float* logits_out, int32_t* ids_out, float* w_out, void* stream) {
+  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  const beam_moe_config& c = h->cfg;
+  const int d = c.hidden;
+  if (n < 1 || !(eps >= 0.0f) || !isfinite(eps)) return BEAM_ERR_INVALID_ARG;
+  if (!z || !h_in || !w_post || !w_pre || !h_out || !z_out) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(z) || !aligned16(h_in) || !aligned16(w_post) || !aligned16(w_pre) ||
+      !aligned16(h_out) || !aligned16(z_out) || (y_out && !aligned16(y_out)))
+    return BEAM_ERR_INVALID_ARG;
+  if ((ids_in == nullptr) != (w_in == nullptr)) return BEAM_ERR_INVALID_ARG;
+  if (ids_in && logits_out) return BEAM_ERR_INVALID_ARG;
+  const void* ptrs4[] = {ids_in, w_in, logits_out, ids_out, w_out};
+  for (const void* p : ptrs4)
+    if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
+  if (d > kBoundaryWgMaxD && !y_out) return BEAM_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)T * d * 2;
+  // the boundary reads h_in row by row before writing that row's h_out (so h_out may
+  // be h_in) and z_out; z is consumed by the expert launches before it runs (so z_out
+  // may be z)
+  if ((h_out != h_in && overlaps(h_out, h_in, bytes)) || overlaps(h_out, z_out, bytes) ||
+      overlaps(z_out, h_in, bytes) || (z_out != z && overlaps(z_out, z, bytes)) ||
+      overlaps(h_out, z, bytes))
+    return BEAM_ERR_INVALID_ARG;
+  if (y_out) {
+    const void* others[] = {z, h_in, h_out, z_out};
+    for (const void* p : others)
+      if (overlaps(y_out, p, bytes)) return BEAM_ERR_INVALID_ARG;
+  }
+  const float c1 = (float)sqrt((double)(n - 1) / (double)n);
+  const float c2 = (float)(1.0 / sqrt((double)n));
+  BoundaryArgs post{T, d, h_in, nullptr, w_post, w_pre, h_out, z_out, c1, c2, eps};
+  return forward_impl(h, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, nullptr, nullptr,
+                      (hipStream_t)stream, nullptr, &post);
 }
 
 int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, const uint16_t* x,
@@ -455,13 +506,13 @@ int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, co
   BoundaryArgs ba{T, d, h_in, x, w_post, w_pre, h_out, z_out, c1, c2, eps};
   if (T == 1 && d <= kBoundaryWgMaxD && c.topk <= kFusedRouteMaxSlots)
     return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
-                        nullptr, s, &ba);
+                        nullptr, s, &ba, nullptr);
   {
     ProfScope ps(K_BOUNDARY, s);
     if (launch_boundary(ba, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
-                      nullptr, s, nullptr);
+                      nullptr, s, nullptr, nullptr);
 }
 
 int beam_profile_enable(int enable) {

@@ -13,6 +13,7 @@
 // 2 reads and 2 writes of d BF16 values. Rows up to 8192 wide get a workgroup
 // each (one chunk per lane); wider rows one wavefront each.
 #include "boundary_device.h"
+#include "combine_device.h"
 
 namespace beam {
 
@@ -20,7 +21,11 @@ namespace beam {
 // ceil(d / 512) waves. Each sum of squares is a per-lane sum of its chunk, a wave
 // sum, then the W wave sums added in wave order through LDS; every lane forms the
 // same total. The whole row is in flight after one round of loads.
-__global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a) {
+// COMBINE: x is the weighted combine of the token's expert rows (combine_chunk), formed
+// in place of the load of x (and written to c.y when that is not null): the MoE
+// output crosses into the next sublayer's boundary without a round trip through HBM.
+template <bool COMBINE>
+__global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a, CombineArgs cb) {
   __shared__ float red[2][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int64_t t = blockIdx.x;
@@ -28,7 +33,13 @@ __global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a) {
   const int idx = threadIdx.x;
   const bool ok = idx < nch;
   const int li = ok ? idx : 0;
-  const u32x4 xv = ld_u32x4((const u32x4*)(a.x + t * a.d) + li);
+  u32x4 xv;
+  if constexpr (COMBINE) {
+    xv = combine_chunk(t, li, cb.k, a.d, cb.E, cb.ids, cb.yk);
+    if (cb.y && ok) st_u32x4((u32x4*)(cb.y + t * a.d) + idx, xv);
+  } else {
+    xv = ld_u32x4((const u32x4*)(a.x + t * a.d) + li);
+  }
   u32x4 hv = ld_u32x4((const u32x4*)(a.h + t * a.d) + li);
   const u32x4 wo = ld_u32x4((const u32x4*)a.w_post + li);
   const u32x4 wr = ld_u32x4((const u32x4*)a.w_pre + li);
@@ -82,10 +93,17 @@ hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s) {
   // the choice depends on d only, so a row's result does not depend on T
   if (a.d <= kBoundaryWgMaxD) {
     const int nv = ((a.d >> 3) + 63) / 64;
-    hipLaunchKernelGGL(boundary_row_wg_kernel, dim3((unsigned)a.T), dim3(64 * nv), 0, s, a);
+    hipLaunchKernelGGL(boundary_row_wg_kernel<false>, dim3((unsigned)a.T), dim3(64 * nv), 0, s, a,
+                       CombineArgs{});
   } else {
     hipLaunchKernelGGL(boundary_rows_wide_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_boundary(const BoundaryArgs& b, const CombineArgs& c, hipStream_t s) {
+  const int nv = ((b.d >> 3) + 63) / 64;
+  hipLaunchKernelGGL(boundary_row_wg_kernel<true>, dim3((unsigned)b.T), dim3(64 * nv), 0, s, b, c);
   return hipGetLastError();
 }
 

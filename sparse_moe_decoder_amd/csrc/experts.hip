@@ -21,6 +21,7 @@
 // so fragment (tile n, k-step s) holds W[16n + l%16][32s + 8(l/16) + i].
 #include "common.h"
 #include "kernels.h"
+#include "combine_device.h"
 
 #include <type_traits>
 
@@ -717,8 +718,8 @@ hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Combine: y[t] = bf16(sum over slots j in order of yk[t*k+j]), FP32, starting
-// from -0.0 (the exact additive identity); slots with an invalid id are skipped.
+// Combine: y[t] = bf16(sum over slots j in order of yk[t*k+j]) (combine_chunk), one
+// 16-byte output chunk per thread.
 __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int d, int E,
                                                       const int32_t* __restrict__ ids,
                                                       const uint16_t* __restrict__ yk,
@@ -728,35 +729,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int k, int d, int E
   if (q >= (int64_t)T * nch) return;
   const int64_t t = q / nch;
   const int c = (int)(q % nch);
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
-  // slots in chunks of eight: all ids, then all rows in flight, then the adds in order
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    bool ok[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = j0 + u < k ? ids[t * k + j0 + u] : -1;
-      ok[u] = e >= 0 && e < E;
-    }
-    u32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = ld_u32x4(yk + ((t * k + (ok[u] ? j0 + u : 0)) * d) + c * 8);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (ok[u]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += lo_bf(v[u][i]);
-          acc[2 * i + 1] += hi_bf(v[u][i]);
-        }
-      }
-  }
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf2(acc[2 * i], acc[2 * i + 1]);
-  st_u32x4(y + t * d + c * 8, o);
+  st_u32x4(y + t * d + c * 8, combine_chunk(t, c, k, d, E, ids, yk));
 }
 
 hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,

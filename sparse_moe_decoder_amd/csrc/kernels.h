@@ -24,6 +24,16 @@ struct BoundaryArgs {
   float c1, c2, eps;
 };
 
+// The combine feeding a fused boundary: the token's k expert rows yk [T*k, d] with
+// their ids [T, k] (invalid ids contribute nothing); y [T, d] receives the combined
+// rows when not null.
+struct CombineArgs {
+  int k, E;
+  const int32_t* ids;
+  const uint16_t* yk;
+  uint16_t* y;
+};
+
 struct RouterArgs {
   int T, d, E;
   const uint16_t* z;  // [T, d] BF16
@@ -83,6 +93,8 @@ struct ExpertArgs {
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
+// the boundary with x = the combine of c (b.x unused); b.d <= kBoundaryWgMaxD
+hipError_t launch_combine_boundary(const BoundaryArgs& b, const CombineArgs& c, hipStream_t s);
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_repack_router(const float* W, uint16_t* out, int E, int d, hipStream_t s);

@@ -110,21 +110,41 @@ __device__ int publish_offsets(const PermArgs& a, int e, int cnt, int* excl_lds)
   return tot[0];
 }
 
-// One block: per-expert running sums over the histogram blocks, then offsets.
+// One block: per-expert totals over the histogram blocks, the offsets, then each
+// block's base (the expert's offset plus the counts of the blocks before it). Thread
+// e walks expert e's column 16 blocks at a time, all 16 loads in flight together.
+constexpr int kScanBatch = 16;
+
 __device__ void scan_all(const PermArgs& a) {
   __shared__ int excl_s[256];
   const int e = threadIdx.x;
+  const bool mine = e < a.E;
   int run = 0;
-  if (e < a.E) {
-    for (int b = 0; b < a.nb; ++b) {
-      int c = a.block_cnt[b * a.E + e];
-      a.block_base[b * a.E + e] = run;
-      run += c;
+  if (mine) {
+    for (int b0 = 0; b0 < a.nb; b0 += kScanBatch) {
+      int cv[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        cv[u] = b0 + u < a.nb ? a.block_cnt[(b0 + u) * a.E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) run += cv[u];
     }
   }
   const int total = publish_offsets(a, e, run, excl_s);
-  if (e < a.E)
-    for (int b = 0; b < a.nb; ++b) a.block_base[b * a.E + e] += excl_s[e];
+  if (mine) {
+    int base = excl_s[e];
+    for (int b0 = 0; b0 < a.nb; b0 += kScanBatch) {
+      int cv[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        cv[u] = b0 + u < a.nb ? a.block_cnt[(b0 + u) * a.E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (b0 + u < a.nb) a.block_base[(b0 + u) * a.E + e] = base;
+        base += cv[u];
+      }
+    }
+  }
   // rows past the valid ones (slots with invalid ids) read as -1
   for (int r = total + threadIdx.x; r < a.n; r += blockDim.x) {
     a.perm[r] = -1;

@@ -173,6 +173,30 @@ def test_sublayer_forward_decode1(beam_gpu):
         assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_forward_boundary_beam(beam_gpu, T):
+    """Beam shapes (d = 5120: ten waves per row): the MoE forward with the next
+    boundary fused into its combine equals the forward then the boundary call, bit
+    for bit, with h and z updated in place."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    moe = beam_gpu["moe"]
+    wl = BASE.with_tokens(T)
+    print(f"[beam] forward+boundary T={T}", flush=True)
+    z, h = sd.tokens(wl, "x", T=T), sd.tokens(wl, "h", T=T)
+    y_ref = torch.empty_like(z)
+    beam.beam_moe_forward(moe.handle, z, y_ref)
+    h_ref, z_ref = beam.beam_sublayer_norm_residual(h, y_ref, beam_gpu["wpost"], beam_gpu["wpre"],
+                                                    wl.n, wl.eps)
+    hh, zz, y = h.clone(), z.clone(), torch.empty_like(z)
+    beam.beam_moe_forward_boundary(moe.handle, zz, hh, beam_gpu["wpost"], beam_gpu["wpre"], wl.n,
+                                   wl.eps, h_out=hh, z_out=zz, y_out=y)
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    assert torch.equal(hh.view(torch.int16), h_ref.view(torch.int16))
+    assert torch.equal(zz.view(torch.int16), z_ref.view(torch.int16))
+
+
 def sampled_tokens(ids, T, hot=(), n_rand=32, seed=0):
     rng = np.random.default_rng(seed)
     pick = set(range(8)) | set(range(T - 8, T)) | set(rng.choice(T, n_rand, replace=False).tolist())

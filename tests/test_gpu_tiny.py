@@ -263,6 +263,104 @@ def test_sublayer_forward_matches_oracle(gpu, host):
     P.assert_bf16_close(got[2], o_y, "tiny y (one call)")
 
 
+def _forward_then_boundary(moe, z, h, wpost, wpre, n, eps, ids_in=None, w_in=None):
+    """Reference sequence: the MoE forward, then the boundary with its output as x."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    T = z.shape[0]
+    E, k = moe.cfg["n_experts"], moe.cfg["topk"]
+    y = torch.empty_like(z)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = None if ids_in is not None else torch.empty((T, E), dtype=torch.float32, device="cuda")
+    beam.beam_moe_forward(moe.handle, z, y, ids_in=ids_in, w_in=w_in, logits_out=lg, ids_out=ids,
+                          w_out=w)
+    h_out, z_out = beam.beam_sublayer_norm_residual(h, y, wpost, wpre, n, eps)
+    out = dict(h=P.bits(h_out), z=P.bits(z_out), y=P.bits(y), ids=ids.cpu().numpy(),
+               w=w.cpu().numpy())
+    if lg is not None:
+        out["logits"] = lg.cpu().numpy()
+    return out
+
+
+def _forward_boundary(moe, z, h, wpost, wpre, n, eps, ids_in=None, w_in=None, want_y=True,
+                      h_in_place=False, z_in_place=False):
+    import torch
+    import sparse_moe_decoder_amd as beam
+    T = z.shape[0]
+    E, k = moe.cfg["n_experts"], moe.cfg["topk"]
+    zz = z.clone() if z_in_place else z
+    hh = h.clone() if h_in_place else h
+    y = torch.empty_like(z) if want_y else None
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lg = None if ids_in is not None else torch.empty((T, E), dtype=torch.float32, device="cuda")
+    h_out, z_out = beam.beam_moe_forward_boundary(
+        moe.handle, zz, hh, wpost, wpre, n, eps, h_out=hh if h_in_place else None,
+        z_out=zz if z_in_place else None, y_out=y, ids_in=ids_in, w_in=w_in, logits_out=lg,
+        ids_out=ids, w_out=w)
+    out = dict(h=P.bits(h_out), z=P.bits(z_out), ids=ids.cpu().numpy(), w=w.cpu().numpy())
+    if want_y:
+        out["y"] = P.bits(y)
+    if lg is not None:
+        out["logits"] = lg.cpu().numpy()
+    return out
+
+
+def _same(a, b, what):
+    for key, v in a.items():
+        assert np.array_equal(v.view(np.uint8), b[key].view(np.uint8)), (what, key)
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+@pytest.mark.parametrize("replay", [False, True])
+def test_forward_boundary_equals_two_calls(gpu, host, T, replay):
+    """The MoE forward with the next boundary fused into its combine equals the
+    forward followed by the boundary call, bit for bit: h', z, y, routing; with
+    h_out = h, z_out = z and without y_out as well."""
+    import torch
+    print(f"[tiny] forward+boundary T={T} replay={replay}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(T)
+    z = torch.randn((T, WL.d), generator=g).to(torch.bfloat16).cuda()
+    h = torch.randn((T, WL.d), generator=g).to(torch.bfloat16).cuda()
+    ids_in = w_in = None
+    if replay:
+        _, ids_in, w_in = gpu["moe"].router_topk(z, want_logits=False)
+        ids_in[0, 0] = WL.E + 3  # an invalid id contributes nothing, on both sides
+    ref = _forward_then_boundary(gpu["moe"], z, h, gpu["wpost"], gpu["wpre"], WL.n, WL.eps,
+                                 ids_in, w_in)
+    for kw in (dict(), dict(want_y=False), dict(h_in_place=True, z_in_place=True)):
+        got = _forward_boundary(gpu["moe"], z, h, gpu["wpost"], gpu["wpre"], WL.n, WL.eps,
+                                ids_in, w_in, **kw)
+        _same(got, ref, f"T={T} {kw}")
+
+
+def test_forward_boundary_wide_rows():
+    """Rows wider than one workgroup's chunks (d = 8448): the combine goes through
+    y_out and the wave-per-row boundary; the same bits as the two calls. Without
+    y_out such a width is rejected."""
+    import sparse_moe_decoder_amd as beam
+    from synth import Workload
+    from synth import device as sd
+    wl = Workload("wide", T=3, d=8448, E=16, G=4, kg=2, k=4, f=256)
+    print(f"[tiny] wide rows {wl}", flush=True)
+    W, b = sd.router(wl)
+    wg, wu, wd = sd.experts(wl)
+    wpost, wpre = sd.norm_weights(wl)
+    moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=8), W, b, wg, wu, wd)
+    try:
+        z = sd.tokens(wl, "x")
+        h = sd.tokens(wl, "h")
+        ref = _forward_then_boundary(moe, z, h, wpost, wpre, wl.n, wl.eps)
+        got = _forward_boundary(moe, z, h, wpost, wpre, wl.n, wl.eps)
+        _same(got, ref, "wide")
+        with pytest.raises(beam.BeamError) as ei:
+            _forward_boundary(moe, z, h, wpost, wpre, wl.n, wl.eps, want_y=False)
+        assert ei.value.status == -2
+    finally:
+        moe.close()
+
+
 def test_edge_sizes(gpu, host):
     """T = 0 is a no-op; T = max_tokens works; T > max_tokens is rejected up front."""
     import torch
