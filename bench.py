@@ -1,11 +1,12 @@
 """Benchmark: one Beam MoE sublayer step (fused boundary + routed MoE FFN) on one MI355X.
 
-A step is one pass of the whole path over one batch of T tokens through
-beam_sublayer_forward: the boundary (post-norm, depth-scaled residual, pre-norm)
-then the MoE FFN (FP32 router, grouped top-k, expert grouping, BF16 SwiGLU
-experts, weighted combine) — the same results as beam_sublayer_norm_residual
-followed by beam_moe_forward, with the boundary inside the routing launch for one
-token. Inputs are seeded synthetic tensors already resident
+A step is one pass of the whole path over one batch of T tokens: the MoE FFN
+(FP32 router, grouped top-k, expert grouping, BF16 SwiGLU experts, weighted
+combine) and one sublayer boundary (post-norm, depth-scaled residual, pre-norm).
+By default (--step boundary-last) it is beam_moe_forward_boundary: the MoE on z,
+then the next sublayer's boundary fused into the combine, as a decode loop runs
+it; --step boundary-first times beam_sublayer_forward (the boundary, then the MoE
+on its z). Both are bit-identical to the separate calls. Inputs are seeded synthetic tensors already resident
 in HBM when the timed region starts; decode steps rotate over distinct token sets
 so the experts touched change from step to step.
 
@@ -44,6 +45,10 @@ def parse():
     p.add_argument("--rotations", type=int, default=None, help="distinct token sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--step", choices=("boundary-first", "boundary-last"), default="boundary-last",
+                   help="boundary-first: beam_sublayer_forward (the boundary, then the MoE on its z); "
+                        "boundary-last: beam_moe_forward_boundary (the MoE on a z computed before the "
+                        "timed region, then the next sublayer's boundary fused into the combine)")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies of BYTES (for scaling HBM "
@@ -140,10 +145,23 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s")
 
-    def step(i):
-        s = i % R
-        beam.beam_sublayer_forward(moe.handle, hs[s], xs[s], wpost, wpre, wl.n, wl.eps, y,
-                                   h_out=h_out, z_out=z)
+    if args.step == "boundary-first":
+        def step(i):
+            s = i % R
+            beam.beam_sublayer_forward(moe.handle, hs[s], xs[s], wpost, wpre, wl.n, wl.eps, y,
+                                       h_out=h_out, z_out=z)
+    else:
+        # each token set's z from its boundary, before the timed region; a step is the MoE on
+        # it and the next boundary (x = the MoE output, written to y as well)
+        z_in = []
+        for s in range(R):
+            z_in.append(beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n,
+                                                         wl.eps)[1])
+
+        def step(i):
+            s = i % R
+            beam.beam_moe_forward_boundary(moe.handle, z_in[s], hs[s], wpost, wpre, wl.n, wl.eps,
+                                           h_out=h_out, z_out=z, y_out=y)
 
     # distinct experts per token set (for the algorithmic byte count)
     distinct = []
@@ -265,7 +283,7 @@ def main():
             "workload": wl.name, "tokens": T, "hidden": wl.d, "experts": wl.E,
             "groups": wl.G, "groups_kept": wl.kg, "topk": wl.k, "d_ff": wl.f,
             "token_sets": R, "distinct_experts_per_step": round(mean_distinct, 1),
-            "mode": mode, "ms_eager": round(ms_eager, 5),
+            "step": args.step, "mode": mode, "ms_eager": round(ms_eager, 5),
             "ms_graph": None if ms_graph is None else round(ms_graph, 5),
             "ms_profiled": round(ms_prof, 5),
             "kernel_us": {k: (None if v is None else round(v, 2)) for k, v in kernel_us.items()},
