@@ -260,8 +260,8 @@ hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s) {
 //   group score = sum of the two largest c of the group (the c itself if E/G = 1)
 //   keep kg groups, then k experts, each by (value desc, index asc)
 //   w_j = (s_j / den) * scale, den summed over the slots in order
-// Selection uses 64-bit keys (order-preserving value bits << 32 | ~index), so one
-// wave max picks the winner and breaks ties toward the lower index.
+// Selection: order-preserving 32-bit keys, a wave max per round and the lowest lane
+// (lowest index) holding it (topk_token).
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ float c_lds[4][256];
   __shared__ int32_t sel_ids[4][32];
