@@ -433,8 +433,9 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs (block b runs
 // on XCD b % 8), so XCD x is given a contiguous range of the tile list, which is
-// ordered (expert, n-tile, m-tile): an expert's m-tiles read each weight tile at
-// about the same time from one L2, and consecutive n-tiles share the expert's rows.
+// ordered by expert, then (in blocks of up to 8 m-tiles) by n-tile, then m-tile:
+// an expert's m-tiles read each weight tile at about the same time from one L2, and
+// consecutive n-tiles share the expert's rows.
 constexpr int GBM = kGemmBM, GBN = 256, GBK = 32, GMAXST = 5;
 constexpr int GSTAGE_A = GBM * GBK, GSTAGE_B = GBN * GBK;  // elements per stage
 constexpr int GSMEM = GMAXST * (GSTAGE_A + GSTAGE_B);      // 160 KB
@@ -665,7 +666,13 @@ __device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile
   }
 }
 
-// Tile (expert, n-tile, m-tile) number L of the list above
+// An XCD runs 32 workgroups at a time; blocks of 8 m-tiles put about 8 m-tiles x 4
+// n-tiles in flight for an expert with many rows, so its row tiles and weight
+// tiles are each re-read from L2 by several concurrent tiles (measured on a skewed
+// 32K-token batch: -4 % gate/up, -15 % down against n-tile-major order).
+constexpr int kGemmMBlock = 8;
+
+// Tile number L of the list above
 __device__ __forceinline__ GemmTile decode_tile(const ExpertArgs& a, int NT, int L) {
   // expert: largest e with tile_start[e] * NT <= L
   int lo = 0, hi = a.E;
@@ -679,10 +686,24 @@ __device__ __forceinline__ GemmTile decode_tile(const ExpertArgs& a, int NT, int
   const int cnt = a.offsets[e + 1] - a.offsets[e];
   // equal tiles, a multiple of 64 rows each (at most GBM; the last one is not empty)
   const int per = (((cnt + mtiles - 1) / mtiles) + 63) & ~63;
+  // an expert's tiles in blocks of up to kGemmMBlock m-tiles: block by block, each
+  // n-tile with the block's m-tiles (an expert of at most kGemmMBlock m-tiles is one
+  // block: n-tile by n-tile, all its m-tiles)
+  int mi, ni;
+  const int nfull = mtiles / kGemmMBlock;
+  if (within < nfull * NT * kGemmMBlock) {
+    const int mb = within / (NT * kGemmMBlock), r = within % (NT * kGemmMBlock);
+    ni = r / kGemmMBlock;
+    mi = mb * kGemmMBlock + r % kGemmMBlock;
+  } else {
+    const int rem = mtiles - nfull * kGemmMBlock, r = within - nfull * NT * kGemmMBlock;
+    ni = r / rem;
+    mi = nfull * kGemmMBlock + r % rem;
+  }
   GemmTile t;
   t.e = e;
-  t.nb = within / mtiles;
-  t.row0 = a.offsets[e] + (within % mtiles) * per;
+  t.nb = ni;
+  t.row0 = a.offsets[e] + mi * per;
   t.rows = min(per, a.offsets[e + 1] - t.row0);
   return t;
 }
