@@ -115,11 +115,19 @@ hipError_t launch_repack_router(const float* W, uint16_t* out, int E, int d, hip
   return hipGetLastError();
 }
 
-// Tile: 256 tokens x 64 experts, 4 waves of 64 tokens x 64 experts (2 x 2 tiles of
-// 32x32x16, three B fragments per product). K advances 32 at a time through four LDS
-// stages filled by direct global-to-LDS loads, three K blocks ahead.
-constexpr int RBM = 256, RBN = 64, RBK = 32, RSTAGES = 4;
+// Tile: 256 tokens x 64 experts per workgroup of 8 waves (two per SIMD): wave w =
+// 2 wm + wn holds tokens [64 wm, 64 wm + 64) x experts [32 wn, 32 wn + 32) as 2 x 1
+// tiles of 32x32x16, three B fragments (the weight's three parts) per product. K
+// advances 32 at a time through NS LDS stages (5 when d / 32 is a multiple of 5,
+// else 4) filled by direct global-to-LDS loads NS - 1 K blocks ahead; each wave's
+// copies of a block are spread between its MFMA groups.
+//   A stage: 256 rows x 32 values (64 B per row), chunk c of row r in slot
+//     c ^ ((r / 4) % 4); wave w copies rows [32 w, 32 w + 32).
+//   B stage: 12 packed 16x16x32 blocks (part p, 16-expert tile t: block 4 p + t);
+//     waves 0-3 copy two blocks each, waves 4-7 one.
+constexpr int RBM = 256, RBN = 64, RBK = 32, RMAXST = 5;
 constexpr int RSTAGE_A = RBM * RBK, RSTAGE_B = 3 * RBN * RBK;  // elements
+static_assert(RMAXST * (RSTAGE_A + RSTAGE_B) * 2 <= 160 * 1024, "LDS");
 
 __device__ __forceinline__ uint32_t lds_addr_r(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -133,113 +141,136 @@ __device__ __forceinline__ void lds_dma16_r(const void* g, uint32_t lds) {
 __device__ __forceinline__ int ra_slot(int row, int c) {
   return row * RBK + ((c ^ ((row >> 2) & 3)) << 3);
 }
+// at most n K blocks of this wave's copies in flight (per block: 4 copies for
+// waves 0-3, 3 for waves 4-7)
+__device__ __forceinline__ void router_wait_blocks(int n, bool four) {
+  if (four) {
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
 
-__global__ __launch_bounds__(256) void router_bf16x3_kernel(RouterX3Args a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[RSTAGES * (RSTAGE_A + RSTAGE_B)];
+template <int NS>
+__device__ __forceinline__ void router_x3_tile(const RouterX3Args& a, uint16_t* smem) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int wm = wvu >> 1, wn = wvu & 1;
+  const bool four = wvu < 4;  // this wave copies two B blocks per K block
   const int t0 = blockIdx.x * RBM;
   const int eb = blockIdx.y;  // 64-expert block
   const int rows = min(RBM, a.T - t0);
   const int KS = a.d / 32, NT = a.E / 16;
-  // A: wave wv fills rows [64 wv, 64 wv + 64): 4 instructions of 16 rows
-  int aoff[4];
+  const int nkb = a.d / RBK;  // a multiple of NS
+  int aoff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wv * 64 + i * 16 + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wv * 32 + i * 16 + (lane >> 2);
     const int rr = r < rows ? r : 0;
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     aoff[i] = (t0 + rr) * a.d + c * 8;
   }
-  // B: 12 blocks per stage (part p, 16-expert tile t: block p * 4 + t); wave wv copies 3
-  int boff[3];
+  const int b0 = four ? 2 * wvu : 8 + (wvu - 4);  // first B block of this wave
+  int boff[2];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int b = wvu * 3 + i, p = b >> 2, t = b & 3;
+  for (int i = 0; i < 2; ++i) {
+    const int b = b0 + i, p = b >> 2, t = b & 3;
     boff[i] = ((p * NT + eb * 4 + t) * KS) * 512 + lane * 8;
   }
-  auto issue = [&](int kb, int st) {
-    const uint32_t A = lds_addr_r(smem + st * RSTAGE_A) + (uint32_t)(wvu * 64 * RBK * 2);
-    const uint32_t B = lds_addr_r(smem + RSTAGES * RSTAGE_A + st * RSTAGE_B) +
-                       (uint32_t)(wvu * 3 * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16_r(a.z + aoff[i] + kb * RBK, A + i * 16 * RBK * 2);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) lds_dma16_r(a.wx3 + boff[i] + kb * 512, B + i * 1024);
+  auto stage_a = [&](int st) -> uint16_t* { return smem + st * RSTAGE_A; };
+  auto stage_b = [&](int st) -> uint16_t* { return smem + NS * RSTAGE_A + st * RSTAGE_B; };
+  // copy q of K block kb (0, 1: A rows; 2, 3: B blocks, 3 only for waves 0-3)
+  auto issue = [&](int kb, int st, int q) {
+    if (q < 2)
+      lds_dma16_r(a.z + aoff[q] + kb * RBK,
+                  lds_addr_r(stage_a(st)) + (uint32_t)(wvu * 32 * RBK * 2) + q * 16 * RBK * 2);
+    else if (q == 2 || four)
+      lds_dma16_r(a.wx3 + boff[q - 2] + kb * 512,
+                  lds_addr_r(stage_b(st)) + (uint32_t)(b0 * 1024) + (q - 2) * 1024);
   };
   const int l32 = lane & 31, lh = lane >> 5;
-  int aread[2][2], bread[2][2];
+  int aread[2][2], bread[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) aread[mt][kk] = ra_slot(wv * 64 + mt * 32 + l32, kk * 2 + lh);
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-      bread[nn][kk] = (nn * 2 + ((lane >> 4) & 1)) * 512 + ((lane & 15) + 16 * (kk * 2 + lh)) * 8;
+    for (int mt = 0; mt < 2; ++mt) aread[mt][kk] = ra_slot(wm * 64 + mt * 32 + l32, kk * 2 + lh);
+    bread[kk] = (wn * 2 + ((lane >> 4) & 1)) * 512 + ((lane & 15) + 16 * (kk * 2 + lh)) * 8;
   }
-  f32x16 acc[2][2];
+  f32x16 acc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
-  const int nkb = a.d / RBK;
   auto step = [&](int kb, auto S) {
     constexpr int st = decltype(S)::value;
-    const int left = nkb - 1 - kb;
-    if (left >= 2) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-    else if (left == 1) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int later = nkb - 1 - kb;
+    router_wait_blocks(later < NS - 2 ? later : NS - 2, four);
     __builtin_amdgcn_s_barrier();
-    const uint16_t* A = smem + st * RSTAGE_A;
-    const uint16_t* B = smem + RSTAGES * RSTAGE_A + st * RSTAGE_B;
-    u32x4 fa[2][2], fb[2][2][3];
+    const uint16_t* A = stage_a(st);
+    const uint16_t* B = stage_b(st);
+    u32x4 fa[2][2], fb[2][3];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) fa[kk][mt] = ld_u32x4(A + aread[mt][kk]);
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-        for (int p = 0; p < 3; ++p) fb[kk][nn][p] = ld_u32x4(B + p * 4 * 512 + bread[nn][kk]);
+      for (int p = 0; p < 3; ++p) fb[kk][p] = ld_u32x4(B + p * 4 * 512 + bread[kk]);
     }
-    if (kb + RSTAGES - 1 < nkb) issue(kb + RSTAGES - 1, (st + 3) & 3);
+    const bool more = kb + NS - 1 < nkb;
+    const int kn = kb + NS - 1, sn = (st + NS - 1) % NS;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
+      for (int p = 0; p < 3; ++p) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn][p], acc[mt][nn]);
+        for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(fa[kk][mt], fb[kk][p], acc[mt]);
+        const int g = kk * 3 + p;  // six MFMA pairs; a copy after pairs 0, 1, 3, 4
+        if (g == 0 || g == 1 || g == 3 || g == 4) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) issue(kn, sn, g < 2 ? g : g - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
   };
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  for (int kb = 0; kb < nkb; kb += 4) {
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) issue(j, j, q);
+  for (int kb = 0; kb < nkb; kb += NS) {
     step(kb, std::integral_constant<int, 0>{});
     step(kb + 1, std::integral_constant<int, 1>{});
     step(kb + 2, std::integral_constant<int, 2>{});
     step(kb + 3, std::integral_constant<int, 3>{});
+    if constexpr (NS == 5) step(kb + 4, std::integral_constant<int, 4>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wv * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < rows)
-          a.logits[(int64_t)(t0 + row) * a.E + eb * 64 + nn * 32 + l32] = acc[mt][nn][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (row < rows) a.logits[(int64_t)(t0 + row) * a.E + eb * 64 + wn * 32 + l32] = acc[mt][r];
+    }
+}
+
+__global__ __launch_bounds__(512) void router_bf16x3_kernel(RouterX3Args a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[RMAXST * (RSTAGE_A + RSTAGE_B)];
+  if ((a.d / RBK) % 5 == 0)
+    router_x3_tile<5>(a, smem);
+  else
+    router_x3_tile<4>(a, smem);
 }
 
 hipError_t launch_router_bf16x3(const RouterX3Args& a, hipStream_t s) {
   dim3 grid((unsigned)((a.T + RBM - 1) / RBM), (unsigned)(a.E / RBN));
-  hipLaunchKernelGGL(router_bf16x3_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(router_bf16x3_kernel, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
