@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(PermArgs a) {
 // token per wave at a time), then the histogram, offsets and stable scatter from
 // LDS, all in one launch.
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, PermArgs a) {
-  __shared__ float c_lds[16][256];
+  __shared__ __attribute__((aligned(16))) float c_lds[16][256];
   __shared__ int32_t sel[16][32];
   __shared__ int32_t ids_lds[1024];
   __shared__ int cnt[256];
@@ -261,49 +261,51 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(TopkArgs ta, 
 }
 
 // Grouping of at most 64 slots by one wave, from the slot ids in LDS (one slot per
-// lane), everything by counting over the wave: a slot's row
-// is the number of valid slots ordered before it by (expert, slot); lane l owns
-// experts 4l .. 4l+3 for counts, offsets, the active list and the tile table.
+// lane). Lane l owns experts 4l .. 4l+3 for counts, offsets, the active list and
+// the tile table. The counts come from an LDS histogram (cnt, 256 ints of LDS
+// scratch; LDS atomics only count); the exclusive prefixes over experts from
+// lane-local sums and ballot bit-plane scans across the lanes; a slot's row is its
+// expert's offset (off, 256 ints of LDS scratch) plus the number of earlier slots
+// with the same expert (a ballot match mask over the id's bit planes): the rows
+// follow (expert, slot) order exactly. At most 64 slots means at most one
+// grouped-GEMM tile per expert.
 static_assert(kGemmBM >= 64, "the one-wave grouping assumes at most one tile per expert");
 __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_t* ids_lds,
-                                                 int lane) {
+                                                 int lane, int* cnt, int* off) {
   const int n = a.n, E = a.E;
   const int e_mine = lane < n ? ids_lds[lane] : -1;
   const bool v = valid_id(e_mine, E);
-  int pos = 0, nvalid = 0, c4[4] = {0, 0, 0, 0}, below4[4] = {0, 0, 0, 0};
-  for (int s2 = 0; s2 < n; ++s2) {
-    const int e2 = __builtin_amdgcn_readlane(e_mine, s2);
-    if (!valid_id(e2, E)) continue;
-    ++nvalid;
-    pos += (e2 < e_mine || (e2 == e_mine && s2 < lane)) ? 1 : 0;
+  *(int4*)(cnt + 4 * lane) = make_int4(0, 0, 0, 0);
+  wave_lds_sync();
+  if (v) atomicAdd(&cnt[e_mine], 1);
+  wave_lds_sync();
+  const int4 c = *(const int4*)(cnt + 4 * lane);
+  const int c4[4] = {c.x, c.y, c.z, c.w};
+  // exclusive prefixes across lanes of: the lane's slot total (< 128: 7 bit planes),
+  // its active experts and tiles (<= 4: 3 bit planes; one tile per active expert)
+  const int tot = c4[0] + c4[1] + c4[2] + c4[3];
+  int act4 = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c4[i] += (e2 == 4 * lane + i) ? 1 : 0;
-      below4[i] += (e2 < 4 * lane + i) ? 1 : 0;
-    }
-  }
-  if (v) {
-    a.perm[pos] = lane;
-    if (a.perm2) a.perm2[pos] = lane;
-  }
-  // active-list index and tile table: exclusive scans over experts (4 per lane). A
-  // lane's own counts are below 8 (at most 4 experts, one tile each: n <= bm), so
-  // each scan is three bit planes: ballot, then count the set lanes below.
-  int act4 = 0, tiles4 = 0;
+  for (int i = 0; i < 4; ++i) act4 += c4[i] > 0 ? 1 : 0;
+  int base = 0, nvalid = 0, aidx = 0, n_act = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    act4 += c4[i] > 0 ? 1 : 0;
-    tiles4 += (c4[i] + a.bm - 1) / a.bm;
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t bb = __ballot((tot >> b) & 1);
+    base += lanes_below(bb) << b;
+    nvalid += __popcll(bb) << b;
   }
-  int aidx = 0, tidx = 0, n_act = 0, n_tiles = 0;
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
-    const uint64_t ba = __ballot((act4 >> b) & 1), bt = __ballot((tiles4 >> b) & 1);
+    const uint64_t ba = __ballot((act4 >> b) & 1);
     aidx += lanes_below(ba) << b;
-    tidx += lanes_below(bt) << b;
     n_act += __popcll(ba) << b;
-    n_tiles += __popcll(bt) << b;
   }
+  int below4[4];
+  below4[0] = base;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) below4[i] = below4[i - 1] + c4[i - 1];
+  *(int4*)(off + 4 * lane) = make_int4(below4[0], below4[1], below4[2], below4[3]);
+  int tidx = aidx;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * lane + i;
@@ -312,15 +314,30 @@ __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_
       a.offsets[e] = below4[i];
       if (a.offsets2) a.offsets2[e] = below4[i];
       a.tile_start[e] = tidx;
-      if (c4[i] > 0) a.active[aidx++] = e;
-      tidx += (c4[i] + a.bm - 1) / a.bm;
+      if (c4[i] > 0) {
+        a.active[tidx] = e;
+        ++tidx;
+      }
     }
   }
   if (lane == 0) {
     a.offsets[E] = nvalid;
     if (a.offsets2) a.offsets2[E] = nvalid;
-    a.tile_start[E] = n_tiles;
+    a.tile_start[E] = n_act;
     *a.n_active = n_act;
+  }
+  // the slot's row: earlier lanes with the same (valid) id, plus its expert's offset
+  uint64_t match = __ballot(v);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t bb = __ballot(v && ((e_mine >> bit) & 1));
+    match &= ((e_mine >> bit) & 1) ? bb : ~bb;
+  }
+  wave_lds_sync();
+  if (v) {
+    const int pos = off[e_mine] + lanes_below(match);
+    a.perm[pos] = lane;
+    if (a.perm2) a.perm2[pos] = lane;
   }
   if (lane >= nvalid && lane < n) {
     a.perm[lane] = -1;
@@ -330,7 +347,7 @@ __device__ __forceinline__ void group_slots_wave(const PermArgs& a, const int32_
 
 // Tiny batches (T*k <= 64): the waves route one token each, then wave 0 groups.
 __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, PermArgs a) {
-  __shared__ float c_lds[16][256];
+  __shared__ __attribute__((aligned(16))) float c_lds[16][256];
   __shared__ int32_t sel[16][32];
   __shared__ int32_t ids_lds[64];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, P
   }
   __syncthreads();
   if (wv != 0) return;
-  group_slots_wave(a, ids_lds, lane);
+  group_slots_wave(a, ids_lds, lane, reinterpret_cast<int*>(c_lds[0]), reinterpret_cast<int*>(c_lds[1]));
 }
 
 // Router, grouped top-k and grouping of a small batch (T <= 16 tokens, T * k <= 64
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
                                                                PermArgs pa, uint32_t* done,
                                                                uint64_t* sc, BoundaryArgs ba) {
   __shared__ float part[3][kRouterRT];
-  __shared__ float c_lds[4][256];
+  __shared__ __attribute__((aligned(16))) float c_lds[4][256];
   __shared__ int32_t sel[4][32];
   __shared__ int32_t ids_lds[64];
   __shared__ int is_last;
@@ -413,7 +430,8 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
     if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
   }
   __syncthreads();
-  if (wv == 0) group_slots_wave(pa, ids_lds, lane);
+  if (wv == 0)
+    group_slots_wave(pa, ids_lds, lane, reinterpret_cast<int*>(c_lds[0]), reinterpret_cast<int*>(c_lds[1]));
 }
 
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
