@@ -361,6 +361,38 @@ def test_forward_boundary_wide_rows():
         moe.close()
 
 
+def test_single_token_routing_ties():
+    """One token through the one-launch routing with
+    exact ties: experts 2i and 2i+1 share their router row and bias, so their scores
+    are equal bit for bit and the lower index must come first. Ids exact and weights
+    within one ulp of the oracle's top-k on the GPU's own logits, over several tokens."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    wl = WL
+    W, b = sd.router(wl)
+    W = W.clone()
+    b = b.clone()
+    W[1::2] = W[0::2]
+    b[1::2] = b[0::2]
+    wg, wu, wd = sd.experts(wl)
+    moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=4), W, b, wg, wu, wd)
+    try:
+        bias = b.cpu().numpy()
+        for t in range(6):
+            z = (torch.randn((1, wl.d), generator=torch.Generator().manual_seed(100 + t))
+                 .to(torch.bfloat16).cuda())
+            _, r = moe.forward(z, want_routing=True)
+            lg = r["logits_out"].cpu().numpy()
+            assert np.array_equal(lg[:, 0::2].view(np.uint32), lg[:, 1::2].view(np.uint32))
+            o_ids, o_w, _, _ = oracle.topk(lg, bias, wl.G, wl.kg, wl.k, wl.scale)
+            assert np.array_equal(r["ids_out"].cpu().numpy(), o_ids), t
+            ulps = np.abs(r["w_out"].cpu().numpy().view(np.int32).astype(np.int64) - o_w.view(np.int32))
+            assert ulps.max() <= 1
+    finally:
+        moe.close()
+
+
 def test_edge_sizes(gpu, host):
     """T = 0 is a no-op; T = max_tokens works; T > max_tokens is rejected up front."""
     import torch
