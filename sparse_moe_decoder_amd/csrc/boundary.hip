@@ -33,6 +33,11 @@ __global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a, C
   const int idx = threadIdx.x;
   const bool ok = idx < nch;
   const int li = ok ? idx : 0;
+  // h and the norm weights first: with COMBINE their loads run under the combine's
+  // dependent loads (ids, then the expert rows)
+  u32x4 hv = ld_u32x4((const u32x4*)(a.h + t * a.d) + li);
+  const u32x4 wo = ld_u32x4((const u32x4*)a.w_post + li);
+  const u32x4 wr = ld_u32x4((const u32x4*)a.w_pre + li);
   u32x4 xv;
   if constexpr (COMBINE) {
     xv = combine_chunk(t, li, cb.k, a.d, cb.E, cb.ids, cb.yk);
@@ -40,9 +45,6 @@ __global__ __launch_bounds__(1024) void boundary_row_wg_kernel(BoundaryArgs a, C
   } else {
     xv = ld_u32x4((const u32x4*)(a.x + t * a.d) + li);
   }
-  u32x4 hv = ld_u32x4((const u32x4*)(a.h + t * a.d) + li);
-  const u32x4 wo = ld_u32x4((const u32x4*)a.w_post + li);
-  const u32x4 wr = ld_u32x4((const u32x4*)a.w_pre + li);
   float ss = wave_sum(ok ? sumsq8(xv) : 0.0f);
   if (lane == 0) red[0][wv] = ss;
   __syncthreads();
