@@ -14,6 +14,9 @@ Parity status of each step (how it is pinned is listed in ``tests/test_oracle_pi
   O4 permutation ..... pinned (brute-force sort of (expert, slot) pairs)
   O5/O6 experts ...... pinned (permutation-matrix closed forms, one-expert dense SwiGLU x 2.5,
                         all-experts dense mixture, FP64 error bound)
+  O7 MXFP4 weights ... pinned (hand-derived blocks from the OCP MX v1.0 definitions: scale
+                        rule, every rounding tie, saturation, signed zero; exact round trip
+                        of representable blocks; the half-step error bound; sign symmetry)
 """
 from __future__ import annotations
 
@@ -62,8 +65,11 @@ def lib():
         L.oracle_permute.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp]
         L.oracle_expert_rows.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.oracle_combine.argtypes = [i64, i64, i64, i64, vp, vp, vp]
+        L.oracle_mxfp4_quantize.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_mxfp4_dequantize.argtypes = [i64, i64, vp, vp, vp]
         for name in ("oracle_boundary", "oracle_router", "oracle_topk", "oracle_permute",
-                     "oracle_expert_rows", "oracle_combine"):
+                     "oracle_expert_rows", "oracle_combine", "oracle_mxfp4_quantize",
+                     "oracle_mxfp4_dequantize"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +191,31 @@ def combine(yk, ids=None, E=None):
     _check(lib().oracle_combine(T, k, d, int(E if E is not None else 1 << 30), _p(ids), _p(yk),
                                 _p(y)), "oracle_combine")
     return y
+
+
+def mxfp4_quantize(v):
+    """O7: BF16 [rows, K] -> (codes uint8 [rows, K/2], scales uint8 [rows, K/32])."""
+    v = _c(v, np.uint16)
+    shape = v.shape
+    K = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    codes = np.empty(shape[:-1] + (K // 2,), dtype=np.uint8)
+    scales = np.empty(shape[:-1] + (K // 32,), dtype=np.uint8)
+    _check(lib().oracle_mxfp4_quantize(rows, K, _p(v), _p(codes), _p(scales)),
+           "oracle_mxfp4_quantize")
+    return codes, scales
+
+
+def mxfp4_dequantize(codes, scales):
+    """O7: exact BF16 values of MXFP4 codes [rows, K/2] with scales [rows, K/32]."""
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    K = codes.shape[-1] * 2
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    assert scales.shape[-1] * 32 == K
+    out = np.empty(codes.shape[:-1] + (K,), dtype=np.uint16)
+    _check(lib().oracle_mxfp4_dequantize(rows, K, _p(codes), _p(scales), _p(out)),
+           "oracle_mxfp4_dequantize")
+    return out
 
 
 # ---- composition -------------------------------------------------------------------------------

@@ -305,3 +305,78 @@ int oracle_combine(int64_t T, int64_t k, int64_t d, int64_t E, const int32_t* id
     }
   return 0;
 }
+
+/*
+ * O7 — 4-bit expert weights.
+ * [vLLM §Modellarchitektur]: the 256 routed experts are stored in a 4-bit
+ *   floating-point format (NVFP4 there); [SGLang §BF16、NVFP4 和 FP8 模型支持]: the
+ *   serving path takes BF16, NVFP4 and FP8 checkpoints.
+ * Reading: the 4-bit format here is MXFP4 as the OCP Microscaling Formats (MX)
+ *   specification v1.0 defines it, the block-scaled 4-bit format gfx950 converts
+ *   natively: FP4 E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 of a
+ *   code is the sign) that share one E8M0 scale 2^X (stored as X + 127) per block of
+ *   32 consecutive values along K. Quantising a block follows the specification's
+ *   conversion: X = floor(log2(max |v|)) - 2, where 2 is the exponent of the largest
+ *   E2M1 normal, clamped to [-127, 127] (an all-zero block takes X = -127); each
+ *   element is v / 2^X rounded to the nearest E2M1 value, ties to the even code,
+ *   magnitudes beyond 6 saturating to 6, with the sign kept even when the magnitude
+ *   rounds to zero. Element 2i of a row is the low nibble of byte i.
+ *   Every E2M1 value times 2^X is a BF16 number, so dequantisation is exact, and the
+ *   experts then compute exactly as in O5 on the dequantised weights (activations
+ *   stay BF16: the decode path is bound by the weight stream, not by arithmetic).
+ */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int oracle_mxfp4_quantize(int64_t rows, int64_t K, const uint16_t* v, uint8_t* codes,
+                          uint8_t* scales) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < K / 32; ++b) {
+      const uint16_t* blk = v + r * K + b * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const double a = fabs((double)oracle_f32(blk[i]));
+        if (!(a <= 3.4e38)) return -1; /* inf or nan */
+        if (a > amax) amax = a;
+      }
+      int X = -127;
+      if (amax > 0.0) {
+        int e;
+        frexp(amax, &e); /* amax = m * 2^e, 0.5 <= m < 1: floor(log2(amax)) = e - 1 */
+        X = (e - 1) - 2;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+      }
+      scales[r * (K / 32) + b] = (uint8_t)(X + 127);
+      for (int i = 0; i < 32; ++i) {
+        const float vi = oracle_f32(blk[i]);
+        const double q = ldexp(fabs((double)vi), -X);
+        int best = 0;
+        for (int j = 1; j < 8; ++j) {
+          const double dj = fabs(q - kE2M1[j]), db = fabs(q - kE2M1[best]);
+          if (dj < db || (dj == db && (j & 1) == 0)) best = j;
+        }
+        const int code = best | (signbit(vi) ? 8 : 0);
+        uint8_t* byte = codes + r * (K / 2) + b * 16 + i / 2;
+        if (i % 2 == 0) *byte = (uint8_t)code;
+        else *byte = (uint8_t)(*byte | (code << 4));
+      }
+    }
+  return 0;
+}
+
+int oracle_mxfp4_dequantize(int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
+                            uint16_t* out) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < K; ++i) {
+      const int s = scales[r * (K / 32) + i / 32];
+      if (s == 255) return -1; /* the E8M0 NaN encoding */
+      const uint8_t byte = codes[r * (K / 2) + i / 2];
+      const int code = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+      const double mag = ldexp(kE2M1[code & 7], s - 127);
+      const double val = (code & 8) ? -mag : mag;
+      out[r * K + i] = oracle_bf16((float)val); /* exact: val is a BF16 number */
+    }
+  return 0;
+}

@@ -69,6 +69,15 @@ int oracle_expert_rows(int64_t R, int64_t d, int64_t f, const uint16_t* zrows,
 int oracle_combine(int64_t T, int64_t k, int64_t d, int64_t E, const int32_t* ids,
                    const uint16_t* yk, uint16_t* y);
 
+/* O7: MXFP4 (OCP MX v1.0: E2M1 elements, one E8M0 scale per 32 values along K).
+ * v: [rows, K] BF16, K % 32 == 0. codes: [rows, K/2] (element 2i in the low
+ * nibble of byte i); scales: [rows, K/32] (X + 127). Non-finite input: -1. */
+int oracle_mxfp4_quantize(int64_t rows, int64_t K, const uint16_t* v, uint8_t* codes,
+                          uint8_t* scales);
+/* Exact inverse image: out [rows, K] BF16 = sign * E2M1 value * 2^(scale - 127). */
+int oracle_mxfp4_dequantize(int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
+                            uint16_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,13 @@ MUTATIONS = [
     ("gate and up swapped", "oracle_silu(gq) * uq", "oracle_silu(uq) * gq"),
     ("weight after rounding", "yk[r * d + o] = oracle_bf16(wrow[r] * acc);",
      "yk[r * d + o] = oracle_bf16(wrow[r] * oracle_f32(oracle_bf16(acc)));"),
+    ("mx scale rounds up", "X = (e - 1) - 2;", "X = e - 2;"),
+    ("mx element exponent 3", "X = (e - 1) - 2;", "X = (e - 1) - 3;"),
+    ("mx ties to the larger", "(dj == db && (j & 1) == 0)", "(dj == db && j > best)"),
+    ("mx zero loses its sign", "best | (signbit(vi) ? 8 : 0)", "best | (vi < 0.0f ? 8 : 0)"),
+    ("mx nibbles swapped", "if (i % 2 == 0) *byte = (uint8_t)code;", "if (i % 2 == 1) *byte = (uint8_t)code;"),
+    ("mx dequant scale off by one", "ldexp(kE2M1[code & 7], s - 127)", "ldexp(kE2M1[code & 7], s - 126)"),
+    ("mx no clamp of tiny scales", "if (X < -127) X = -127;", ""),
     ("combine rounds each add", "acc = acc + oracle_f32(yk[(t * k + j) * d + o]);",
      "acc = oracle_f32(oracle_bf16(acc + oracle_f32(yk[(t * k + j) * d + o])));"),
 ]

@@ -529,3 +529,114 @@ def test_expert_weight_applied_before_rounding():
         alt = F(to_bf16((np.float32(wrow[r]) * F(to_bf16(s))).astype(np.float32)))
         assert np.array_equal(F(yk[r]), want)
         assert not np.array_equal(want, alt)  # the case does tell the two readings apart
+
+
+# ---- O7: MXFP4 expert weights ------------------------------------------------------------------
+
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _golden_value(v):
+    """A fixture value: a decimal, "-0.0", or "a*2^b" / "2^b" (exact binary fractions)."""
+    if isinstance(v, str):
+        if v == "-0.0":
+            return -0.0
+        mant, _, exp = v.rpartition("2^")
+        m = float(mant.rstrip("*")) if mant else 1.0
+        return math.ldexp(m, int(exp))
+    return float(v)
+
+
+def _to_bf16_exact(vals):
+    f = np.asarray(vals, dtype=np.float32)
+    bits = f.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "fixture value is not exactly BF16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def _nibbles(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = c & 15
+    out[..., 1::2] = c >> 4
+    return out
+
+
+def test_mxfp4_golden_blocks():
+    """Hand-derived blocks (tests/golden/mxfp4.json): the scale rule, every rounding tie,
+    saturation, signed zero, the clamped scale of tiny and the largest blocks."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "mxfp4.json")
+    blocks = json.load(open(path))["blocks"]
+    for blk in blocks:
+        vals = [0.0] * 32
+        for i, v in blk["inputs"]:
+            vals[i] = _golden_value(v)
+        want = [0] * 32
+        for i, c in blk["codes"]:
+            want[i] = c
+        codes, scales = oracle.mxfp4_quantize(_to_bf16_exact(vals)[None, :])
+        assert int(scales[0, 0]) == blk["scale"], blk["note"]
+        assert _nibbles(codes)[0].tolist() == want, blk["note"]
+        # the dequantised block is the E2M1 grid value times the scale, exactly
+        deq = oracle.bf16_to_f32(oracle.mxfp4_dequantize(codes, scales))[0].astype(np.float64)
+        for i, c in enumerate(want):
+            m = math.ldexp(_E2M1[c & 7], blk["scale"] - 127)
+            assert deq[i] == (-m if c & 8 else m) and math.copysign(1, deq[i]) == (-1 if c & 8 else 1)
+
+
+def test_mxfp4_round_trip_of_representable_blocks():
+    """A block whose values are E2M1 values times 2^X, with one magnitude 4 or 6 so that
+    floor(log2 max) - 2 = X, quantises to exactly those codes and dequantises to itself."""
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        X = int(rng.integers(-120, 121))
+        codes = rng.integers(0, 16, size=32)
+        codes[int(rng.integers(0, 32))] = int(rng.choice([6, 7, 14, 15]))
+        vals = np.array([(-1.0 if c & 8 else 1.0) * math.ldexp(_E2M1[c & 7], X) for c in codes])
+        q, s = oracle.mxfp4_quantize(_to_bf16_exact(vals)[None, :])
+        assert int(s[0, 0]) == X + 127
+        assert _nibbles(q)[0].tolist() == codes.tolist()
+        back = oracle.mxfp4_dequantize(q, s)[0]
+        assert back.tolist() == _to_bf16_exact(vals).tolist()
+
+
+def test_mxfp4_scale_rule_and_half_step_bound():
+    """Random BF16 blocks: scale byte = floor(log2 max|v|) - 2 + 127 (from frexp), and each
+    element lands on the grid point nearest v / 2^X (within half the local grid step),
+    saturating at 6; the sign of the code is the sign of v."""
+    rng = np.random.default_rng(11)
+    for std in (0.02, 1.0, 300.0):
+        v32 = (rng.standard_normal((64, 128)) * std).astype(np.float32)
+        vb = (v32.view(np.uint32) >> 16).astype(np.uint16)  # truncation: exact BF16 inputs
+        q, s = oracle.mxfp4_quantize(vb)
+        codes = _nibbles(q)
+        vals = oracle.bf16_to_f32(vb).astype(np.float64)
+        for r in range(vals.shape[0]):
+            for b in range(vals.shape[1] // 32):
+                blk = vals[r, 32 * b:32 * b + 32]
+                _, e = math.frexp(float(np.max(np.abs(blk))))
+                X = max(-127, min(127, (e - 1) - 2))
+                assert int(s[r, b]) == X + 127
+                for i in range(32):
+                    c = int(codes[r, 32 * b + i])
+                    qv = abs(blk[i]) / 2.0 ** X
+                    g = _E2M1[c & 7]
+                    assert bool(c & 8) == (math.copysign(1.0, blk[i]) < 0)
+                    if qv >= 6.0:
+                        assert g == 6.0
+                    else:
+                        step = 0.5 if qv < 2.0 else (1.0 if qv < 4.0 else 2.0)
+                        assert abs(qv - g) <= step / 2, (qv, g)
+                        assert all(abs(qv - g) <= abs(qv - o) for o in _E2M1)
+
+
+def test_mxfp4_sign_symmetry():
+    rng = np.random.default_rng(3)
+    v32 = (rng.standard_normal((8, 64)) * 0.05).astype(np.float32)
+    vb = (v32.view(np.uint32) >> 16).astype(np.uint16)
+    q1, s1 = oracle.mxfp4_quantize(vb)
+    q2, s2 = oracle.mxfp4_quantize(vb ^ np.uint16(0x8000))
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(q1 ^ np.uint8(0x88), q2)
