@@ -50,6 +50,10 @@ def parse():
                         "boundary-last: beam_moe_forward_boundary (the MoE on a z computed before the "
                         "timed region, then the next sublayer's boundary fused into the combine)")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU sample")
+    p.add_argument("--experts", choices=("bf16", "mxfp4"), default="bf16",
+                   help="expert weight format: BF16, or MXFP4 (4-bit E2M1 codes with one E8M0 "
+                        "scale per 32 values, quantised on the device from the BF16 weights; "
+                        "BF16 activations; decode batches only)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies of BYTES (for scaling HBM "
                         "counter readings) and exit")
@@ -133,7 +137,19 @@ def main():
     wpost, wpre = sd.norm_weights(wl)
     W, b = sd.router(wl)
     wg, wu, wd = sd.experts(wl)
-    moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, wg, wu, wd)
+    mx = args.experts == "mxfp4"
+    if mx and not decode:
+        print("--experts mxfp4 covers the decode batches (T <= 128)", file=sys.stderr)
+        sys.exit(2)
+    if mx:
+        fp4 = []
+        for t in (wg, wu, wd):
+            fp4 += list(beam.beam_mxfp4_quantize(t))
+        moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, None, None, None,
+                           mxfp4=tuple(fp4))
+        del fp4
+    else:
+        moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, wg, wu, wd)
     del wg, wu, wd
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -238,17 +254,18 @@ def main():
 
     # roofline of the dominant kernel (expert gate/up)
     gu_us = kernel_us.get("gate_up")
-    src = source_hash("experts.hip", "common.h")
+    src = source_hash("experts_mxfp4.hip" if mx else "experts.hip", "common.h")
+    wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
     if decode:
         # algorithmic bytes per launch: each touched expert's gate+up weights once, the
         # token rows in, the activations out
-        bytes_gu = mean_distinct * 2 * wl.f * wl.d * 2 + T * wl.d * 2 + T * wl.k * wl.f * 2
+        bytes_gu = mean_distinct * 2 * wl.f * wl.d * wbytes + T * wl.d * 2 + T * wl.k * wl.f * 2
         achieved = bytes_gu / (gu_us * 1e-6) / 1e9
         roof = dict(kernel="gate_up", bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4))
-        traffic = read_traffic("gate_up", wl.name, src)
+        traffic = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
         roof["traffic"] = traffic
-        step_bytes = (mean_distinct * 3 * wl.f * wl.d * 2 + wl.E * wl.d * 4
+        step_bytes = (mean_distinct * 3 * wl.f * wl.d * wbytes + wl.E * wl.d * 4
                       + T * wl.d * 2 * 6 + T * wl.k * (wl.f * 4 + wl.d * 4))
         whole = dict(algorithmic_bytes=round(step_bytes), hbm_frac=round(
             step_bytes / (best_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
@@ -265,7 +282,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_sample)
+        cpu = cpu_baseline(wl, args.cpu_sample, mxfp4=mx)
 
     out = {
         "metric": METRIC,
@@ -278,11 +295,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not mx else "bf16 (mxfp4 expert weights)",
         "data": "synthetic (seeded counter-based generator; random-init weights of Beam's MoE layer)",
         "config": {
             "workload": wl.name, "tokens": T, "hidden": wl.d, "experts": wl.E,
             "groups": wl.G, "groups_kept": wl.kg, "topk": wl.k, "d_ff": wl.f,
+            "experts_format": args.experts,
             "token_sets": R, "distinct_experts_per_step": round(mean_distinct, 1),
             "step": args.step, "mode": mode, "ms_eager": round(ms_eager, 5),
             "ms_graph": None if ms_graph is None else round(ms_graph, 5),
@@ -297,10 +315,11 @@ def main():
     moe.close()
 
 
-def cpu_baseline(wl, sample=None):
+def cpu_baseline(wl, sample=None, mxfp4=False):
     """The CPU oracle, as it is, on a bounded sample of the same workload: each
     sampled token goes through boundary, router, routing, its experts and the
-    combine, single-threaded per token; tokens run in a thread pool."""
+    combine, single-threaded per token; tokens run in a thread pool. With mxfp4 the
+    experts' weights are the oracle's MXFP4 quantisation, dequantised (not timed)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -333,6 +352,9 @@ def cpu_baseline(wl, sample=None):
     need = sorted(set(int(e) for r in routes for e in r.ravel()))
     log(f"cpu baseline: drawing {len(need)} experts for {len(hh)} tokens")
     weights = {e: synth.expert_weights(wl, e) for e in need}  # each draw is threaded
+    if mxfp4:
+        weights = {e: tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m)) for m in ws)
+                   for e, ws in weights.items()}
 
     def one(i):
         out = oracle.sublayer(hh[i], xx[i], wpost, wpre, wl.n, wl.eps, Wr, bias, wl.G, wl.kg,
@@ -345,7 +367,8 @@ def cpu_baseline(wl, sample=None):
     dt = time.perf_counter() - t0
     log(f"cpu baseline: {len(hh)} tokens in {dt:.2f}s on {threads} threads")
     return dict(value=round(len(hh) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{len(hh)} tokens of {wl.name}, each through the whole path "
+                sample=f"{len(hh)} tokens of {wl.name}{' (mxfp4 experts)' if mxfp4 else ''}, "
+                       f"each through the whole path "
                        f"(boundary, FP32 router, grouped top-k, {wl.k} SwiGLU experts, combine) "
                        f"single-threaded, {threads} tokens at a time; {dt:.1f} s wall")
 

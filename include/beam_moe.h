@@ -84,6 +84,45 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                   void* stream, beam_moe_handle* out);
 
+/*
+ * beam_mxfp4_quantize — 4-bit block quantisation of BF16 rows (MXFP4).
+ * [vLLM §Modellarchitektur]: the routed experts are served with 4-bit floating-point
+ * weights; [SGLang §BF16、NVFP4 和 FP8 模型支持]: 4-bit expert checkpoints. The format here
+ * is MXFP4 of the OCP Microscaling Formats specification v1.0, which gfx950 converts
+ * natively: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign) sharing one
+ * E8M0 scale 2^(s-127) per 32 consecutive values of a row. Per block:
+ *   X = floor(log2 max|v|) - 2, clamped to [-127, 127] (-127 for an all-zero block);
+ *   code = v / 2^X rounded to the nearest E2M1 value, ties to the even code, |.| > 6
+ *          saturating to 6, sign kept (also when the magnitude rounds to zero).
+ * Arguments: src [rows, K] BF16, K % 32 == 0 (16-byte aligned). Outputs codes_out
+ * [rows, K/2] (element 2i in the low nibble of byte i; 16-byte aligned) and scales_out
+ * [rows, K/32] (the byte X + 127). Stateless; rows == 0 is a no-op. Non-finite inputs
+ * give unspecified codes.
+ */
+int beam_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t* src, uint8_t* codes_out,
+                        uint8_t* scales_out, void* stream);
+
+/*
+ * beam_moe_init_mxfp4 — a handle like beam_moe_init's whose experts hold MXFP4
+ * weights (the layout beam_mxfp4_quantize writes):
+ *   gate_codes, up_codes [E, f, d/2] and gate_scales, up_scales [E, f, d/32];
+ *   down_codes [E, d, f/2] and down_scales [E, d, f/32].
+ * The codes are dequantised exactly (every E2M1 value times a power of two is a BF16
+ * number) inside the expert kernels, with BF16 activations, so the forward computes
+ * what a beam_moe_init handle computes on the dequantised weights, bit for bit, while
+ * reading about 0.53 bytes per weight instead of 2 (the decode path is bound by the
+ * weight stream). Every compute entry point takes either kind of handle.
+ * Supported: the beam_moe_init shapes with hidden % 512 == 0, d_ff % 512 == 0 and
+ * max_tokens <= 128 (the weight-streaming decode range); others give
+ * BEAM_ERR_UNSUPPORTED. Code arrays must be 4-byte aligned. The weights are copied
+ * and repacked into handle-owned memory; the caller may free its copies after return.
+ */
+int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
+                        const float* router_bias, const uint8_t* gate_codes,
+                        const uint8_t* gate_scales, const uint8_t* up_codes,
+                        const uint8_t* up_scales, const uint8_t* down_codes,
+                        const uint8_t* down_scales, void* stream, beam_moe_handle* out);
+
 /* beam_moe_destroy — synchronise and free everything the handle owns. NULL is a no-op. */
 int beam_moe_destroy(beam_moe_handle h);
 

@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     beam_moe_forward,
     beam_moe_forward_boundary,
     beam_moe_init,
+    beam_moe_init_mxfp4,
+    beam_mxfp4_quantize,
     beam_router_topk,
     beam_sublayer_forward,
     beam_sublayer_norm_residual,

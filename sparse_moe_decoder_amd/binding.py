@@ -38,6 +38,9 @@ def lib():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         L.beam_moe_init.argtypes = [ctypes.POINTER(beam_moe_config), vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(vp)]
+        L.beam_moe_init_mxfp4.argtypes = [ctypes.POINTER(beam_moe_config), vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, ctypes.POINTER(vp)]
+        L.beam_mxfp4_quantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
         L.beam_moe_destroy.argtypes = [vp]
         L.beam_sublayer_norm_residual.argtypes = [i32, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]
         L.beam_router_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp]
@@ -55,7 +58,8 @@ def lib():
         L.beam_kernel_count.restype = i32
         L.beam_kernel_name.argtypes = [i32]
         L.beam_kernel_name.restype = ctypes.c_char_p
-        for name in ("beam_moe_init", "beam_moe_destroy", "beam_sublayer_norm_residual",
+        for name in ("beam_moe_init", "beam_moe_init_mxfp4", "beam_mxfp4_quantize",
+                     "beam_moe_destroy", "beam_sublayer_norm_residual",
                      "beam_router_topk", "beam_grouped_topk", "beam_moe_forward",
                      "beam_sublayer_forward", "beam_moe_forward_boundary",
                      "beam_profile_enable", "beam_profile_reset", "beam_profile_read"):
@@ -107,6 +111,43 @@ def beam_moe_init(cfg: dict, router_w, router_bias, w_gate, w_up, w_down, stream
         _ptr(w_gate, torch.bfloat16, (E, f, d), "w_gate"),
         _ptr(w_up, torch.bfloat16, (E, f, d), "w_up"),
         _ptr(w_down, torch.bfloat16, (E, d, f), "w_down"), _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def beam_mxfp4_quantize(src, codes_out=None, scales_out=None, stream=None):
+    """MXFP4 codes [..., K/2] (uint8) and scales [..., K/32] (uint8) of BF16 rows [..., K]."""
+    import torch
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    lead = tuple(src.shape[:-1])
+    if codes_out is None:
+        codes_out = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=src.device)
+    if scales_out is None:
+        scales_out = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=src.device)
+    _check("beam_mxfp4_quantize", lib().beam_mxfp4_quantize(
+        rows, K, _ptr(src, torch.bfloat16, name="src"),
+        _ptr(codes_out, torch.uint8, lead + (K // 2,), "codes_out"),
+        _ptr(scales_out, torch.uint8, lead + (K // 32,), "scales_out"), _stream(stream)))
+    return codes_out, scales_out
+
+
+def beam_moe_init_mxfp4(cfg: dict, router_w, router_bias, gate_codes, gate_scales, up_codes,
+                        up_scales, down_codes, down_scales, stream=None):
+    import torch
+    c = beam_moe_config(cfg["hidden"], cfg["n_experts"], cfg["n_groups"], cfg["topk_groups"],
+                        cfg["topk"], cfg["d_ff"], cfg["max_tokens"], cfg["routed_scale"])
+    E, d, f = cfg["n_experts"], cfg["hidden"], cfg["d_ff"]
+    u8 = torch.uint8
+    h = ctypes.c_void_p()
+    _check("beam_moe_init_mxfp4", lib().beam_moe_init_mxfp4(
+        ctypes.byref(c), _ptr(router_w, torch.float32, (E, d), "router_w"),
+        _ptr(router_bias, torch.float32, (E,), "router_bias"),
+        _ptr(gate_codes, u8, (E, f, d // 2), "gate_codes"),
+        _ptr(gate_scales, u8, (E, f, d // 32), "gate_scales"),
+        _ptr(up_codes, u8, (E, f, d // 2), "up_codes"),
+        _ptr(up_scales, u8, (E, f, d // 32), "up_scales"),
+        _ptr(down_codes, u8, (E, d, f // 2), "down_codes"),
+        _ptr(down_scales, u8, (E, d, f // 32), "down_scales"), _stream(stream), ctypes.byref(h)))
     return h
 
 
@@ -227,9 +268,17 @@ def profile_read():
 class BeamMoE:
     """One MoE layer handle with torch-allocated outputs."""
 
-    def __init__(self, cfg: dict, router_w, router_bias, w_gate, w_up, w_down, stream=None):
+    def __init__(self, cfg: dict, router_w, router_bias, w_gate, w_up, w_down, stream=None,
+                 mxfp4=None):
+        """BF16 experts from (w_gate, w_up, w_down); or, with mxfp4 = (gate_codes,
+        gate_scales, up_codes, up_scales, down_codes, down_scales) and the three BF16
+        weights None, 4-bit experts (see beam_moe_init_mxfp4)."""
         self.cfg = dict(cfg)
-        self.handle = beam_moe_init(cfg, router_w, router_bias, w_gate, w_up, w_down, stream)
+        self.handle = None
+        if mxfp4 is not None:
+            self.handle = beam_moe_init_mxfp4(cfg, router_w, router_bias, *mxfp4, stream=stream)
+        else:
+            self.handle = beam_moe_init(cfg, router_w, router_bias, w_gate, w_up, w_down, stream)
 
     def close(self):
         if self.handle is not None and self.handle.value:

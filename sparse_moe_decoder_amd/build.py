@@ -6,7 +6,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbeam_moe.so")
-SOURCES = ["api.hip", "boundary.hip", "router.hip", "permute.hip", "experts.hip"]
+SOURCES = ["api.hip", "boundary.hip", "router.hip", "permute.hip", "experts.hip",
+           "experts_mxfp4.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed-FP32 instructions in device code

@@ -98,8 +98,13 @@ struct beam_moe_ctx {
   float* router_w = nullptr;  // [E, d]
   uint16_t* router_x3 = nullptr;  // [3][E/16][d/32][64][8]: W = hi + mid + lo, BF16 parts
   float* bias = nullptr;      // [E]
-  uint16_t* wgu = nullptr;    // packed gate/up
-  uint16_t* wdp = nullptr;    // packed down
+  uint16_t* wgu = nullptr;    // packed gate/up (BF16 experts)
+  uint16_t* wdp = nullptr;    // packed down (BF16 experts)
+  bool mxfp4 = false;         // 4-bit experts: the four arrays below instead of wgu, wdp
+  uint8_t* qgu = nullptr;     // gate/up codes, decode layout
+  uint8_t* sgu = nullptr;     // gate/up scales
+  uint8_t* qd = nullptr;      // down codes
+  uint8_t* sd = nullptr;      // down scales
   // workspace (owned), sized for max_tokens
   float* logits = nullptr;     // [maxT, E]
   int32_t* ids = nullptr;      // [maxT, k]
@@ -251,8 +256,16 @@ int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, con
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk};
-  if (T <= kStreamMaxT) {
+                h->n_active, h->tile_start, w, h->act, h->yk, h->qgu, h->sgu, h->qd, h->sd};
+  if (h->mxfp4) {  // max_tokens <= kStreamMaxT: the weight-streaming passes only
+    const int max_active = slots < E ? slots : E;
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_fp4(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    ProfScope ps(K_DOWN, s);
+    if (launch_down_fp4(ea, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+  } else if (T <= kStreamMaxT) {
     const int max_active = slots < E ? slots : E;
     {
       ProfScope ps(K_GATEUP, s);
@@ -302,15 +315,15 @@ const char* beam_status_string(int status) {
   }
 }
 
-int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float* router_bias,
-                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                  void* stream, beam_moe_handle* out) {
-  int st = validate_config(cfg);
-  if (st != BEAM_OK) return st;
-  if (!out || !router_w || !router_bias || !w_gate || !w_up || !w_down) return BEAM_ERR_INVALID_ARG;
-  if (!aligned16(router_w) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      ((uintptr_t)router_bias & 3u))
-    return BEAM_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Shared part of the two init entry points: the handle, the router copies and all
+// workspace; `experts` allocates and fills the expert weights on stream s.
+template <class Experts>
+int init_handle(const beam_moe_config* cfg, const float* router_w, const float* router_bias,
+                void* stream, beam_moe_handle* out, Experts experts) {
   beam_moe_ctx* h = new (std::nothrow) beam_moe_ctx();
   if (!h) return BEAM_ERR_OOM;
   h->cfg = *cfg;
@@ -325,7 +338,6 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
   const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
   bool ok = dev_alloc(h, &h->router_w, E * d) && dev_alloc(h, &h->router_x3, 3 * E * d) &&
             dev_alloc(h, &h->bias, E) &&
-            dev_alloc(h, &h->wgu, E * 2 * f * d) && dev_alloc(h, &h->wdp, E * d * f) &&
             dev_alloc(h, &h->logits, T * E) && dev_alloc(h, &h->ids, slots) &&
             dev_alloc(h, &h->w, slots) && dev_alloc(h, &h->counts, E) &&
             dev_alloc(h, &h->offsets, E + 1) && dev_alloc(h, &h->active, E) &&
@@ -335,18 +347,22 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
             dev_alloc(h, &h->block_cnt, nb * E) &&
             dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
             dev_alloc(h, &h->yk, slots * d);
+  hipError_t e = hipSuccess;
+  if (ok) {
+    const int st = experts(h, s);
+    if (st == BEAM_ERR_OOM) ok = false;
+    else if (st != BEAM_OK) e = hipErrorUnknown;
+  }
   if (!ok) {
     free_all(h);
     delete h;
     return BEAM_ERR_OOM;
   }
-  hipError_t e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float),
-                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(h->route_done, 0, sizeof(uint32_t), s);
-  if (e == hipSuccess)
-    e = launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, (int)E, (int)f, (int)d, s);
   if (e == hipSuccess && E % 64 == 0)
     e = launch_repack_router(router_w, h->router_x3, (int)E, (int)d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -358,6 +374,65 @@ int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float
   }
   *out = h;
   return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_moe_init(const beam_moe_config* cfg, const float* router_w, const float* router_bias,
+                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                  void* stream, beam_moe_handle* out) {
+  int st = validate_config(cfg);
+  if (st != BEAM_OK) return st;
+  if (!out || !router_w || !router_bias || !w_gate || !w_up || !w_down) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(router_w) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      ((uintptr_t)router_bias & 3u))
+    return BEAM_ERR_INVALID_ARG;
+  return init_handle(cfg, router_w, router_bias, stream, out, [&](beam_moe_ctx* h, hipStream_t s) -> int {
+    const size_t E = cfg->n_experts, d = cfg->hidden, f = cfg->d_ff;
+    if (!dev_alloc(h, &h->wgu, E * 2 * f * d) || !dev_alloc(h, &h->wdp, E * d * f))
+      return BEAM_ERR_OOM;
+    return hip_status(launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, (int)E, (int)f, (int)d, s));
+  });
+}
+
+int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
+                        const float* router_bias, const uint8_t* gate_codes,
+                        const uint8_t* gate_scales, const uint8_t* up_codes,
+                        const uint8_t* up_scales, const uint8_t* down_codes,
+                        const uint8_t* down_scales, void* stream, beam_moe_handle* out) {
+  int st = validate_config(cfg);
+  if (st != BEAM_OK) return st;
+  if (cfg->max_tokens > kStreamMaxT || cfg->hidden % 512 != 0 || cfg->d_ff % 512 != 0)
+    return BEAM_ERR_UNSUPPORTED;
+  if (!out || !router_w || !router_bias || !gate_codes || !gate_scales || !up_codes ||
+      !up_scales || !down_codes || !down_scales)
+    return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(router_w) || ((uintptr_t)router_bias & 3u) || ((uintptr_t)gate_codes & 3u) ||
+      ((uintptr_t)up_codes & 3u) || ((uintptr_t)down_codes & 3u))
+    return BEAM_ERR_INVALID_ARG;
+  return init_handle(cfg, router_w, router_bias, stream, out, [&](beam_moe_ctx* h, hipStream_t s) -> int {
+    const size_t E = cfg->n_experts, d = cfg->hidden, f = cfg->d_ff;
+    h->mxfp4 = true;
+    if (!dev_alloc(h, &h->qgu, E * 2 * f * d / 2) || !dev_alloc(h, &h->sgu, E * 2 * f * d / 32) ||
+        !dev_alloc(h, &h->qd, E * d * f / 2) || !dev_alloc(h, &h->sd, E * d * f / 32))
+      return BEAM_ERR_OOM;
+    return hip_status(launch_repack_mxfp4(gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                                          down_scales, (int)E, (int)f, (int)d, h->qgu, h->sgu,
+                                          h->qd, h->sd, s));
+  });
+}
+
+int beam_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t* src, uint8_t* codes_out,
+                        uint8_t* scales_out, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return BEAM_ERR_INVALID_ARG;
+  if (rows > ((int64_t)1 << 40) / K) return BEAM_ERR_UNSUPPORTED;
+  if (rows == 0) return BEAM_OK;
+  if (!src || !codes_out || !scales_out || !aligned16(src) || !aligned16(codes_out))
+    return BEAM_ERR_INVALID_ARG;
+  return hip_status(launch_mxfp4_quantize(rows * (K / 32), src, codes_out, scales_out,
+                                          (hipStream_t)stream));
 }
 
 int beam_moe_destroy(beam_moe_handle h) {

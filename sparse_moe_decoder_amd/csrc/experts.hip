@@ -22,6 +22,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "combine_device.h"
+#include "expert_device.h"
 
 #include <type_traits>
 
@@ -94,17 +95,6 @@ hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t*
 // flight. Rows of the expert (at most 16*MT per pass) ride along as the MFMA
 // A operand, so every weight byte is read once per pass however many rows the
 // expert has. Partial sums from the four waves are added in wave order.
-
-__device__ __forceinline__ int expert_of_block(const ExpertArgs& a, int slot, int& row0,
-                                               int& cnt) {
-  // slot < E, so active[slot] is in bounds: both loads are issued before either is used
-  const int na = *a.n_active, e = a.active[slot];
-  asm volatile("" ::"s"(na), "s"(e));
-  if (slot >= na) return -1;
-  row0 = a.offsets[e];
-  cnt = a.offsets[e + 1] - row0;
-  return e;
-}
 
 template <int MT, int U>
 __global__ __launch_bounds__(256) void gateup_stream_kernel(ExpertArgs a) {

@@ -1,0 +1,461 @@
+// Routed SwiGLU experts with 4-bit (MXFP4) weights: quantisation, the decode-layout
+// repack, and the weight-streaming gate/up and down kernels.
+//
+// [vLLM "Serving Reflection Beam auf vLLM ab Tag 0", §Modellarchitektur] the routed
+//   experts are served with 4-bit floating-point weights (NVFP4 on the pages'
+//   hardware). [SGLang "SGLang 支撑编程模型 Beam 生产部署", §BF16、NVFP4 和 FP8 模型支持]
+//   BF16, NVFP4 and FP8 checkpoints.
+// The 4-bit format here is MXFP4 (OCP Microscaling Formats specification v1.0):
+// E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign), one E8M0 scale
+// 2^(s - 127) per 32 consecutive values along K, element 2i in the low nibble of
+// byte i. gfx950 converts a code pair and a scale to two BF16 values in one
+// instruction (v_cvt_scalef32_pk_bf16_fp4); every E2M1 value times a power of two
+// is a BF16 number, so the dequantised weights are exact and the kernels below run
+// the BF16 decode kernels' arithmetic (same K split, same MFMA order) on them.
+//
+// Decode layout (repacked at init). A "k-quad" is 128 consecutive K values = four
+// 32-wide MFMA k-steps; lane l of a 16-row output tile holds row l % 16 and, for
+// each k-step s of the quad, K values 32 s + 8 (l / 16) .. +7 as one dword (8
+// codes), so one 16-byte load per lane brings four B fragments:
+//   gate/up codes:  [E][f/16][d/128][gate|up][64 lanes][16 B]
+//   gate/up scales: [E][f/16][d/128][gate|up][16 rows][4 k-steps]   (1 B each)
+//   down codes:     [E][d/16][f/128][64 lanes][16 B]
+//   down scales:    [E][d/16][f/128][16 rows][4 k-steps]
+// A lane's four scales of one quad are one dword at row * 4.
+#include "common.h"
+#include "kernels.h"
+#include "expert_device.h"
+
+namespace beam {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 2^(s - 127) as an FP32 multiplier (s = 0 is 2^-127, a subnormal; s = 255, the
+// E8M0 NaN, is never produced by the quantiser)
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Eight codes (one dword) times the scale: the BF16 operand fragment, element i in
+// half-word i
+__device__ __forceinline__ u32x4 fp4x8_bf16(uint32_t codes, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t ld_stream_u32(const void* p) {
+  return __builtin_nontemporal_load((const uint32_t*)p);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Quantisation: one thread per block of 32 values of a row.
+//   X = floor(log2 max|v|) - 2, clamped to [-127, 127]: for a BF16 maximum with
+//   exponent field ex (0 for zero and subnormals), X = max(ex - 129, -127), so the
+//   stored scale is max(ex - 2, 0).
+//   q = |v| * 2^-X (exact: a power-of-two scaling, q < 8) is rounded to the nearest
+//   E2M1 magnitude with ties to the even code and saturation at 6: the code counts
+//   the decision points q passes, strictly past a point where the lower neighbour
+//   has the even code (0.25, 1.25, 2.5, 5) and from the point on where the upper one
+//   has it (0.75, 1.75, 3.5). The sign bit is the input's.
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(int64_t nblocks, const uint16_t* __restrict__ src,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld_u32x4(src + b * 32 + i * 8);
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = v[i][j];
+        amax = max_u32(amax, max_u32(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+      }
+    const int ex = (int)(amax >> 7);                      // BF16 exponent field (< 255: finite)
+    const int sbyte = ex > 2 ? ex - 2 : 0;                // X + 127
+    const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-X
+    u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t bits = hh ? (v[i][j] >> 16) : (v[i][j] & 0xFFFFu);
+          const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+          const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
+                             (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
+          const uint32_t code = m | ((bits >> 12) & 8u);
+          const int e = i * 8 + j * 2 + hh;  // element of the block
+          out[e >> 3] |= code << (4 * (e & 7));
+        }
+    st_u32x4(codes + b * 16, out);
+    scales[b] = (uint8_t)sbyte;
+  }
+}
+
+hipError_t launch_mxfp4_quantize(int64_t nblocks, const uint16_t* src, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s) {
+  int64_t g = (nblocks + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3((unsigned)g), dim3(256), 0, s, nblocks, src,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Repack (init only): row-major codes [E][N][K/2] and scales [E][N][K/32] of NMAT
+// matrices (gate, up: NMAT = 2, interleaved per quad; down: NMAT = 1) into the
+// decode layout above.
+__global__ void repack_mxfp4_kernel(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
+                                    const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
+                                    int nmat, int E, int N, int K, uint8_t* __restrict__ qout,
+                                    uint8_t* __restrict__ sout) {
+  const int64_t NT = N / 16, KQ = K / 128;
+  const int64_t total = (int64_t)E * NT * KQ * nmat * 64;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = q % 64;
+    int64_t r = q / 64;
+    const int64_t m = r % nmat;
+    r /= nmat;
+    const int64_t kq = r % KQ;
+    r /= KQ;
+    const int64_t t = r % NT;
+    const int64_t e = r / NT;
+    const int64_t row = t * 16 + (lane & 15);
+    const uint8_t* cs = (m ? c1 : c0) + (e * N + row) * (K / 2);
+    const uint8_t* ss = (m ? s1 : s0) + (e * N + row) * (K / 32);
+    u32x4 o;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)  // k-step s: K values 128 kq + 32 s + 8 (lane / 16) .. +7
+      o[s] = *(const uint32_t*)(cs + (128 * kq + 32 * s + 8 * (lane >> 4)) / 2);
+    st_u32x4(qout + q * 16, o);
+    if (lane < 16) {
+      uint32_t sc = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sc |= (uint32_t)ss[4 * kq + s] << (8 * s);
+      const int64_t quad = q / 64;  // (e, t, kq, m)
+      *(uint32_t*)(sout + quad * 64 + lane * 4) = sc;
+    }
+  }
+}
+
+hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                               const uint8_t* us, const uint8_t* dq, const uint8_t* ds, int E,
+                               int f, int d, uint8_t* qgu, uint8_t* sgu, uint8_t* qd, uint8_t* sd,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(repack_mxfp4_kernel, dim3(16384), dim3(256), 0, s, gq, gs, uq, us, 2, E, f, d,
+                     qgu, sgu);
+  hipLaunchKernelGGL(repack_mxfp4_kernel, dim3(16384), dim3(256), 0, s, dq, ds, dq, ds, 1, E, d, f,
+                     qd, sd);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gate/up: one workgroup per (active expert, 16 outputs); the four waves split K
+// into quarters (d/512 quads each) in wave order, each with a ring of U quads of
+// code and scale loads in flight (slot u consumed, then refilled U quads ahead);
+// the expert's rows (at most 16 MT per pass) ride along as the MFMA A operand
+// through a buffer resource (rows past the count read zeros with no traffic). Per
+// k-step: dequantise the gate and up fragments, then the MFMAs, in the BF16
+// kernel's order, so the result equals the BF16 kernel's on the dequantised weights.
+template <int MT, int U>
+__global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
+  const int NJ = a.f / 16;
+  const int j = blockIdx.x % NJ;
+  int row0, cnt;
+  const int e = expert_of_block(a, blockIdx.x / NJ, row0, cnt);
+  if (e < 0) return;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KQ = a.d / 128, kqw = KQ / 4, kq0 = wv * kqw;
+  const int64_t quad0 = ((int64_t)e * NJ + j) * KQ + kq0;  // (expert, tile, quad) of this wave
+  const uint8_t* cp = a.qgu + quad0 * 2 * 1024 + lane * 16;
+  const uint8_t* sp = a.sgu + quad0 * 2 * 64 + (lane & 15) * 4;
+  const uint32_t zbytes = (uint32_t)a.T * a.d * 2;
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, zbytes);
+  __shared__ f32x4 red[3][2 * MT][64];
+  for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+    f32x4 ag[MT], au[MT];
+    int pv[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      au[mt] = ag[mt];
+      const int r = m0 + mt * 16 + (lane & 15);
+      pv[mt] = a.perm[row0 + (r < cnt ? r : cnt - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t xo[MT];
+    u32x4 cg[U], cu[U], x[MT][U][4];
+    uint32_t sg[U], su[U];
+    auto load_w = [&](int u, int kq) {
+      cg[u] = ld_stream_u32x4(cp + (int64_t)kq * 2048);
+      cu[u] = ld_stream_u32x4(cp + (int64_t)kq * 2048 + 1024);
+      sg[u] = ld_stream_u32(sp + (int64_t)kq * 128);
+      su[u] = ld_stream_u32(sp + (int64_t)kq * 128 + 64);
+    };
+    auto load_x = [&](int u, int kq) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x[mt][u][s] = ld_buf_u32x4(zr, xo[mt] + (kq * 4 + s) * 64);
+    };
+    auto use = [&](int u) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 bg = fp4x8_bf16(cg[u][s], e8m0_scale((sg[u] >> (8 * s)) & 255u));
+        const u32x4 bu = fp4x8_bf16(cu[u][s], e8m0_scale((su[u] >> (8 * s)) & 255u));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          ag[mt] = mfma16(x[mt][u][s], bg, ag[mt]);
+          au[mt] = mfma16(x[mt][u][s], bu, au[mt]);
+        }
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_w(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = m0 + mt * 16 + (lane & 15);
+      xo[mt] = r < cnt ? 2u * (uint32_t)((pv[mt] / a.k) * a.d + kq0 * 128 + 8 * (lane >> 4)) : zbytes;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load_x(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int kq = 0; kq < kqw - U; kq += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        use(u);
+        load_w(u, kq + U + u);
+        load_x(u, kq + U + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) use(u);
+    if (wv > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        red[wv - 1][2 * mt][lane] = ag[mt];
+        red[wv - 1][2 * mt + 1][lane] = au[mt];
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 g = ag[mt], u = au[mt];
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+          g += red[w][2 * mt][lane];
+          u += red[w][2 * mt + 1][lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+          if (r < cnt) {
+            const float gv = bf2f(f2bf(g[i])), uv = bf2f(f2bf(u[i]));
+            a.act[(int64_t)(row0 + r) * a.f + j * 16 + (lane & 15)] = f2bf(silu(gv) * uv);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Down for batches up to 16 tokens: one workgroup per (active expert, 16 output
+// columns), the four waves split K (f) into quarters with a ring of U quads each;
+// the quarters are added in wave order and bf16(w * sum) goes to the row's slot
+// (the BF16 split kernel's order).
+template <int U>
+__global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
+  const int ND = a.d / 16;
+  const int nt = blockIdx.x % ND;
+  int row0, cnt;
+  const int e = expert_of_block(a, blockIdx.x / ND, row0, cnt);
+  if (e < 0) return;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KQ = a.f / 128, kqw = KQ / 4, kq0 = wv * kqw;
+  const int64_t quad0 = ((int64_t)e * ND + nt) * KQ + kq0;
+  const uint8_t* cp = a.qd + quad0 * 1024 + lane * 16;
+  const uint8_t* sp = a.sd + quad0 * 64 + (lane & 15) * 4;
+  const uint32_t abytes = (uint32_t)a.T * a.k * a.f * 2;
+  __shared__ f32x4 red[3][64];
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int r = m0 + (lane & 15);
+    const uint32_t xo = r < cnt ? 2u * (uint32_t)((row0 + r) * a.f + kq0 * 128 + 8 * (lane >> 4)) : abytes;
+    u32x4 c[U], x[U][4];
+    uint32_t sc[U];
+    auto load = [&](int u, int kq) {
+      c[u] = ld_stream_u32x4(cp + (int64_t)kq * 1024);
+      sc[u] = ld_stream_u32(sp + (int64_t)kq * 64);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        x[u][s] = xo < abytes ? ld_u32x4((const char*)a.act + xo + (kq * 4 + s) * 64)
+                              : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto use = [&](int u) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = mfma16(x[u][s], fp4x8_bf16(c[u][s], e8m0_scale((sc[u] >> (8 * s)) & 255u)), acc);
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int kq = 0; kq < kqw - U; kq += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        use(u);
+        load(u, kq + U + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) use(u);
+    if (wv > 0) red[wv - 1][lane] = acc;
+    __syncthreads();
+    if (wv == 0) {
+      f32x4 v = acc;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) v += red[w][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = m0 + 4 * (lane >> 4) + i;
+        if (rr < cnt) {
+          const int slot = a.perm[row0 + rr];
+          a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * v[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Down for 17..128 tokens: a workgroup covers 4 output tiles of 16 columns of one
+// expert, one wave per tile accumulating the full K in order, U quads per batch
+// (the BF16 streaming kernel's order).
+template <int MT, int U>
+__global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
+  const int ND = a.d / 16, NB = ND / 4;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nt = (blockIdx.x % NB) * 4 + wv;
+  int row0, cnt;
+  const int e = expert_of_block(a, blockIdx.x / NB, row0, cnt);
+  if (e < 0) return;
+  const int KQ = a.f / 128;
+  const int64_t quad0 = ((int64_t)e * ND + nt) * KQ;
+  const uint8_t* cp = a.qd + quad0 * 1024 + lane * 16;
+  const uint8_t* sp = a.sd + quad0 * 64 + (lane & 15) * 4;
+  for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+    f32x4 acc[MT];
+    const uint16_t* ap[MT];
+    bool av[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = m0 + mt * 16 + (lane & 15);
+      av[mt] = r < cnt;
+      ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + 8 * (lane >> 4);
+    }
+    for (int kq = 0; kq < KQ; kq += U) {
+      u32x4 c[U], x[MT][U][4];
+      uint32_t sc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        c[u] = ld_stream_u32x4(cp + (int64_t)(kq + u) * 1024);
+        sc[u] = ld_stream_u32(sp + (int64_t)(kq + u) * 64);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            x[mt][u][s] = av[mt] ? ld_u32x4(ap[mt] + ((kq + u) * 4 + s) * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 b = fp4x8_bf16(c[u][s], e8m0_scale((sc[u] >> (8 * s)) & 255u));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u][s], b, acc[mt]);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+        if (r < cnt) {
+          const int slot = a.perm[row0 + r];
+          a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * acc[mt][i]);
+        }
+      }
+  }
+}
+
+// Launches: the grids are sized for the largest possible number of active experts;
+// workgroups past the active count exit at once. Needs d % 512 == 0 and f % 512 == 0
+// (whole quads per wave quarter).
+hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
+  const int kqw = a.d / 128 / 4;
+  dim3 g((unsigned)(max_active * (a.f / 16))), blk(256);
+  if (a.T <= 16) {
+    if (kqw % 5 == 0)
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 5>), g, blk, 0, s, a);
+    else if (kqw % 4 == 0)
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 4>), g, blk, 0, s, a);
+    else if (kqw % 2 == 0)
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 1>), g, blk, 0, s, a);
+  } else {
+    if (kqw % 2 == 0)
+      hipLaunchKernelGGL((gateup_fp4_kernel<2, 2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((gateup_fp4_kernel<2, 1>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
+  if (a.T <= kSplitDownMaxT) {
+    const int kqw = a.f / 128 / 4;
+    dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
+    if (kqw % 5 == 0)
+      hipLaunchKernelGGL((down_split_fp4_kernel<5>), g, blk, 0, s, a);
+    else if (kqw % 4 == 0)
+      hipLaunchKernelGGL((down_split_fp4_kernel<4>), g, blk, 0, s, a);
+    else if (kqw % 2 == 0)
+      hipLaunchKernelGGL((down_split_fp4_kernel<2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((down_split_fp4_kernel<1>), g, blk, 0, s, a);
+  } else {
+    const int KQ = a.f / 128;
+    dim3 g((unsigned)(max_active * (a.d / 64))), blk(256);
+    if (KQ % 2 == 0)
+      hipLaunchKernelGGL((down_stream_fp4_kernel<2, 2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((down_stream_fp4_kernel<2, 1>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace beam

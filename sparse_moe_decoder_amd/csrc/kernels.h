@@ -90,9 +90,25 @@ struct ExpertArgs {
   const float* w;             // [T*k] routing weight by slot
   uint16_t* act;              // [T*k, f] by row (expert-grouped order)
   uint16_t* yk;               // [T*k, d] by slot t*k+j
+  // MXFP4 experts (decode layout of experts_mxfp4.hip); null for BF16 experts
+  const uint8_t* qgu = nullptr;  // gate/up codes
+  const uint8_t* sgu = nullptr;  // gate/up scales
+  const uint8_t* qd = nullptr;   // down codes
+  const uint8_t* sd = nullptr;   // down scales
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
+// MXFP4 experts: block quantisation of BF16 rows (nblocks blocks of 32 values), the
+// init-time repack of row-major codes/scales into the decode layout, and the
+// weight-streaming expert passes (T <= kStreamMaxT; d, f multiples of 512)
+hipError_t launch_mxfp4_quantize(int64_t nblocks, const uint16_t* src, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                               const uint8_t* us, const uint8_t* dq, const uint8_t* ds, int E,
+                               int f, int d, uint8_t* qgu, uint8_t* sgu, uint8_t* qd, uint8_t* sd,
+                               hipStream_t s);
+hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
+hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
 // the boundary with x = the combine of c (b.x unused); b.d <= kBoundaryWgMaxD
 hipError_t launch_combine_boundary(const BoundaryArgs& b, const CombineArgs& c, hipStream_t s);
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);

@@ -118,3 +118,40 @@ def test_product_path_has_no_oracle_or_fallback():
                 src = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert "import oracle" not in src and "from oracle" not in src, fn
                 assert "beam_oracle" not in src and "liboracle" not in src, fn
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_tokens=129), -2),        # beyond the weight-streaming decode range
+    (dict(hidden=768), -2),            # hidden % 512 != 0
+    (dict(d_ff=2816), -2),             # d_ff % 512 != 0
+    (dict(n_groups=7), -1),            # the shared checks still come first
+])
+def test_init_mxfp4_rejects_bad_config(L, kw, status):
+    h = ctypes.c_void_p()
+    p = ctypes.c_void_p(0x1000)
+    st = L.beam_moe_init_mxfp4(ctypes.byref(_cfg(**kw)), p, p, p, p, p, p, p, p, None,
+                               ctypes.byref(h))
+    assert st == status
+    assert not h.value
+
+
+def test_init_mxfp4_rejects_null_and_misaligned(L):
+    h = ctypes.c_void_p()
+    p = ctypes.c_void_p(0x1000)
+    f = L.beam_moe_init_mxfp4
+    assert f(ctypes.byref(_cfg()), p, p, None, p, p, p, p, p, None, ctypes.byref(h)) == -1
+    assert f(ctypes.byref(_cfg()), p, p, p, p, p, p, p, None, None, ctypes.byref(h)) == -1
+    assert f(ctypes.byref(_cfg()), p, p, ctypes.c_void_p(0x1002), p, p, p, p, p, None,
+             ctypes.byref(h)) == -1
+    assert not h.value
+
+
+def test_mxfp4_quantize_validation(L):
+    p = ctypes.c_void_p(0x1000)
+    f = L.beam_mxfp4_quantize
+    assert f(4, 48, p, p, p, None) == -1          # K % 32 != 0
+    assert f(-1, 64, p, p, p, None) == -1         # negative rows
+    assert f(4, 0, p, p, p, None) == -1
+    assert f(4, 64, None, p, p, None) == -1       # null
+    assert f(4, 64, ctypes.c_void_p(0x1008), p, p, None) == -1  # misaligned source
+    assert f(0, 64, None, None, None, None) == 0  # rows = 0: no-op
