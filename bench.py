@@ -328,7 +328,7 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
     import synth
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    n = sample or (2 * threads)
+    n = sample or (threads if mxfp4 else 2 * threads)
     rows = list(range(min(n, wl.T))) if wl.T >= n else list(range(wl.T))
     if len(rows) < n:  # decode: also take tokens of the rotation sets
         extra = n - len(rows)
@@ -353,8 +353,13 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
     log(f"cpu baseline: drawing {len(need)} experts for {len(hh)} tokens")
     weights = {e: synth.expert_weights(wl, e) for e in need}  # each draw is threaded
     if mxfp4:
-        weights = {e: tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m)) for m in ws)
-                   for e, ws in weights.items()}
+        def quant(e):
+            return e, tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m)) for m in weights[e])
+        with ThreadPoolExecutor(threads) as ex:
+            for i, (e, ws) in enumerate(ex.map(quant, need)):
+                weights[e] = ws
+                if i % 16 == 15 or i + 1 == len(need):
+                    log(f"cpu baseline: quantised {i + 1} of {len(need)} experts")
 
     def one(i):
         out = oracle.sublayer(hh[i], xx[i], wpost, wpre, wl.n, wl.eps, Wr, bias, wl.G, wl.kg,

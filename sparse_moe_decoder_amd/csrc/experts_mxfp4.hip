@@ -160,47 +160,57 @@ hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8
 }
 
 // ---------------------------------------------------------------------------------------------
-// Gate/up: one workgroup per (active expert, 16 outputs); the four waves split K
-// into quarters (d/512 quads each) in wave order, each with a ring of U quads of
-// code and scale loads in flight (slot u consumed, then refilled U quads ahead);
-// the expert's rows (at most 16 MT per pass) ride along as the MFMA A operand
-// through a buffer resource (rows past the count read zeros with no traffic). Per
-// k-step: dequantise the gate and up fragments, then the MFMAs, in the BF16
-// kernel's order, so the result equals the BF16 kernel's on the dequantised weights.
-template <int MT, int U>
+// Gate/up: one workgroup per (active expert, NTW tiles of 16 outputs); the four
+// waves split K into quarters (d/512 quads each) in wave order, each with a ring of
+// U quads of code and scale loads in flight (slot u consumed, then refilled U quads
+// ahead) for its NTW tiles, which share one activation fragment per k-step; the
+// expert's rows (at most 16 MT per pass) ride along as the MFMA A operand through a
+// buffer resource (rows past the count read zeros with no traffic). Per k-step:
+// dequantise the gate and up fragments, then the MFMAs. Each output accumulates its
+// k-steps in the BF16 kernel's order and the quarters are added in wave order, so
+// the result equals the BF16 kernel's on the dequantised weights.
+template <int MT, int U, int NTW>
 __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
-  const int NJ = a.f / 16;
-  const int j = blockIdx.x % NJ;
+  const int NJ = a.f / 16, NB = NJ / NTW;
+  const int j0 = (blockIdx.x % NB) * NTW;
   int row0, cnt;
-  const int e = expert_of_block(a, blockIdx.x / NJ, row0, cnt);
+  const int e = expert_of_block(a, blockIdx.x / NB, row0, cnt);
   if (e < 0) return;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KQ = a.d / 128, kqw = KQ / 4, kq0 = wv * kqw;
-  const int64_t quad0 = ((int64_t)e * NJ + j) * KQ + kq0;  // (expert, tile, quad) of this wave
+  const int64_t quad0 = ((int64_t)e * NJ + j0) * KQ + kq0;  // (expert, tile, quad) of this wave
+  const int64_t tstride = (int64_t)KQ * 2;                 // quads of one tile (gate and up)
   const uint8_t* cp = a.qgu + quad0 * 2 * 1024 + lane * 16;
   const uint8_t* sp = a.sgu + quad0 * 2 * 64 + (lane & 15) * 4;
   const uint32_t zbytes = (uint32_t)a.T * a.d * 2;
   const __amdgpu_buffer_rsrc_t zr = make_rsrc(a.z, zbytes);
-  __shared__ f32x4 red[3][2 * MT][64];
+  __shared__ f32x4 red[3][2 * MT * NTW][64];
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
-    f32x4 ag[MT], au[MT];
+    f32x4 ag[NTW][MT], au[NTW][MT];
     int pv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      ag[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[mt] = ag[mt];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        ag[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        au[t][mt] = ag[t][mt];
+      }
       const int r = m0 + mt * 16 + (lane & 15);
       pv[mt] = a.perm[row0 + (r < cnt ? r : cnt - 1)];
     }
     __builtin_amdgcn_sched_barrier(0);
     uint32_t xo[MT];
-    u32x4 cg[U], cu[U], x[MT][U][4];
-    uint32_t sg[U], su[U];
+    u32x4 cg[U][NTW], cu[U][NTW], x[MT][U][4];
+    uint32_t sg[U][NTW], su[U][NTW];
     auto load_w = [&](int u, int kq) {
-      cg[u] = ld_stream_u32x4(cp + (int64_t)kq * 2048);
-      cu[u] = ld_stream_u32x4(cp + (int64_t)kq * 2048 + 1024);
-      sg[u] = ld_stream_u32(sp + (int64_t)kq * 128);
-      su[u] = ld_stream_u32(sp + (int64_t)kq * 128 + 64);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int64_t q = t * tstride + kq * 2;
+        cg[u][t] = ld_stream_u32x4(cp + q * 1024);
+        cu[u][t] = ld_stream_u32x4(cp + q * 1024 + 1024);
+        sg[u][t] = ld_stream_u32(sp + q * 64);
+        su[u][t] = ld_stream_u32(sp + q * 64 + 64);
+      }
     };
     auto load_x = [&](int u, int kq) {
 #pragma unroll
@@ -210,15 +220,17 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
     };
     auto use = [&](int u) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 bg = fp4x8_bf16(cg[u][s], e8m0_scale((sg[u] >> (8 * s)) & 255u));
-        const u32x4 bu = fp4x8_bf16(cu[u][s], e8m0_scale((su[u] >> (8 * s)) & 255u));
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          ag[mt] = mfma16(x[mt][u][s], bg, ag[mt]);
-          au[mt] = mfma16(x[mt][u][s], bu, au[mt]);
+        for (int t = 0; t < NTW; ++t) {
+          const u32x4 bg = fp4x8_bf16(cg[u][t][s], e8m0_scale((sg[u][t] >> (8 * s)) & 255u));
+          const u32x4 bu = fp4x8_bf16(cu[u][t][s], e8m0_scale((su[u][t] >> (8 * s)) & 255u));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            ag[t][mt] = mfma16(x[mt][u][s], bg, ag[t][mt]);
+            au[t][mt] = mfma16(x[mt][u][s], bu, au[t][mt]);
+          }
         }
-      }
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -248,62 +260,71 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
     for (int u = 0; u < U; ++u) use(u);
     if (wv > 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        red[wv - 1][2 * mt][lane] = ag[mt];
-        red[wv - 1][2 * mt + 1][lane] = au[mt];
-      }
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          red[wv - 1][(t * MT + mt) * 2][lane] = ag[t][mt];
+          red[wv - 1][(t * MT + mt) * 2 + 1][lane] = au[t][mt];
+        }
     }
     __syncthreads();
     if (wv == 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 g = ag[mt], u = au[mt];
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
-          g += red[w][2 * mt][lane];
-          u += red[w][2 * mt + 1][lane];
-        }
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 g = ag[t][mt], u = au[t][mt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
-          if (r < cnt) {
-            const float gv = bf2f(f2bf(g[i])), uv = bf2f(f2bf(u[i]));
-            a.act[(int64_t)(row0 + r) * a.f + j * 16 + (lane & 15)] = f2bf(silu(gv) * uv);
+          for (int w = 0; w < 3; ++w) {
+            g += red[w][(t * MT + mt) * 2][lane];
+            u += red[w][(t * MT + mt) * 2 + 1][lane];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+            if (r < cnt) {
+              const float gv = bf2f(f2bf(g[i])), uv = bf2f(f2bf(u[i]));
+              a.act[(int64_t)(row0 + r) * a.f + (j0 + t) * 16 + (lane & 15)] = f2bf(silu(gv) * uv);
+            }
           }
         }
-      }
     }
     __syncthreads();
   }
 }
 
-// Down for batches up to 16 tokens: one workgroup per (active expert, 16 output
-// columns), the four waves split K (f) into quarters with a ring of U quads each;
-// the quarters are added in wave order and bf16(w * sum) goes to the row's slot
-// (the BF16 split kernel's order).
-template <int U>
+// Down for batches up to 16 tokens: one workgroup per (active expert, NTW tiles of
+// 16 output columns), the four waves split K (f) into quarters with a ring of U
+// quads each; the quarters are added in wave order and bf16(w * sum) goes to the
+// row's slot (the BF16 split kernel's order).
+template <int U, int NTW>
 __global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
-  const int ND = a.d / 16;
-  const int nt = blockIdx.x % ND;
+  const int ND = a.d / 16, NB = ND / NTW;
+  const int nt0 = (blockIdx.x % NB) * NTW;
   int row0, cnt;
-  const int e = expert_of_block(a, blockIdx.x / ND, row0, cnt);
+  const int e = expert_of_block(a, blockIdx.x / NB, row0, cnt);
   if (e < 0) return;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KQ = a.f / 128, kqw = KQ / 4, kq0 = wv * kqw;
-  const int64_t quad0 = ((int64_t)e * ND + nt) * KQ + kq0;
+  const int64_t quad0 = ((int64_t)e * ND + nt0) * KQ + kq0;
   const uint8_t* cp = a.qd + quad0 * 1024 + lane * 16;
   const uint8_t* sp = a.sd + quad0 * 64 + (lane & 15) * 4;
   const uint32_t abytes = (uint32_t)a.T * a.k * a.f * 2;
-  __shared__ f32x4 red[3][64];
+  __shared__ f32x4 red[3][NTW][64];
   for (int m0 = 0; m0 < cnt; m0 += 16) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int r = m0 + (lane & 15);
     const uint32_t xo = r < cnt ? 2u * (uint32_t)((row0 + r) * a.f + kq0 * 128 + 8 * (lane >> 4)) : abytes;
-    u32x4 c[U], x[U][4];
-    uint32_t sc[U];
+    u32x4 c[U][NTW], x[U][4];
+    uint32_t sc[U][NTW];
     auto load = [&](int u, int kq) {
-      c[u] = ld_stream_u32x4(cp + (int64_t)kq * 1024);
-      sc[u] = ld_stream_u32(sp + (int64_t)kq * 64);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        c[u][t] = ld_stream_u32x4(cp + ((int64_t)t * KQ + kq) * 1024);
+        sc[u][t] = ld_stream_u32(sp + ((int64_t)t * KQ + kq) * 64);
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         x[u][s] = xo < abytes ? ld_u32x4((const char*)a.act + xo + (kq * 4 + s) * 64)
@@ -312,7 +333,10 @@ __global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
     auto use = [&](int u) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        acc = mfma16(x[u][s], fp4x8_bf16(c[u][s], e8m0_scale((sc[u] >> (8 * s)) & 255u)), acc);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          acc[t] = mfma16(x[u][s], fp4x8_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u)),
+                          acc[t]);
     };
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -329,18 +353,24 @@ __global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) use(u);
-    if (wv > 0) red[wv - 1][lane] = acc;
+    if (wv > 0) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) red[wv - 1][t][lane] = acc[t];
+    }
     __syncthreads();
     if (wv == 0) {
-      f32x4 v = acc;
 #pragma unroll
-      for (int w = 0; w < 3; ++w) v += red[w][lane];
+      for (int t = 0; t < NTW; ++t) {
+        f32x4 v = acc[t];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = m0 + 4 * (lane >> 4) + i;
-        if (rr < cnt) {
-          const int slot = a.perm[row0 + rr];
-          a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * v[i]);
+        for (int w = 0; w < 3; ++w) v += red[w][t][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = m0 + 4 * (lane >> 4) + i;
+          if (rr < cnt) {
+            const int slot = a.perm[row0 + rr];
+            a.yk[(int64_t)slot * a.d + (nt0 + t) * 16 + (lane & 15)] = f2bf(a.w[slot] * v[i]);
+          }
         }
       }
     }
@@ -348,112 +378,124 @@ __global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
   }
 }
 
-// Down for 17..128 tokens: a workgroup covers 4 output tiles of 16 columns of one
-// expert, one wave per tile accumulating the full K in order, U quads per batch
-// (the BF16 streaming kernel's order).
-template <int MT, int U>
+// Down for 17..128 tokens: a workgroup covers 4 NTW output tiles of 16 columns of
+// one expert, each wave NTW tiles accumulating the full K in order (the BF16
+// streaming kernel's order) through a ring of U quads.
+template <int MT, int U, int NTW>
 __global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
-  const int ND = a.d / 16, NB = ND / 4;
+  const int ND = a.d / 16, NB = ND / (4 * NTW);
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nt = (blockIdx.x % NB) * 4 + wv;
+  const int nt0 = (blockIdx.x % NB) * 4 * NTW + wv * NTW;
   int row0, cnt;
   const int e = expert_of_block(a, blockIdx.x / NB, row0, cnt);
   if (e < 0) return;
   const int KQ = a.f / 128;
-  const int64_t quad0 = ((int64_t)e * ND + nt) * KQ;
+  const int64_t quad0 = ((int64_t)e * ND + nt0) * KQ;
   const uint8_t* cp = a.qd + quad0 * 1024 + lane * 16;
   const uint8_t* sp = a.sd + quad0 * 64 + (lane & 15) * 4;
   for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
-    f32x4 acc[MT];
+    f32x4 acc[NTW][MT];
     const uint16_t* ap[MT];
     bool av[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = m0 + mt * 16 + (lane & 15);
       av[mt] = r < cnt;
       ap[mt] = a.act + (int64_t)(row0 + (av[mt] ? r : 0)) * a.f + 8 * (lane >> 4);
     }
-    for (int kq = 0; kq < KQ; kq += U) {
-      u32x4 c[U], x[MT][U][4];
-      uint32_t sc[U];
+    u32x4 c[U][NTW], x[MT][U][4];
+    uint32_t sc[U][NTW];
+    auto load = [&](int u, int kq) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        c[u] = ld_stream_u32x4(cp + (int64_t)(kq + u) * 1024);
-        sc[u] = ld_stream_u32(sp + (int64_t)(kq + u) * 64);
+      for (int t = 0; t < NTW; ++t) {
+        c[u][t] = ld_stream_u32x4(cp + ((int64_t)t * KQ + kq) * 1024);
+        sc[u][t] = ld_stream_u32(sp + ((int64_t)t * KQ + kq) * 64);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int s = 0; s < 4; ++s)
+          x[mt][u][s] = av[mt] ? ld_u32x4(ap[mt] + (kq * 4 + s) * 32) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto use = [&](int u) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            x[mt][u][s] = av[mt] ? ld_u32x4(ap[mt] + ((kq + u) * 4 + s) * 32) : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int t = 0; t < NTW; ++t) {
+          const u32x4 b = fp4x8_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u));
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 b = fp4x8_bf16(c[u][s], e8m0_scale((sc[u] >> (8 * s)) & 255u));
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(x[mt][u][s], b, acc[mt]);
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16(x[mt][u][s], b, acc[t][mt]);
         }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int kq = 0; kq < KQ - U; kq += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        use(u);
+        load(u, kq + U + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int u = 0; u < U; ++u) use(u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
-        if (r < cnt) {
-          const int slot = a.perm[row0 + r];
-          a.yk[(int64_t)slot * a.d + nt * 16 + (lane & 15)] = f2bf(a.w[slot] * acc[mt][i]);
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + mt * 16 + 4 * (lane >> 4) + i;
+          if (r < cnt) {
+            const int slot = a.perm[row0 + r];
+            a.yk[(int64_t)slot * a.d + (nt0 + t) * 16 + (lane & 15)] = f2bf(a.w[slot] * acc[t][mt][i]);
+          }
         }
-      }
   }
 }
 
 // Launches: the grids are sized for the largest possible number of active experts;
 // workgroups past the active count exit at once. Needs d % 512 == 0 and f % 512 == 0
-// (whole quads per wave quarter).
+// (whole quads per wave quarter; tile counts divisible by the tiles per workgroup).
+// Every pass uses 16-row MFMA blocks: rows do not interact in an MFMA, so the block
+// height changes no result, and most experts hold few rows at these batch sizes.
+// Tiles per wave and ring depths (measured on Beam's shapes): gate/up one tile per
+// wave up to 16 tokens (more workgroups for the few experts), two above; down four
+// tiles per wave in both ranges, with a ring of two quads from 17 tokens on.
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
-  const int kqw = a.d / 128 / 4;
-  dim3 g((unsigned)(max_active * (a.f / 16))), blk(256);
+  const int kqw = a.d / 128 / 4;  // >= 1; U = 2 when it divides
   if (a.T <= 16) {
-    if (kqw % 5 == 0)
-      hipLaunchKernelGGL((gateup_fp4_kernel<1, 5>), g, blk, 0, s, a);
-    else if (kqw % 4 == 0)
-      hipLaunchKernelGGL((gateup_fp4_kernel<1, 4>), g, blk, 0, s, a);
-    else if (kqw % 2 == 0)
-      hipLaunchKernelGGL((gateup_fp4_kernel<1, 2>), g, blk, 0, s, a);
-    else
-      hipLaunchKernelGGL((gateup_fp4_kernel<1, 1>), g, blk, 0, s, a);
-  } else {
+    dim3 g((unsigned)(max_active * (a.f / 16))), blk(256);
     if (kqw % 2 == 0)
-      hipLaunchKernelGGL((gateup_fp4_kernel<2, 2>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 2, 1>), g, blk, 0, s, a);
     else
-      hipLaunchKernelGGL((gateup_fp4_kernel<2, 1>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 1, 1>), g, blk, 0, s, a);
+  } else {
+    dim3 g((unsigned)(max_active * (a.f / 32))), blk(256);
+    if (kqw % 2 == 0)
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 2, 2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((gateup_fp4_kernel<1, 1, 2>), g, blk, 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   if (a.T <= kSplitDownMaxT) {
-    const int kqw = a.f / 128 / 4;
-    dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
-    if (kqw % 5 == 0)
-      hipLaunchKernelGGL((down_split_fp4_kernel<5>), g, blk, 0, s, a);
-    else if (kqw % 4 == 0)
-      hipLaunchKernelGGL((down_split_fp4_kernel<4>), g, blk, 0, s, a);
-    else if (kqw % 2 == 0)
-      hipLaunchKernelGGL((down_split_fp4_kernel<2>), g, blk, 0, s, a);
-    else
-      hipLaunchKernelGGL((down_split_fp4_kernel<1>), g, blk, 0, s, a);
+    dim3 g((unsigned)(max_active * (a.d / 64))), blk(256);
+    hipLaunchKernelGGL((down_split_fp4_kernel<1, 4>), g, blk, 0, s, a);
   } else {
     const int KQ = a.f / 128;
-    dim3 g((unsigned)(max_active * (a.d / 64))), blk(256);
+    dim3 g((unsigned)(max_active * (a.d / 256))), blk(256);
     if (KQ % 2 == 0)
-      hipLaunchKernelGGL((down_stream_fp4_kernel<2, 2>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((down_stream_fp4_kernel<1, 2, 4>), g, blk, 0, s, a);
     else
-      hipLaunchKernelGGL((down_stream_fp4_kernel<2, 1>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((down_stream_fp4_kernel<1, 1, 4>), g, blk, 0, s, a);
   }
   return hipGetLastError();
 }
