@@ -41,7 +41,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode1",
                    choices=["decode1", "decode32", "decode128", "prefill16k", "skew32k",
-                            "skew32k_half", "tiny"])
+                            "skew32k_half", "tiny", "dense1", "dense16k"],
+                   help="dense1 / dense16k: Beam's dense SwiGLU layer (d_ff 20480) instead of "
+                        "the MoE; a step is that layer, then the next boundary on its output")
     p.add_argument("--rotations", type=int, default=None, help="distinct token sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
@@ -138,10 +140,14 @@ def main():
     W, b = sd.router(wl)
     wg, wu, wd = sd.experts(wl)
     mx = args.experts == "mxfp4"
-    if mx and not decode:
-        print("--experts mxfp4 covers the decode batches (T <= 128)", file=sys.stderr)
+    dense = wl.name.startswith("dense")
+    if mx and (not decode or dense):
+        print("--experts mxfp4 covers the MoE decode batches (T <= 128)", file=sys.stderr)
         sys.exit(2)
-    if mx:
+    if dense:
+        moe = None
+        dense_h = beam.beam_dense_init(wl.d, wl.f, T, wg[0], wu[0], wd[0])
+    elif mx:
         fp4 = []
         for t in (wg, wu, wd):
             fp4 += list(beam.beam_mxfp4_quantize(t))
@@ -161,7 +167,18 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t0:.1f}s")
 
-    if args.step == "boundary-first":
+    if dense:
+        # each token set's z from its boundary, before the timed region; a step is the dense
+        # layer on it, then the next boundary with its output as the branch
+        z_in = [beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps)[1]
+                for s in range(R)]
+
+        def step(i):
+            s = i % R
+            beam.beam_dense_forward(dense_h, z_in[s], y)
+            beam.beam_sublayer_norm_residual(hs[s], y, wpost, wpre, wl.n, wl.eps, h_out=h_out,
+                                             z_out=z)
+    elif args.step == "boundary-first":
         def step(i):
             s = i % R
             beam.beam_sublayer_forward(moe.handle, hs[s], xs[s], wpost, wpre, wl.n, wl.eps, y,
@@ -183,11 +200,13 @@ def main():
     distinct = []
     ids_buf = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
     w_buf = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
-    for s in range(R):
+    for s in range(R if not dense else 0):
         beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps, h_out=h_out,
                                          z_out=z)
         beam.beam_router_topk(moe.handle, z, ids_buf, w_buf)
         distinct.append(len(np.unique(ids_buf.cpu().numpy())))
+    if dense:
+        distinct = [1]
     mean_distinct = float(np.mean(distinct))
 
     def timed(fn, n):
@@ -229,7 +248,7 @@ def main():
             log(f"graph: {ms_graph * 1e3:.1f} us/step")
             # graph result equals the eager result
             step(0)
-            out = y if args.step == "boundary-first" else z  # the step's last output
+            out = y if (args.step == "boundary-first" and not dense) else z  # last output
             out_eager = out.clone()
             graphs[0].replay()
             torch.cuda.synchronize()
@@ -265,7 +284,7 @@ def main():
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4))
         traffic = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
         roof["traffic"] = traffic
-        step_bytes = (mean_distinct * 3 * wl.f * wl.d * wbytes + wl.E * wl.d * 4
+        step_bytes = (mean_distinct * 3 * wl.f * wl.d * wbytes + (0 if dense else wl.E * wl.d * 4)
                       + T * wl.d * 2 * 6 + T * wl.k * (wl.f * 4 + wl.d * 4))
         whole = dict(algorithmic_bytes=round(step_bytes), hbm_frac=round(
             step_bytes / (best_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
@@ -312,7 +331,10 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    moe.close()
+    if dense:
+        beam.beam_moe_destroy(dense_h)
+    else:
+        moe.close()
 
 
 def cpu_baseline(wl, sample=None, mxfp4=False):
@@ -328,7 +350,7 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
     import synth
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    n = sample or (threads if mxfp4 else 2 * threads)
+    n = sample or (threads if (mxfp4 or wl.name.startswith("dense")) else 2 * threads)
     rows = list(range(min(n, wl.T))) if wl.T >= n else list(range(wl.T))
     if len(rows) < n:  # decode: also take tokens of the rotation sets
         extra = n - len(rows)
@@ -342,6 +364,22 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
          [synth.token_rows(wl, [t], "x", token_set=s) for s, t in rot]
     wpost, wpre = synth.norm_weight(wl, "post"), synth.norm_weight(wl, "pre")
     Wr, bias = synth.router_weight(wl), synth.router_bias(wl)
+    if wl.name.startswith("dense"):
+        W = synth.expert_weights(wl, 0)
+
+        def one_dense(i):
+            _, z = oracle.boundary(hh[i], xx[i], wpost, wpre, wl.n, wl.eps)
+            return oracle.dense_swiglu(z, *W)
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one_dense, range(len(hh))))
+        dt = time.perf_counter() - t0
+        log(f"cpu baseline: {len(hh)} tokens in {dt:.2f}s on {threads} threads")
+        return dict(value=round(len(hh) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                    sample=f"{len(hh)} tokens of {wl.name}, each through the boundary and the "
+                           f"dense SwiGLU layer single-threaded, {threads} tokens at a time; "
+                           f"{dt:.1f} s wall")
     # routing first (cheap) to know which experts to draw; drawing inputs is not timed
     zs, routes = [], []
     for h, x in zip(hh, xx):

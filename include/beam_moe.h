@@ -24,7 +24,8 @@
  *   - Non-finite inputs give unspecified (but in-bounds) results.
  *   - Compute calls allocate nothing, so they can be captured in a HIP graph.
  *   - A handle must not be used by two streams at the same time (its
- *     workspace is shared by its calls).
+ *     workspace is shared by its calls). A dense-layer handle (beam_dense_init)
+ *     serves beam_dense_forward only; the MoE compute calls reject it.
  *   - No exception or signal crosses the ABI.
  */
 #ifndef BEAM_MOE_H
@@ -50,7 +51,7 @@ enum {
  * [vLLM §MoE und Residual-Stream]: Beam uses hidden 5120, 256 routed experts
  * in 8 groups, best 4 groups then top 8 experts, d_ff 2560, scale 2.5.
  * Supported here: hidden % 256 == 0 and hidden <= 16384; d_ff % 256 == 0 and
- * d_ff <= 16384; n_experts <= 256 and a multiple of n_groups; n_groups <= 64;
+ * d_ff <= 32768; n_experts <= 256 and a multiple of n_groups; n_groups <= 64;
  * 1 <= topk_groups <= n_groups; 1 <= topk <= min(32, topk_groups * E/G);
  * 1 <= max_tokens and max_tokens * topk < 2^31; routed_scale finite. */
 typedef struct {
@@ -122,6 +123,31 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
                         const uint8_t* gate_scales, const uint8_t* up_codes,
                         const uint8_t* up_scales, const uint8_t* down_codes,
                         const uint8_t* down_scales, void* stream, beam_moe_handle* out);
+
+/*
+ * beam_dense_init — a handle for one dense SwiGLU MLP layer.
+ * [vLLM §Modellarchitektur]: Beam's layers 0-2 use a dense SwiGLU MLP (d_ff 20480)
+ * instead of the routed experts. Computed per token row with the experts' rounding
+ * points (FP32 accumulation; gate, up and the activation rounded to BF16):
+ *   g = bf16(z . Wg^T), u = bf16(z . Wu^T), act = bf16(silu(g) * u), y = bf16(act . Wd^T)
+ * Arguments: hidden (d), d_ff (f) and max_tokens as in beam_moe_config (the same
+ * shape limits); w_gate, w_up [f, d] BF16 and w_down [d, f] BF16 (device memory,
+ * read during the call only; copied and repacked into the handle). The handle runs
+ * the expert kernels as one expert that every token takes with weight 1 (exactly the
+ * dense result), and serves only beam_dense_forward; the MoE entry points reject it
+ * with BEAM_ERR_INVALID_ARG. Synchronises; *out is set only on BEAM_OK.
+ */
+int beam_dense_init(int32_t hidden, int32_t d_ff, int32_t max_tokens, const uint16_t* w_gate,
+                    const uint16_t* w_up, const uint16_t* w_down, void* stream,
+                    beam_moe_handle* out);
+
+/*
+ * beam_dense_forward — y [T, d] BF16 = the dense SwiGLU layer of beam_dense_init on
+ * z [T, d] BF16 (T <= max_tokens, else BEAM_ERR_CAPACITY; T == 0 is a no-op). y_out
+ * must not overlap z. A handle from beam_moe_init gives BEAM_ERR_INVALID_ARG.
+ */
+int beam_dense_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                       void* stream);
 
 /* beam_moe_destroy — synchronise and free everything the handle owns. NULL is a no-op. */
 int beam_moe_destroy(beam_moe_handle h);

@@ -182,6 +182,15 @@ def expert_rows(zrows, Wg, Wu, Wd, wrow):
     return out
 
 
+def dense_swiglu(z, Wg, Wu, Wd):
+    """A dense SwiGLU MLP layer ([vLLM page, §Modellarchitektur]: Beam's layers 0-2, d_ff
+    20480) on rows z [T, d]: O5 with routing weight 1, i.e. g = bf16(z.Wg^T), u = bf16(z.Wu^T),
+    act = bf16(silu(g) * u), y = bf16(act.Wd^T) (1 * acc is exact). Reading: the dense layer
+    keeps the experts' rounding points."""
+    z = _c(z, np.uint16)
+    return expert_rows(z, Wg, Wu, Wd, np.ones(z.shape[0], dtype=np.float32))
+
+
 def combine(yk, ids=None, E=None):
     yk = _c(yk, np.uint16)
     T, k, d = yk.shape

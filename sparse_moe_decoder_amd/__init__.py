@@ -9,6 +9,8 @@ from .binding import (  # noqa: F401
     BeamError,
     BeamMoE,
     LIB_PATH,
+    beam_dense_forward,
+    beam_dense_init,
     beam_grouped_topk,
     beam_moe_destroy,
     beam_moe_forward,

@@ -41,6 +41,8 @@ def lib():
         L.beam_moe_init_mxfp4.argtypes = [ctypes.POINTER(beam_moe_config), vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, ctypes.POINTER(vp)]
         L.beam_mxfp4_quantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp]
+        L.beam_dense_init.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.POINTER(vp)]
+        L.beam_dense_forward.argtypes = [vp, i32, vp, vp, vp]
         L.beam_moe_destroy.argtypes = [vp]
         L.beam_sublayer_norm_residual.argtypes = [i32, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp]
         L.beam_router_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp]
@@ -59,6 +61,7 @@ def lib():
         L.beam_kernel_name.argtypes = [i32]
         L.beam_kernel_name.restype = ctypes.c_char_p
         for name in ("beam_moe_init", "beam_moe_init_mxfp4", "beam_mxfp4_quantize",
+                     "beam_dense_init", "beam_dense_forward",
                      "beam_moe_destroy", "beam_sublayer_norm_residual",
                      "beam_router_topk", "beam_grouped_topk", "beam_moe_forward",
                      "beam_sublayer_forward", "beam_moe_forward_boundary",
@@ -149,6 +152,29 @@ def beam_moe_init_mxfp4(cfg: dict, router_w, router_bias, gate_codes, gate_scale
         _ptr(down_codes, u8, (E, d, f // 2), "down_codes"),
         _ptr(down_scales, u8, (E, d, f // 32), "down_scales"), _stream(stream), ctypes.byref(h)))
     return h
+
+
+def beam_dense_init(hidden, d_ff, max_tokens, w_gate, w_up, w_down, stream=None):
+    import torch
+    bf, f, d = torch.bfloat16, d_ff, hidden
+    h = ctypes.c_void_p()
+    _check("beam_dense_init", lib().beam_dense_init(
+        int(hidden), int(d_ff), int(max_tokens), _ptr(w_gate, bf, (f, d), "w_gate"),
+        _ptr(w_up, bf, (f, d), "w_up"), _ptr(w_down, bf, (d, f), "w_down"), _stream(stream),
+        ctypes.byref(h)))
+    return h
+
+
+def beam_dense_forward(handle, z, y_out=None, stream=None):
+    """Dense SwiGLU layer on z [T, d]; returns y [T, d]."""
+    import torch
+    T, d = z.shape
+    if y_out is None:
+        y_out = torch.empty_like(z)
+    bf = torch.bfloat16
+    _check("beam_dense_forward", lib().beam_dense_forward(
+        handle, T, _ptr(z, bf, (T, d), "z"), _ptr(y_out, bf, (T, d), "y_out"), _stream(stream)))
+    return y_out
 
 
 def beam_moe_destroy(handle):

@@ -101,6 +101,7 @@ struct beam_moe_ctx {
   uint16_t* wgu = nullptr;    // packed gate/up (BF16 experts)
   uint16_t* wdp = nullptr;    // packed down (BF16 experts)
   bool mxfp4 = false;         // 4-bit experts: the four arrays below instead of wgu, wdp
+  bool dense = false;         // a dense SwiGLU layer (beam_dense_init): one expert, no routing
   uint8_t* qgu = nullptr;     // gate/up codes, decode layout
   uint8_t* sgu = nullptr;     // gate/up scales
   uint8_t* qd = nullptr;      // down codes
@@ -139,7 +140,7 @@ int validate_config(const beam_moe_config* c) {
   const int64_t wide = c->hidden > c->d_ff ? c->hidden : c->d_ff;
   if ((int64_t)c->max_tokens * c->topk * wide >= (1ll << 31)) return BEAM_ERR_UNSUPPORTED;
   if (c->hidden % 256 != 0 || c->hidden > 16384) return BEAM_ERR_UNSUPPORTED;
-  if (c->d_ff % 256 != 0 || c->d_ff > 16384) return BEAM_ERR_UNSUPPORTED;
+  if (c->d_ff % 256 != 0 || c->d_ff > 32768) return BEAM_ERR_UNSUPPORTED;
   if (c->n_experts > 256 || c->n_groups > 64 || c->topk > 32) return BEAM_ERR_UNSUPPORTED;
   return BEAM_OK;
 }
@@ -359,11 +360,15 @@ int init_handle(const beam_moe_config* cfg, const float* router_w, const float* 
     return BEAM_ERR_OOM;
   }
   if (e == hipSuccess)
-    e = hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float), hipMemcpyDeviceToDevice, s);
+    e = router_w ? hipMemcpyAsync(h->router_w, router_w, E * d * sizeof(float),
+                                  hipMemcpyDeviceToDevice, s)
+                 : hipMemsetAsync(h->router_w, 0, E * d * sizeof(float), s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(h->bias, router_bias, E * sizeof(float), hipMemcpyDeviceToDevice, s);
+    e = router_bias ? hipMemcpyAsync(h->bias, router_bias, E * sizeof(float),
+                                     hipMemcpyDeviceToDevice, s)
+                    : hipMemsetAsync(h->bias, 0, E * sizeof(float), s);
   if (e == hipSuccess) e = hipMemsetAsync(h->route_done, 0, sizeof(uint32_t), s);
-  if (e == hipSuccess && E % 64 == 0)
+  if (e == hipSuccess && E % 64 == 0 && router_w)
     e = launch_repack_router(router_w, h->router_x3, (int)E, (int)d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -435,6 +440,62 @@ int beam_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t* src, uint8_t* c
                                           (hipStream_t)stream));
 }
 
+int beam_dense_init(int32_t hidden, int32_t d_ff, int32_t max_tokens, const uint16_t* w_gate,
+                    const uint16_t* w_up, const uint16_t* w_down, void* stream,
+                    beam_moe_handle* out) {
+  beam_moe_config cfg{hidden, 1, 1, 1, 1, d_ff, max_tokens, 1.0f};
+  int st = validate_config(&cfg);
+  if (st != BEAM_OK) return st;
+  if (!out || !w_gate || !w_up || !w_down) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down)) return BEAM_ERR_INVALID_ARG;
+  return init_handle(&cfg, nullptr, nullptr, stream, out, [&](beam_moe_ctx* h, hipStream_t s) -> int {
+    const size_t d = hidden, f = d_ff;
+    h->dense = true;
+    if (!dev_alloc(h, &h->wgu, 2 * f * d) || !dev_alloc(h, &h->wdp, d * f)) return BEAM_ERR_OOM;
+    if (launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, 1, (int)f, (int)d, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    PermArgs pa{max_tokens, 1, 1, kGemmBM, nullptr, h->counts, h->offsets, h->perm, nullptr,
+                nullptr, h->active, h->n_active, h->tile_start, nullptr, nullptr};
+    return hip_status(launch_dense_plan(0, max_tokens, true, pa, h->w, s));
+  });
+}
+
+int beam_dense_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                       void* stream) {
+  if (!h || !h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  const beam_moe_config& c = h->cfg;
+  if (!z || !y_out || !aligned16(z) || !aligned16(y_out) ||
+      overlaps(z, y_out, (int64_t)T * c.hidden * 2))
+    return BEAM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  PermArgs pa{T, 1, 1, kGemmBM, nullptr, h->counts, h->offsets, h->perm, nullptr, nullptr,
+              h->active, h->n_active, h->tile_start, nullptr, nullptr};
+  {
+    ProfScope ps(K_PERMUTE, s);
+    if (launch_dense_plan(T, c.max_tokens, false, pa, h->w, s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  // the down pass writes each row's bf16(1 * sum) straight to y (one slot per token)
+  ExpertArgs ea{T, 1, c.hidden, c.d_ff, 1, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
+                h->n_active, h->tile_start, h->w, h->act, y_out};
+  if (T <= kStreamMaxT) {
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_stream(ea, 1, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    ProfScope ps(K_DOWN, s);
+    return hip_status(T <= kSplitDownMaxT ? launch_down_split(ea, 1, s) : launch_down_stream(ea, 1, s));
+  }
+  const int max_tiles = (T + kGemmBM - 1) / kGemmBM + 1;
+  {
+    ProfScope ps(K_GATEUP, s);
+    if (launch_gateup_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  ProfScope ps(K_DOWN, s);
+  return hip_status(launch_down_gemm(ea, max_tiles, s));
+}
+
 int beam_moe_destroy(beam_moe_handle h) {
   if (!h) return BEAM_OK;
   int st = hip_status(hipDeviceSynchronize());
@@ -464,7 +525,7 @@ int beam_sublayer_norm_residual(int32_t T, int32_t d, const uint16_t* h_in, cons
 
 int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* logits_out,
                      int32_t* ids_out, float* w_out, void* stream) {
-  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
   if (!z || !ids_out || !w_out || !aligned16(z) || ((uintptr_t)ids_out & 3u) ||
@@ -475,7 +536,7 @@ int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* log
 
 int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t* ids_out,
                       float* w_out, void* stream) {
-  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
   if (!logits || !ids_out || !w_out || ((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) ||
@@ -493,7 +554,7 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
                      const int32_t* ids_in, const float* w_in, float* logits_out,
                      int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
                      void* stream) {
-  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
   if (!z || !y_out || !aligned16(z) || !aligned16(y_out)) return BEAM_ERR_INVALID_ARG;
@@ -513,7 +574,7 @@ int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
                               int32_t n, float eps, uint16_t* h_out, uint16_t* z_out,
                               uint16_t* y_out, const int32_t* ids_in, const float* w_in,
                               float* logits_out, int32_t* ids_out, float* w_out, void* stream) {
-  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
   const beam_moe_config& c = h->cfg;
@@ -553,7 +614,7 @@ int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, co
                           const uint16_t* w_post, const uint16_t* w_pre, int32_t n, float eps,
                           uint16_t* h_out, uint16_t* z_out, uint16_t* y_out, float* logits_out,
                           int32_t* ids_out, float* w_out, void* stream) {
-  if (!h || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
   const beam_moe_config& c = h->cfg;

@@ -108,6 +108,11 @@ hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8
                                int f, int d, uint8_t* qgu, uint8_t* sgu, uint8_t* qd, uint8_t* sd,
                                hipStream_t s);
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
+// Dense SwiGLU layer as one expert taking every token with weight 1: with init, rows
+// 0..max_tokens-1 get the identity order and weight 1; always, the counts, offsets,
+// active list and tile table of a T-token call (one expert, tiles of bm rows)
+hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a, float* w,
+                             hipStream_t s);
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
 // the boundary with x = the combine of c (b.x unused); b.d <= kBoundaryWgMaxD
 hipError_t launch_combine_boundary(const BoundaryArgs& b, const CombineArgs& c, hipStream_t s);

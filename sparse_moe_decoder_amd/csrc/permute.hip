@@ -434,6 +434,35 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
     group_slots_wave(pa, ids_lds, lane, reinterpret_cast<int*>(c_lds[0]), reinterpret_cast<int*>(c_lds[1]));
 }
 
+// Dense layer plan (see launch_dense_plan): one expert, every row in token order.
+__global__ __launch_bounds__(256) void dense_plan_kernel(int T, int max_tokens, int init, PermArgs a,
+                                                         float* w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (init) {
+    for (int r = i; r < max_tokens; r += gridDim.x * blockDim.x) {
+      a.perm[r] = r;
+      w[r] = 1.0f;
+    }
+  }
+  if (i == 0) {
+    a.counts[0] = T;
+    a.offsets[0] = 0;
+    a.offsets[1] = T;
+    a.active[0] = 0;
+    *a.n_active = T > 0 ? 1 : 0;
+    a.tile_start[0] = 0;
+    a.tile_start[1] = (T + a.bm - 1) / a.bm;
+  }
+}
+
+hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a, float* w,
+                             hipStream_t s) {
+  const unsigned g = init ? (unsigned)((max_tokens + 255) / 256) : 1u;
+  hipLaunchKernelGGL(dense_plan_kernel, dim3(g), dim3(init ? 256 : 64), 0, s, T, max_tokens,
+                     init ? 1 : 0, a, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
                                    uint32_t* done, uint64_t* sc, hipStream_t s) {
   hipLaunchKernelGGL(route_fused_tiny_kernel<false>, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a,

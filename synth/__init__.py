@@ -61,6 +61,11 @@ def _beam(name, T, **kw):
     return Workload(name=name, T=T, d=5120, E=256, G=8, kg=4, k=8, f=2560, **kw)
 
 
+def _dense(name, T, **kw):
+    # a dense SwiGLU layer (Beam's layers 0-2) as one expert that every token takes
+    return Workload(name=name, T=T, d=5120, E=1, G=1, kg=1, k=1, f=20480, scale=1.0, **kw)
+
+
 HOT16 = tuple(range(0, 256, 16))  # two per group of 32: balanced across groups
 
 WORKLOADS = {
@@ -72,6 +77,8 @@ WORKLOADS = {
     "prefill16k": _beam("prefill16k", 16384, note="prefill 8 x 2048 tokens"),
     "skew32k": _beam("skew32k", 32768, hot_experts=HOT16, hot_bias=0.5,
                      note="skewed long prefill: 16 hot experts at bias +0.5"),
+    "dense1": _dense("dense1", 1, note="dense SwiGLU layer (d_ff 20480), batch-1 decode"),
+    "dense16k": _dense("dense16k", 16384, note="dense SwiGLU layer (d_ff 20480), prefill 8 x 2048"),
     "skew32k_half": _beam("skew32k_half", 32768, hot_experts=HOT16, hot_bias=0.255,
                           note="skewed long prefill: bias +0.255 (about half the assignments hot)"),
 }

@@ -155,3 +155,16 @@ def test_mxfp4_quantize_validation(L):
     assert f(4, 64, None, p, p, None) == -1       # null
     assert f(4, 64, ctypes.c_void_p(0x1008), p, p, None) == -1  # misaligned source
     assert f(0, 64, None, None, None, None) == 0  # rows = 0: no-op
+
+
+def test_dense_validation(L):
+    h = ctypes.c_void_p()
+    p = ctypes.c_void_p(0x1000)
+    f = L.beam_dense_init
+    assert f(5000, 20480, 16, p, p, p, None, ctypes.byref(h)) == -2    # hidden % 256 != 0
+    assert f(5120, 40960, 16, p, p, p, None, ctypes.byref(h)) == -2    # d_ff above 32768
+    assert f(5120, 20480, 0, p, p, p, None, ctypes.byref(h)) == -1     # max_tokens
+    assert f(5120, 20480, 16, None, p, p, None, ctypes.byref(h)) == -1
+    assert f(5120, 20480, 16, p, ctypes.c_void_p(0x1008), p, None, ctypes.byref(h)) == -1
+    assert not h.value
+    assert L.beam_dense_forward(None, 1, p, p, None) == -1
