@@ -1,7 +1,7 @@
 """GPU parity of the dense SwiGLU layer (beam_dense_init / beam_dense_forward) against the
 oracle, every call through the C ABI:
 
-- a small layer (d 512, d_ff 1280) at T = 1, 8, 20, 40 and 300: every row compared; this takes
+- a small layer (d 512, d_ff 2048) at T = 1, 8, 20, 40 and 300: every row compared; this takes
   both weight-streaming down passes and the grouped GEMM with a ragged last tile;
 - Beam's dense layer (d 5120, d_ff 20480) at T = 1 and 20 (every element) and at 16384 tokens
   (sampled rows, first and last rows of tiles included);
@@ -20,7 +20,7 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
-SMALL = dataclasses.replace(synth.WORKLOADS["dense1"], d=512, f=1280, name="dense_small")
+SMALL = dataclasses.replace(synth.WORKLOADS["dense1"], d=512, f=2048, name="dense_small")
 BEAM = synth.WORKLOADS["dense1"]
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
