@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--experts", choices=("bf16", "mxfp4"), default="bf16",
                    help="expert weight format: BF16, or MXFP4 (4-bit E2M1 codes with one E8M0 "
                         "scale per 32 values, quantised on the device from the BF16 weights; "
-                        "BF16 activations; decode batches only)")
+                        "BF16 activations)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies of BYTES (for scaling HBM "
                         "counter readings) and exit")
@@ -141,8 +141,8 @@ def main():
     wg, wu, wd = sd.experts(wl)
     mx = args.experts == "mxfp4"
     dense = wl.name.startswith("dense")
-    if mx and (not decode or dense):
-        print("--experts mxfp4 covers the MoE decode batches (T <= 128)", file=sys.stderr)
+    if mx and dense:
+        print("--experts mxfp4 applies to the MoE workloads", file=sys.stderr)
         sys.exit(2)
     if dense:
         moe = None

@@ -113,10 +113,11 @@ int beam_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t* src, uint8_t* c
  * what a beam_moe_init handle computes on the dequantised weights, bit for bit, while
  * reading about 0.53 bytes per weight instead of 2 (the decode path is bound by the
  * weight stream). Every compute entry point takes either kind of handle.
- * Supported: the beam_moe_init shapes with hidden % 512 == 0, d_ff % 512 == 0 and
- * max_tokens <= 128 (the weight-streaming decode range); others give
- * BEAM_ERR_UNSUPPORTED. Code arrays must be 4-byte aligned. The weights are copied
- * and repacked into handle-owned memory; the caller may free its copies after return.
+ * Supported: the beam_moe_init shapes with hidden % 512 == 0 and d_ff % 512 == 0;
+ * others give BEAM_ERR_UNSUPPORTED. Code arrays must be 4-byte aligned. The weights are
+ * copied and repacked into handle-owned memory (one layout for the weight-streaming
+ * passes of T <= 128, and, when max_tokens > 128, a second one for the grouped GEMMs:
+ * about 0.53 and 1.06 bytes per weight); the caller may free its copies after return.
  */
 int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
                         const float* router_bias, const uint8_t* gate_codes,

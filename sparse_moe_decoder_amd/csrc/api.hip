@@ -106,6 +106,10 @@ struct beam_moe_ctx {
   uint8_t* sgu = nullptr;     // gate/up scales
   uint8_t* qd = nullptr;      // down codes
   uint8_t* sd = nullptr;      // down scales
+  uint8_t* pqgu = nullptr;    // grouped-GEMM layout of the 4-bit weights (max_tokens > 128)
+  uint8_t* psgu = nullptr;
+  uint8_t* pqd = nullptr;
+  uint8_t* psd = nullptr;
   // workspace (owned), sized for max_tokens
   float* logits = nullptr;     // [maxT, E]
   int32_t* ids = nullptr;      // [maxT, k]
@@ -257,8 +261,17 @@ int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, con
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk, h->qgu, h->sgu, h->qd, h->sd};
-  if (h->mxfp4) {  // max_tokens <= kStreamMaxT: the weight-streaming passes only
+                h->n_active, h->tile_start, w, h->act, h->yk, h->qgu, h->sgu, h->qd, h->sd,
+                h->pqgu, h->psgu, h->pqd, h->psd};
+  if (h->mxfp4 && T > kStreamMaxT) {  // 4-bit grouped GEMMs
+    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_gateup_gemm_fp4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+    ProfScope ps(K_DOWN, s);
+    if (launch_down_gemm_fp4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+  } else if (h->mxfp4) {  // 4-bit weight-streaming passes
     const int max_active = slots < E ? slots : E;
     {
       ProfScope ps(K_GATEUP, s);
@@ -409,8 +422,7 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
                         const uint8_t* down_scales, void* stream, beam_moe_handle* out) {
   int st = validate_config(cfg);
   if (st != BEAM_OK) return st;
-  if (cfg->max_tokens > kStreamMaxT || cfg->hidden % 512 != 0 || cfg->d_ff % 512 != 0)
-    return BEAM_ERR_UNSUPPORTED;
+  if (cfg->hidden % 512 != 0 || cfg->d_ff % 512 != 0) return BEAM_ERR_UNSUPPORTED;
   if (!out || !router_w || !router_bias || !gate_codes || !gate_scales || !up_codes ||
       !up_scales || !down_codes || !down_scales)
     return BEAM_ERR_INVALID_ARG;
@@ -423,9 +435,16 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
     if (!dev_alloc(h, &h->qgu, E * 2 * f * d / 2) || !dev_alloc(h, &h->sgu, E * 2 * f * d / 32) ||
         !dev_alloc(h, &h->qd, E * d * f / 2) || !dev_alloc(h, &h->sd, E * d * f / 32))
       return BEAM_ERR_OOM;
-    return hip_status(launch_repack_mxfp4(gate_codes, gate_scales, up_codes, up_scales, down_codes,
-                                          down_scales, (int)E, (int)f, (int)d, h->qgu, h->sgu,
-                                          h->qd, h->sd, s));
+    if (launch_repack_mxfp4(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
+                            (int)E, (int)f, (int)d, h->qgu, h->sgu, h->qd, h->sd, s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    if (cfg->max_tokens <= kStreamMaxT) return BEAM_OK;
+    if (!dev_alloc(h, &h->pqgu, E * 2 * f * d / 2) || !dev_alloc(h, &h->psgu, E * 2 * f * d / 32) ||
+        !dev_alloc(h, &h->pqd, E * d * f / 2) || !dev_alloc(h, &h->psd, E * d * f / 32))
+      return BEAM_ERR_OOM;
+    return hip_status(launch_repack_mxfp4_gemm(gate_codes, gate_scales, up_codes, up_scales,
+                                               down_codes, down_scales, (int)E, (int)f, (int)d,
+                                               h->pqgu, h->psgu, h->pqd, h->psd, s));
   });
 }
 

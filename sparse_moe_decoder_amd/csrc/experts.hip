@@ -442,11 +442,35 @@ __device__ __forceinline__ void wait_blocks(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// s_waitcnt vmcnt(3 n): the same for three copies per K block (4-bit weights)
+__device__ __forceinline__ void wait_blocks3(int n) {
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// 4-bit weights in the grouped GEMM (MXFP4, see experts_mxfp4.hip): per (expert, n-tile of
+// 256 stage columns, 32-wide K block) 4096 bytes of codes — stage column c at 16 c, the
+// 8-value half h of its 16-wide k-step kk at ((h ^ ((c >> 4) & 1)) * 8 + kk * 4) — and 256
+// scale bytes (column c's scale of the block, byte c). Stage columns: gate/up c < 128 gate
+// output 128 nb + c, c >= 128 up output 128 nb + c - 128; down output 256 nb + c.
+constexpr int GSTAGE_Q = 4096 + 256;  // bytes per 4-bit B stage
+
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return r;
+}
+
 struct GemmTile {
   int e, row0, rows, nb;
 };
 
-template <bool GATEUP, int MW, int NS>
+template <bool GATEUP, int MW, int NS, bool FP4 = false>
 __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTile& t,
                                                uint16_t* smem) {
   constexpr int NW = 8;
@@ -491,6 +515,17 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
     }
   }
   const int bstep = GATEUP ? 2 * 512 : 512;  // elements per 32-wide K block
+  // 4-bit B: waves 0-3 copy a quarter each of a block's codes, waves 4-7 its scales
+  // (lanes 0-15; the same bytes), so every wave issues three copies per K block
+  const uint8_t* qsrc = nullptr;
+  uint32_t qdst = 0;
+  if constexpr (FP4) {
+    const int NTL = GATEUP ? a.f / 128 : a.d / 256;
+    const int64_t blk0 = ((int64_t)e * NTL + nb) * nkb;  // (expert, n-tile, K block 0)
+    qsrc = wv < 4 ? (GATEUP ? a.pqgu : a.pqd) + blk0 * 4096 + wv * 1024 + lane * 16
+                  : (GATEUP ? a.psgu : a.psd) + blk0 * 256 + (lane & 15) * 16;
+    qdst = wvu < 4 ? (uint32_t)(wvu * 1024) : 4096u;
+  }
   // down: thread r < 256 holds row r's slot and routing weight for the epilogue
   // (loaded now, so the loads are long done when the K loop ends)
   int my_slot = 0;
@@ -501,16 +536,25 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   }
 
   auto stage_a = [&](int st) -> uint16_t* { return smem + st * GSTAGE_A; };
-  auto stage_b = [&](int st) -> uint16_t* { return smem + NS * GSTAGE_A + st * GSTAGE_B; };
-  // copy p (0, 1: A rows; 2, 3: B blocks) of K block kb into stage st
+  auto stage_b = [&](int st) -> uint16_t* {
+    if constexpr (FP4) return smem + NS * GSTAGE_A + st * (GSTAGE_Q / 2);
+    return smem + NS * GSTAGE_A + st * GSTAGE_B;
+  };
+  // copy p (0, 1: A rows; 2, 3: B blocks; 4-bit: 2 is the wave's share of the B block)
+  // of K block kb into stage st
   auto issue = [&](int kb, int st, int p) {
-    if (p < 2)
+    if (p < 2) {
       lds_dma16(abase + aoff[p] + kb * GBK,
                 lds_addr(stage_a(st)) + (uint32_t)(wvu * 32 * GBK * 2) + p * 16 * GBK * 2);
-    else
+    } else if constexpr (FP4) {
+      const uint16_t* src = (const uint16_t*)(qsrc + (int64_t)kb * (wv < 4 ? 4096 : 256));
+      if (wv < 4 || lane < 16) lds_dma16(src, lds_addr(stage_b(st)) + qdst);
+    } else {
       lds_dma16(bbase + boff[p - 2] + kb * bstep,
                 lds_addr(stage_b(st)) + (uint32_t)(wvu * 2 * 1024) + (p - 2) * 1024);
+    }
   };
+  constexpr int CP = FP4 ? 3 : 4;  // copies per wave and K block
 
   const int l32 = lane & 31, lh = lane >> 5;
   int aread[2], bread[2][2];
@@ -541,12 +585,29 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
     const uint16_t* A = stage_a(st);
     const uint16_t* B = stage_b(st);
     u32x4 fa[2][MW], fb[2][2];
+    if constexpr (FP4) {
+      // stage column of this lane's N tile nn; both k-steps' codes in one 8-byte read
+      const uint8_t* Bq = (const uint8_t*)B;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int nn = 0; nn < 2; ++nn) {
+        const int c = GATEUP ? nn * 128 + 32 * wn + l32 : 64 * wn + 32 * nn + l32;
+        const uint2 q = *(const uint2*)(Bq + c * 16 + ((lh ^ ((c >> 4) & 1)) * 8));
+        const float sc = __uint_as_float(Bq[4096 + c] ? ((uint32_t)Bq[4096 + c] << 23) : 0x00400000u);
+        fb[0][nn] = fp4x8_to_bf16(q.x, sc);
+        fb[1][nn] = fp4x8_to_bf16(q.y, sc);
+      }
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn) fb[kk][nn] = ld_u32x4(B + bread[nn][kk]);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
+        for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn) fb[kk][nn] = ld_u32x4(B + bread[nn][kk]);
+#pragma unroll
+        for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
+      }
     }
     const bool more = kb + NS - 1 < nkb;
     const int kn = kb + NS - 1, sn = (st + NS - 1) % NS;
@@ -558,17 +619,17 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
         const int q = kk * MW + mt;
-        if (q % EVERY == 0 && q / EVERY < 4) {
+        if (q % EVERY == 0 && q / EVERY < CP) {
           __builtin_amdgcn_sched_barrier(0);
           if (more) issue(kn, sn, q / EVERY);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    if (MW == 1) {  // two MFMA groups: the last two copies go after them
+    if (MW == 1) {  // two MFMA groups: the remaining copies go after them
       __builtin_amdgcn_sched_barrier(0);
       if (more) {
-        issue(kn, sn, 2);
-        issue(kn, sn, 3);
+#pragma unroll
+        for (int p = 2; p < CP; ++p) issue(kn, sn, p);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -578,14 +639,15 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   auto step = [&](int kb, auto S) {
     constexpr int st = decltype(S)::value;
     const int later = nkb - 1 - kb;
-    wait_blocks(later < NS - 2 ? later : NS - 2);
+    if constexpr (FP4) wait_blocks3(later < NS - 2 ? later : NS - 2);
+    else wait_blocks(later < NS - 2 ? later : NS - 2);
     __builtin_amdgcn_s_barrier();
     compute(st, kb);
   };
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) issue(j, j, p);
+    for (int p = 0; p < CP; ++p) issue(j, j, p);
   for (int kb = 0; kb < nkb; kb += NS) {
     step(kb, std::integral_constant<int, 0>{});
     step(kb + 1, std::integral_constant<int, 1>{});
@@ -646,13 +708,13 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   }
 }
 
-template <bool GATEUP, int NS>
+template <bool GATEUP, int NS, bool FP4 = false>
 __device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile& t, uint16_t* smem) {
   switch ((t.rows + 63) >> 6) {  // 64-row steps: tiles per wave
-    case 1: gemm_tile_body<GATEUP, 1, NS>(a, t, smem); break;
-    case 2: gemm_tile_body<GATEUP, 2, NS>(a, t, smem); break;
-    case 3: gemm_tile_body<GATEUP, 3, NS>(a, t, smem); break;
-    default: gemm_tile_body<GATEUP, 4, NS>(a, t, smem); break;
+    case 1: gemm_tile_body<GATEUP, 1, NS, FP4>(a, t, smem); break;
+    case 2: gemm_tile_body<GATEUP, 2, NS, FP4>(a, t, smem); break;
+    case 3: gemm_tile_body<GATEUP, 3, NS, FP4>(a, t, smem); break;
+    default: gemm_tile_body<GATEUP, 4, NS, FP4>(a, t, smem); break;
   }
 }
 
@@ -713,6 +775,38 @@ __global__ __launch_bounds__(512) void grouped_gemm_kernel(ExpertArgs a) {
     gemm_tile_mw<GATEUP, 5>(a, t, smem);
   else
     gemm_tile_mw<GATEUP, 4>(a, t, smem);
+}
+
+// The same GEMM on 4-bit weights: the B stages hold codes and scales (GSTAGE_Q bytes),
+// each lane dequantises its B fragments when it reads them (exact BF16 values), so the
+// MFMAs and their order are the BF16 kernel's.
+template <bool GATEUP>
+__global__ __launch_bounds__(512) void grouped_gemm_fp4_kernel(ExpertArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GSMEM];
+  const int NT = GATEUP ? a.f / 128 : a.d / 256;
+  const int total = a.tile_start[a.E] * NT;
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int R = (total + 7) >> 3;
+  const int L = xcd * R + q;
+  if (q >= R || L >= total) return;
+  const GemmTile t = decode_tile(a, NT, L);
+  if (((GATEUP ? a.d : a.f) / GBK) % 5 == 0)
+    gemm_tile_mw<GATEUP, 5, true>(a, t, smem);
+  else
+    gemm_tile_mw<GATEUP, 4, true>(a, t, smem);
+}
+static_assert(GMAXST * (GSTAGE_A * 2 + GSTAGE_Q) <= GSMEM * 2, "4-bit stages");
+
+hipError_t launch_gateup_gemm_fp4(const ExpertArgs& a, int max_tiles, hipStream_t s) {
+  const unsigned gx = (unsigned)(8 * ((max_tiles * (a.f / 128) + 7) / 8));
+  hipLaunchKernelGGL(grouped_gemm_fp4_kernel<true>, dim3(gx), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemm_fp4(const ExpertArgs& a, int max_tiles, hipStream_t s) {
+  const unsigned gx = (unsigned)(8 * ((max_tiles * (a.d / 256) + 7) / 8));
+  hipLaunchKernelGGL(grouped_gemm_fp4_kernel<false>, dim3(gx), dim3(512), 0, s, a);
+  return hipGetLastError();
 }
 
 // 1-D grid of 8 * ceil(max_tiles * n-tiles / 8) workgroups (see the tile order above)

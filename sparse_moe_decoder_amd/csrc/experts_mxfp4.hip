@@ -159,6 +159,51 @@ hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8
   return hipGetLastError();
 }
 
+// Repack (init only) into the grouped-GEMM layout of experts.hip: per (expert, n-tile of
+// 256 stage columns, 32-wide K block) 4096 bytes of codes (column c at 16 c; the 8-value
+// half h of k-step kk at ((h ^ ((c >> 4) & 1)) * 8 + kk * 4)) and 256 scale bytes. Stage
+// columns: gate/up (gateup = 1) c < 128 gate row 128 nt + c, c >= 128 up row 128 nt + c -
+// 128; down row 256 nt + c. One thread per (expert, n-tile, K block, column).
+__global__ void repack_mxfp4_gemm_kernel(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
+                                         const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
+                                         int gateup, int E, int N, int K, uint8_t* __restrict__ qout,
+                                         uint8_t* __restrict__ sout) {
+  const int64_t NT = gateup ? N / 128 : N / 256, KB = K / 32;
+  const int64_t total = (int64_t)E * NT * KB * 256;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(q % 256);
+    const int64_t blk = q / 256;  // (e, nt, kb)
+    const int64_t kb = blk % KB, r = blk / KB;
+    const int64_t nt = r % NT, e = r / NT;
+    const bool up = gateup && c >= 128;
+    const int64_t row = gateup ? nt * 128 + (c & 127) : nt * 256 + c;
+    const uint8_t* rc = (up ? c1 : c0) + (e * N + row) * (K / 2) + kb * 16;
+    // dword j of the block's 16 code bytes holds K values 8 j .. 8 j + 7 = k-step j / 2, half j % 2
+    const int sw = (c >> 4) & 1;
+    uint32_t dw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[j] = *(const uint32_t*)(rc + 4 * j);
+    uint32_t* dst = (uint32_t*)(qout + blk * 4096 + c * 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) dst[(h ^ sw) * 2 + kk] = dw[kk * 2 + h];
+    sout[blk * 256 + c] = (up ? s1 : s0)[(e * N + row) * (K / 32) + kb];
+  }
+}
+
+hipError_t launch_repack_mxfp4_gemm(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                                    const uint8_t* us, const uint8_t* dq, const uint8_t* ds,
+                                    int E, int f, int d, uint8_t* pqgu, uint8_t* psgu,
+                                    uint8_t* pqd, uint8_t* psd, hipStream_t s) {
+  hipLaunchKernelGGL(repack_mxfp4_gemm_kernel, dim3(16384), dim3(256), 0, s, gq, gs, uq, us, 1, E,
+                     f, d, pqgu, psgu);
+  hipLaunchKernelGGL(repack_mxfp4_gemm_kernel, dim3(16384), dim3(256), 0, s, dq, ds, dq, ds, 0, E,
+                     d, f, pqd, psd);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Gate/up: one workgroup per (active expert, NTW tiles of 16 outputs); the four
 // waves split K into quarters (d/512 quads each) in wave order, each with a ring of

@@ -95,6 +95,11 @@ struct ExpertArgs {
   const uint8_t* sgu = nullptr;  // gate/up scales
   const uint8_t* qd = nullptr;   // down codes
   const uint8_t* sd = nullptr;   // down scales
+  // MXFP4 experts, grouped-GEMM layout (experts.hip); null unless the handle serves T > 128
+  const uint8_t* pqgu = nullptr;
+  const uint8_t* psgu = nullptr;
+  const uint8_t* pqd = nullptr;
+  const uint8_t* psd = nullptr;
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
@@ -108,6 +113,13 @@ hipError_t launch_repack_mxfp4(const uint8_t* gq, const uint8_t* gs, const uint8
                                int f, int d, uint8_t* qgu, uint8_t* sgu, uint8_t* qd, uint8_t* sd,
                                hipStream_t s);
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
+hipError_t launch_gateup_gemm_fp4(const ExpertArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm_fp4(const ExpertArgs& a, int max_tiles, hipStream_t s);
+// row-major codes/scales of gate and up (gateup) or down into the grouped-GEMM layout
+hipError_t launch_repack_mxfp4_gemm(const uint8_t* gq, const uint8_t* gs, const uint8_t* uq,
+                                    const uint8_t* us, const uint8_t* dq, const uint8_t* ds,
+                                    int E, int f, int d, uint8_t* pqgu, uint8_t* psgu,
+                                    uint8_t* pqd, uint8_t* psd, hipStream_t s);
 // Dense SwiGLU layer as one expert taking every token with weight 1: with init, rows
 // 0..max_tokens-1 get the identity order and weight 1; always, the counts, offsets,
 // active list and tile table of a T-token call (one expert, tiles of bm rows)

@@ -121,7 +121,6 @@ def test_product_path_has_no_oracle_or_fallback():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(max_tokens=129), -2),        # beyond the weight-streaming decode range
     (dict(hidden=768), -2),            # hidden % 512 != 0
     (dict(d_ff=2816), -2),             # d_ff % 512 != 0
     (dict(n_groups=7), -1),            # the shared checks still come first

@@ -4,11 +4,12 @@
   normals at many magnitudes and on every rounding decision point with its BF16
   neighbours, signed zeros, subnormals and the largest finite values;
 - an MXFP4 layer against a BF16 layer built from the oracle's dequantised weights,
-  bit for bit (the 4-bit kernels run the BF16 decode kernels' arithmetic on exactly
-  those values), at T = 1, 8 and 40 (both down-pass kinds), computed and replayed
-  routing, and the fused boundary entry points;
+  bit for bit (the 4-bit kernels run the BF16 kernels' arithmetic on exactly those
+  values), at T = 1, 8 and 40 (both weight-streaming down passes) and 129, 300 and 2048
+  (the grouped GEMMs, up to 512 rows per expert: every tile height), computed and
+  replayed routing, and the fused boundary entry points;
 - end to end against the oracle (MoE on the oracle's z; routing exact), at a small
-  shape (d 512, 32 experts, d_ff 512) and at Beam's decode shapes.
+  shape (d 512, 32 experts, d_ff 512), at Beam's decode shapes and at 4096 tokens.
 """
 import dataclasses
 import os
@@ -103,7 +104,7 @@ def layer():
     stack = lambda m, i: np.stack([q[e][m][i] for e in range(WL.E)])  # noqa: E731
     fp4 = tuple(P.to_dev(stack(m, i)) for m in range(3) for i in range(2))
     W, b = sd.router(WL)
-    cfg = sd.moe_config(WL, max_tokens=64)
+    cfg = sd.moe_config(WL, max_tokens=2048)
     d = dict(deq=deq)
     d["wpost"], d["wpre"] = sd.norm_weights(WL)
     d["moe4"] = beam.BeamMoE(cfg, W, b, None, None, None, mxfp4=fp4)
@@ -115,7 +116,7 @@ def layer():
     d["moe_deq"].close()
 
 
-@pytest.mark.parametrize("T", [1, 8, 40])
+@pytest.mark.parametrize("T", [1, 8, 40, 129, 300, 2048])
 def test_mxfp4_equals_bf16_on_dequantised(layer, T):
     import torch
     from synth import device as sd
@@ -225,3 +226,42 @@ def test_mxfp4_beam_decode(beam4, T, sample):
                                   threads=THREADS)
     keep = same[:sample]
     P.assert_bf16_close(P.bits(y)[:sample][keep], y_ref[keep], f"mxfp4 beam T={T} y")
+
+
+def test_mxfp4_beam_prefill_sampled(beam4):
+    """Beam shapes at 4096 tokens (the 4-bit grouped GEMMs): routing for every token
+    against the oracle, the permutation's invariants, and the MoE output of sampled
+    tokens against the oracle (which quantises their experts itself)."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from concurrent.futures import ThreadPoolExecutor
+    from synth import device as sd
+    T = 4096
+    wl = BEAM.with_tokens(T)
+    W, b = sd.router(BEAM)
+    moe = beam.BeamMoE(sd.moe_config(BEAM, max_tokens=T), W, b, None, None, None,
+                       mxfp4=tuple(beam4["codes"]))
+    hh = synth.token_rows(wl, range(T), "h")
+    xx = synth.token_rows(wl, range(T), "x")
+    _, z = oracle.boundary(hh, xx, synth.norm_weight(wl, "post"), synth.norm_weight(wl, "pre"),
+                           wl.n, wl.eps)
+    logits = oracle.router_threaded(z, synth.router_weight(wl), THREADS)
+    ids, w, ggap, egap = oracle.topk(logits, synth.router_bias(wl), wl.G, wl.kg, wl.k, wl.scale)
+    y, r = moe.forward(P.to_dev(z), want_routing=True)
+    torch.cuda.synchronize()
+    g_ids = r["ids_out"].cpu().numpy()
+    same, _ = P.check_routing(g_ids, r["w_out"].cpu().numpy(), ids, w, ggap, egap,
+                              r["logits_out"].cpu().numpy(), logits, "mxfp4 beam T=4096")
+    P.check_permutation_valid(g_ids, r["perm_out"].cpu().numpy(), r["offsets_out"].cpu().numpy(),
+                              wl.E)
+    rows = [0, 1, 1000, 2047, 2048, 4095]
+    need = sorted(set(int(e) for e in ids[rows].ravel()))
+    print(f"[mxfp4] prefill: oracle quantises {len(need)} Beam experts", flush=True)
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(lambda e: quantised_experts(wl, [e]), need))
+    deq = {e: p[1][e] for e, p in zip(need, parts)}
+    y_ref, _ = oracle.moe_experts(z[rows], ids[rows], w[rows], wl.E, deq.__getitem__,
+                                  threads=THREADS)
+    keep = same[rows]
+    P.assert_bf16_close(P.bits(y)[rows][keep], y_ref[keep], "mxfp4 beam T=4096 y (sampled)")
+    moe.close()
