@@ -110,6 +110,7 @@ struct beam_moe_ctx {
   uint8_t* psgu = nullptr;
   uint8_t* pqd = nullptr;
   uint8_t* psd = nullptr;
+  float* dense_part = nullptr;  // dense layers: FP32 partials of the split-K down pass [4][16][d]
   // workspace (owned), sized for max_tokens
   float* logits = nullptr;     // [maxT, E]
   int32_t* ids = nullptr;      // [maxT, k]
@@ -470,7 +471,9 @@ int beam_dense_init(int32_t hidden, int32_t d_ff, int32_t max_tokens, const uint
   return init_handle(&cfg, nullptr, nullptr, stream, out, [&](beam_moe_ctx* h, hipStream_t s) -> int {
     const size_t d = hidden, f = d_ff;
     h->dense = true;
-    if (!dev_alloc(h, &h->wgu, 2 * f * d) || !dev_alloc(h, &h->wdp, d * f)) return BEAM_ERR_OOM;
+    if (!dev_alloc(h, &h->wgu, 2 * f * d) || !dev_alloc(h, &h->wdp, d * f) ||
+        !dev_alloc(h, &h->dense_part, (size_t)kDenseSplitK * 16 * d))
+      return BEAM_ERR_OOM;
     if (launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, 1, (int)f, (int)d, s) != hipSuccess)
       return BEAM_ERR_HIP;
     PermArgs pa{max_tokens, 1, 1, kGemmBM, nullptr, h->counts, h->offsets, h->perm, nullptr,
@@ -504,6 +507,8 @@ int beam_dense_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t
       if (launch_gateup_stream(ea, 1, s) != hipSuccess) return BEAM_ERR_HIP;
     }
     ProfScope ps(K_DOWN, s);
+    if (T <= kSplitDownMaxT && (c.d_ff / 32) % (4 * kDenseSplitK) == 0)
+      return hip_status(launch_down_splitk_dense(ea, kDenseSplitK, h->dense_part, s));
     return hip_status(T <= kSplitDownMaxT ? launch_down_split(ea, 1, s) : launch_down_stream(ea, 1, s));
   }
   const int max_tiles = (T + kGemmBM - 1) / kGemmBM + 1;

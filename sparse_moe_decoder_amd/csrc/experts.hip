@@ -342,6 +342,91 @@ __global__ __launch_bounds__(256) void down_split_kernel(ExpertArgs a) {
   }
 }
 
+// Down projection of a dense layer (one expert) for up to 16 tokens: the expert alone
+// gives only d/16 column tiles, too few workgroups for the chip, so K (f) is also split
+// across P workgroups per tile. Workgroup (tile nt, part p) covers K values
+// [p f/P, (p+1) f/P), its four waves a quarter of that each (summed in wave order), and
+// writes FP32 partial sums part[p][row][col]; dense_finish_kernel adds the P parts in order
+// and rounds once.
+template <int U>
+__global__ __launch_bounds__(256) void down_splitk_kernel(ExpertArgs a, int P, float* __restrict__ part) {
+  const int ND = a.d / 16;
+  const int nt = blockIdx.x % ND, pk = blockIdx.x / ND;
+  const int cnt = a.T;  // one expert, rows in token order
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KS = a.f / 32, ksp = KS / P, ksw = ksp / 4, ks0 = pk * ksp + wv * ksw;
+  const uint16_t* bp = a.wdp + (int64_t)nt * KS * 512 + (int64_t)ks0 * 512 + lane * 8;
+  const uint32_t abytes = (uint32_t)a.T * a.f * 2;
+  __shared__ f32x4 red[3][64];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r = lane & 15;
+  const uint32_t xo = r < cnt ? 2u * (uint32_t)(r * a.f + ks0 * 32 + 8 * (lane >> 4)) : abytes;
+  u32x4 b[U], x[U];
+  auto load = [&](int u, int ks) {
+    b[u] = ld_stream_u32x4(bp + (int64_t)ks * 512);
+    x[u] = xo < abytes ? ld_u32x4((const char*)a.act + xo + ks * 64) : u32x4{0u, 0u, 0u, 0u};
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int ks = 0; ks < ksw - U; ks += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc = mfma16(x[u], b[u], acc);
+      load(u, ks + U + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc = mfma16(x[u], b[u], acc);
+  if (wv > 0) red[wv - 1][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    f32x4 v = acc;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) v += red[w][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (lane >> 4) + i;
+      if (row < cnt) part[((int64_t)pk * 16 + row) * a.d + nt * 16 + (lane & 15)] = v[i];
+    }
+  }
+}
+
+// y[t][o] = bf16(w[t] * (((part[0] + part[1]) + ...) + part[P-1])), one output per thread
+__global__ __launch_bounds__(256) void dense_finish_kernel(int T, int d, int P, const float* __restrict__ part,
+                                                           const float* __restrict__ w,
+                                                           uint16_t* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * d) return;
+  const int t = i / d, o = i % d;
+  float v = part[(int64_t)t * d + o];
+  for (int p = 1; p < P; ++p) v += part[((int64_t)p * 16 + t) * d + o];
+  y[i] = f2bf(w[t] * v);
+}
+
+hipError_t launch_down_splitk_dense(const ExpertArgs& a, int P, float* part, hipStream_t s) {
+  const int ksw = a.f / 32 / P / 4;
+  dim3 g((unsigned)((a.d / 16) * P)), blk(256);
+  if (ksw % 10 == 0)
+    hipLaunchKernelGGL((down_splitk_kernel<10>), g, blk, 0, s, a, P, part);
+  else if (ksw % 8 == 0)
+    hipLaunchKernelGGL((down_splitk_kernel<8>), g, blk, 0, s, a, P, part);
+  else if (ksw % 4 == 0)
+    hipLaunchKernelGGL((down_splitk_kernel<4>), g, blk, 0, s, a, P, part);
+  else if (ksw % 2 == 0)
+    hipLaunchKernelGGL((down_splitk_kernel<2>), g, blk, 0, s, a, P, part);
+  else
+    hipLaunchKernelGGL((down_splitk_kernel<1>), g, blk, 0, s, a, P, part);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const int n = a.T * a.d;
+  hipLaunchKernelGGL(dense_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.T,
+                     a.d, P, (const float*)part, a.w, a.yk);
+  return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_gateup_stream_mt(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int ksw = a.d / 32 / 4;

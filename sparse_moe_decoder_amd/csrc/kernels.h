@@ -9,6 +9,7 @@ constexpr int kPermChunk = 1024;  // slots per permutation block (256 threads x 
 constexpr int kGemmBM = 256;      // rows per grouped-GEMM tile
 constexpr int kStreamMaxT = 128;  // largest T served by the weight-streaming expert path
 constexpr int kSplitDownMaxT = 16;  // largest T whose down pass splits K over four waves
+constexpr int kDenseSplitK = 4;     // dense layers, T <= 16: workgroups per down column tile
 constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
 constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
 constexpr int kBoundaryWgMaxD = 8192;   // boundary rows up to this width: a workgroup per row
@@ -123,6 +124,10 @@ hipError_t launch_repack_mxfp4_gemm(const uint8_t* gq, const uint8_t* gs, const 
 // Dense SwiGLU layer as one expert taking every token with weight 1: with init, rows
 // 0..max_tokens-1 get the identity order and weight 1; always, the counts, offsets,
 // active list and tile table of a T-token call (one expert, tiles of bm rows)
+// dense layer down pass for T <= 16 with K split over P workgroups per column tile
+// (FP32 partials in part [P][16][d], then the finishing pass writes a.yk = y);
+// needs (f / 32) % (4 P) == 0
+hipError_t launch_down_splitk_dense(const ExpertArgs& a, int P, float* part, hipStream_t s);
 hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a, float* w,
                              hipStream_t s);
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
