@@ -273,7 +273,9 @@ def main():
 
     # roofline of the dominant kernel (expert gate/up)
     gu_us = kernel_us.get("gate_up")
-    src = source_hash("experts_mxfp4.hip" if mx else "experts.hip", "common.h")
+    # the sources of the gate/up kernels (4-bit: streams in experts_mxfp4.hip, GEMM in experts.hip)
+    src = source_hash(*(("experts.hip", "experts_mxfp4.hip", "common.h") if mx
+                        else ("experts.hip", "common.h")))
     wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
     if decode:
         # algorithmic bytes per launch: each touched expert's gate+up weights once, the
