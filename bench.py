@@ -257,6 +257,21 @@ def main():
             log(f"graph capture unavailable: {exc!r}")
             ms_graph = None
 
+    # per-step spread: events around each eager step (a separate pass; the value above is
+    # the whole timed region divided by the step count)
+    per = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(steps, 200))]
+    torch.cuda.synchronize()
+    for i, (a, b_) in enumerate(ev):
+        a.record()
+        step(i)
+        b_.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b_) for a, b_ in ev)
+    pct = {f"p{q}": round(float(np.percentile(per, q)), 5) for q in (10, 50, 90)}
+    log(f"per-step ms: {pct}")
+
     # 3) per-kernel durations from HIP events around each launch, over a timed region
     beam.profile_reset()
     beam.profile_enable(True)
@@ -326,6 +341,7 @@ def main():
             "step": args.step, "mode": mode, "ms_eager": round(ms_eager, 5),
             "ms_graph": None if ms_graph is None else round(ms_graph, 5),
             "ms_profiled": round(ms_prof, 5),
+            "ms_per_step_eager_percentiles": pct,
             "kernel_us": {k: (None if v is None else round(v, 2)) for k, v in kernel_us.items()},
             "whole_step": whole,
         },
