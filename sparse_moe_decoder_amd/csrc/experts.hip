@@ -23,6 +23,7 @@
 #include "kernels.h"
 #include "combine_device.h"
 #include "expert_device.h"
+#include "mxfp4_device.h"
 
 #include <type_traits>
 
@@ -542,15 +543,6 @@ __device__ __forceinline__ void wait_blocks3(int n) {
 // output 128 nb + c, c >= 128 up output 128 nb + c - 128; down output 256 nb + c.
 constexpr int GSTAGE_Q = 4096 + 256;  // bytes per 4-bit B stage
 
-__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
-  return r;
-}
-
 struct GemmTile {
   int e, row0, rows, nb;
 };
@@ -677,7 +669,7 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
       for (int nn = 0; nn < 2; ++nn) {
         const int c = GATEUP ? nn * 128 + 32 * wn + l32 : 64 * wn + 32 * nn + l32;
         const uint2 q = *(const uint2*)(Bq + c * 16 + ((lh ^ ((c >> 4) & 1)) * 8));
-        const float sc = __uint_as_float(Bq[4096 + c] ? ((uint32_t)Bq[4096 + c] << 23) : 0x00400000u);
+        const float sc = e8m0_scale(Bq[4096 + c]);
         fb[0][nn] = fp4x8_to_bf16(q.x, sc);
         fb[1][nn] = fp4x8_to_bf16(q.y, sc);
       }

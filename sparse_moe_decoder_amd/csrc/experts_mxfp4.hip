@@ -25,27 +25,9 @@
 #include "common.h"
 #include "kernels.h"
 #include "expert_device.h"
+#include "mxfp4_device.h"
 
 namespace beam {
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// 2^(s - 127) as an FP32 multiplier (s = 0 is 2^-127, a subnormal; s = 255, the
-// E8M0 NaN, is never produced by the quantiser)
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-  return __uint_as_float(s ? (s << 23) : 0x00400000u);
-}
-
-// Eight codes (one dword) times the scale: the BF16 operand fragment, element i in
-// half-word i
-__device__ __forceinline__ u32x4 fp4x8_bf16(uint32_t codes, float scale) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
-  return r;
-}
 
 __device__ __forceinline__ uint32_t ld_stream_u32(const void* p) {
   return __builtin_nontemporal_load((const uint32_t*)p);
@@ -268,8 +250,8 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          const u32x4 bg = fp4x8_bf16(cg[u][t][s], e8m0_scale((sg[u][t] >> (8 * s)) & 255u));
-          const u32x4 bu = fp4x8_bf16(cu[u][t][s], e8m0_scale((su[u][t] >> (8 * s)) & 255u));
+          const u32x4 bg = fp4x8_to_bf16(cg[u][t][s], e8m0_scale((sg[u][t] >> (8 * s)) & 255u));
+          const u32x4 bu = fp4x8_to_bf16(cu[u][t][s], e8m0_scale((su[u][t] >> (8 * s)) & 255u));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             ag[t][mt] = mfma16(x[mt][u][s], bg, ag[t][mt]);
@@ -380,7 +362,7 @@ __global__ __launch_bounds__(256) void down_split_fp4_kernel(ExpertArgs a) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
-          acc[t] = mfma16(x[u][s], fp4x8_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u)),
+          acc[t] = mfma16(x[u][s], fp4x8_to_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u)),
                           acc[t]);
     };
 #pragma unroll
@@ -469,7 +451,7 @@ __global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          const u32x4 b = fp4x8_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u));
+          const u32x4 b = fp4x8_to_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16(x[mt][u][s], b, acc[t][mt]);
         }
