@@ -32,7 +32,10 @@ namespace beam {
 // Direct global-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
 // address lds + 16 l (lds must be wave-uniform). Issued as inline assembly so the
 // compiler does not add its own conservative waits on the stage buffers; the
-// kernel waits explicitly (vmcnt) before a stage is read.
+// kernel waits explicitly (vmcnt) before a stage is read. The asm sets m0 (the LDS
+// base of the copy) and lists it as clobbered; the compiler warns that it does not
+// save m0 around the asm, which is safe here because on gfx950 these kernels hold
+// no value in m0 (LDS reads and writes do not use it; nothing else here does).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

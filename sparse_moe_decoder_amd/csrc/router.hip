@@ -132,6 +132,8 @@ static_assert(RMAXST * (RSTAGE_A + RSTAGE_B) * 2 <= 160 * 1024, "LDS");
 __device__ __forceinline__ uint32_t lds_addr_r(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// Direct global-to-LDS 16-byte copy per lane (to lds + 16 lane), as in the expert GEMM:
+// inline assembly that sets m0 itself; the kernel holds no value in m0.
 __device__ __forceinline__ void lds_dma16_r(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
