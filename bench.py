@@ -114,7 +114,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
               "no multi-GPU path; the per-GPU kernels are what one GPU shows.", file=sys.stderr)
         sys.exit(2)
     import numpy as np

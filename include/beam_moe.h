@@ -41,7 +41,7 @@ extern "C" {
 enum {
   BEAM_OK = 0,
   BEAM_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad scalar */
-  BEAM_ERR_UNSUPPORTED = -2, /* a shape this build does not implement */
+  BEAM_ERR_UNSUPPORTED = -2, /* a shape the library does not implement */
   BEAM_ERR_OOM = -3,         /* device allocation failed (init only) */
   BEAM_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
   BEAM_ERR_CAPACITY = -5     /* T larger than the handle's max_tokens */
