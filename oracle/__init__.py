@@ -8,9 +8,11 @@ marshalling. It shares no code with the GPU library and imports nothing from it.
 BF16 tensors are numpy ``uint16`` arrays holding the bit patterns.
 
 Parity status of each step (how it is pinned is listed in ``tests/test_oracle_pins.py``):
-  O1 boundary ........ pinned (closed forms, n = 1 identity, unit-variance invariant)
+  O1 boundary ........ pinned (closed forms, n = 1 identity, unit-variance invariant; the
+                        BF16 post-norm output on rows with an exact norm factor)
   O2 router .......... pinned (one-hot rows, exact small-integer sums, FP64 error bound)
-  O3 grouped top-k ... pinned (brute-force enumeration, forced ties, sum of weights)
+  O3 grouped top-k ... pinned (brute-force enumeration, forced ties, sum of weights; the
+                        sigmoid equals the FP32 rounding of a 50-digit evaluation)
   O4 permutation ..... pinned (brute-force sort of (expert, slot) pairs)
   O5/O6 experts ...... pinned (permutation-matrix closed forms, one-expert dense SwiGLU x 2.5,
                         all-experts dense mixture, FP64 error bound)

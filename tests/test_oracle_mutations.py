@@ -41,6 +41,18 @@ MUTATIONS = [
     ("mx no clamp of tiny scales", "if (X < -127) X = -127;", ""),
     ("combine rounds each add", "acc = acc + oracle_f32(yk[(t * k + j) * d + o]);",
      "acc = oracle_f32(oracle_bf16(acc + oracle_f32(yk[(t * k + j) * d + o])));"),
+    ("sigmoid in FP32", "(float)(1.0 / (1.0 + exp(-(double)logit)))",
+     "1.0f / (1.0f + expf(-logit))"),
+    # the branch scaled from the unrounded post-norm output (norm factor recomputed per row)
+    ("post-norm output not rounded", [
+        ("rmsnorm_row(d, xr, w_post, eps, xn); /* post-norm of the branch, rounded */",
+         "rmsnorm_row(d, xr, w_post, eps, xn); /* post-norm of the branch, rounded */\n"
+         "    float rr_ = 0.0f;\n"
+         "    for (int64_t q = 0; q < d; ++q) rr_ = rr_ + oracle_f32(xr[q]) * oracle_f32(xr[q]);\n"
+         "    rr_ = 1.0f / sqrtf(rr_ / (float)d + eps);"),
+        ("uint16_t b = oracle_bf16(c2 * oracle_f32(xn[i]));",
+         "uint16_t b = oracle_bf16(c2 * ((oracle_f32(xr[i]) * rr_) * oracle_f32(w_post[i])));"),
+    ]),
 ]
 
 PIN_TESTS = [(name, fn) for name, fn in inspect.getmembers(pins, inspect.isfunction)
@@ -63,11 +75,19 @@ def _run_pins(golden):
     return failed
 
 
-@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_mutation(label, old, new, tmp_path, golden):
+def _edits(m):
+    """A mutation is (label, old, new) or (label, [(old, new), ...])."""
+    return m[1] if len(m) == 2 else [(m[1], m[2])]
+
+
+@pytest.mark.parametrize("label,edits", [(m[0], _edits(m)) for m in MUTATIONS],
+                         ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(label, edits, tmp_path, golden):
     src = open(oracle.SRC_PATH).read()
-    assert src.count(old) >= 1, label
-    mutated = src.replace(old, new)
+    mutated = src
+    for old, new in edits:
+        assert mutated.count(old) >= 1, label
+        mutated = mutated.replace(old, new)
     c_path = tmp_path / "mut.c"
     c_path.write_text(mutated)
     hdr = os.path.join(os.path.dirname(oracle.SRC_PATH), "beam_oracle.h")

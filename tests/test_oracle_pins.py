@@ -52,6 +52,41 @@ def test_sigmoid_golden(golden):
         assert abs(s - case["score"]) <= case["ulps"] * ulp + 0.0, case
 
 
+def _f32_nearest(v):
+    """The FP32 number nearest to the Decimal v (ties to even): the double nearest to v,
+    narrowed, then its FP32 neighbours compared with v exactly."""
+    from decimal import Decimal
+    f = np.float32(float(v))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    errs = [abs(Decimal(float(c)) - v) for c in cands]
+    best = min(errs)
+    picks = [c for c, e in zip(cands, errs) if e == best]
+    if len(picks) > 1:  # a tie: the even significand
+        picks = [c for c in picks if (int(np.float32(c).view(np.uint32)) & 1) == 0]
+    return picks[0]
+
+
+def test_sigmoid_correctly_rounded():
+    """Scores are sigmoid(logit) in FP32 ([vLLM page, MoE und Residual-Stream]; reading:
+    the FP32 value nearest to the exact sigmoid). Checked against 1 / (1 + e^-v) evaluated
+    with 50 significant digits (Python's decimal module) and rounded to the nearest FP32
+    number, over logits spanning the router's range and the saturating tails."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    rng = np.random.default_rng(43)
+    xs = np.concatenate([rng.standard_normal(2500) * 2.0, rng.uniform(-20.0, 20.0, 1000),
+                         np.array([-88.0, -30.0, -17.5, -1e-6, 1e-6, 15.9, 17.0, 40.0])])
+    xs = xs.astype(np.float32)
+    bad = []
+    for v in xs:
+        exact = Decimal(1) / (Decimal(1) + (-Decimal(float(v))).exp())
+        want = _f32_nearest(exact)
+        got = np.float32(oracle.sigmoid(v))
+        if got != want:
+            bad.append((float(v), float(got), float(want)))
+    assert not bad, bad[:5]
+
+
 def test_sigmoid_symmetry_and_range():
     xs = np.linspace(-30, 30, 2001, dtype=np.float32)
     s = np.array([oracle.sigmoid(v) for v in xs])
@@ -499,6 +534,39 @@ def test_boundary_operands_rounded_before_add():
     h = cand[pick[:d]].reshape(1, d)
     hp, _ = oracle.boundary(h, x, ones, ones, n, 0.0)
     assert np.array_equal(F(hp[0]), rounded[pick[:d]])
+
+
+def power_of_four_rows(T, seed):
+    """Branch rows of 64 small odd integers (twenty 5s, thirty 3s, nine 1s, five 7s, random
+    signs and order) whose squares sum to 1024 = 64 * 16: the mean square is exactly 16 in
+    any summation order, so with eps = 0 the RMSNorm factor is exactly 1/4, and each
+    x * (1/4) * w (at most 3 + 8 significant bits) is exact in FP32 but usually not a
+    BF16 number."""
+    base = np.array([5.0] * 20 + [3.0] * 30 + [1.0] * 9 + [7.0] * 5, np.float32)
+    assert float(np.sum(base.astype(np.float64) ** 2)) == 1024.0
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.permutation(base) * rng.choice([-1.0, 1.0], 64) for _ in range(T)])
+    return to_bf16(rows.astype(np.float32))
+
+
+def test_boundary_postnorm_output_rounded(golden):
+    """[SGLang, sandwich norm section] the unfused boundary writes the post-normed branch
+    and reads it back for the residual: the post-norm output is a BF16 tensor before it is
+    scaled by 1/sqrt(n). On rows with an exact norm factor (h = 0, eps = 0) the result is
+    h' = bf16(c2 * bf16(x * w / 4)); scaling the unrounded x * w / 4 instead gives a
+    different h' on some elements, which this case checks it has."""
+    d, n = 64, 20
+    c2 = np.float32([c["c2"] for c in golden["depth_scaled_residual"]["cases"]
+                     if c["n"] == n][0])
+    x = power_of_four_rows(8, 41)
+    w_post = to_bf16(np.random.default_rng(42).uniform(0.9, 1.1, d))
+    ones = to_bf16(np.ones(d))
+    xn = (F(x) * np.float32(0.25)) * F(w_post)  # exact in FP32
+    with_r1 = F(to_bf16(c2 * F(to_bf16(xn))))
+    without_r1 = F(to_bf16(c2 * xn))
+    assert np.count_nonzero(with_r1 != without_r1) >= 16  # the case can tell them apart
+    hp, _ = oracle.boundary(np.zeros_like(x), x, w_post, ones, n, 0.0)
+    assert np.array_equal(F(hp), with_r1)
 
 
 def test_expert_weight_applied_before_rounding():
