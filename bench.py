@@ -1,4 +1,4 @@
-"""Benchmark: one Beam MoE sublayer step (fused boundary + routed MoE FFN) on one MI355X.
+"""Benchmark: the Beam MoE sublayer (routed MoE FFN + one sublayer boundary) on one MI355X.
 
 A step is one pass of the whole path over one batch of T tokens: the MoE FFN
 (FP32 router, grouped top-k, expert grouping, BF16 SwiGLU experts, weighted
@@ -6,9 +6,17 @@ combine) and one sublayer boundary (post-norm, depth-scaled residual, pre-norm).
 By default (--step boundary-last) it is beam_moe_forward_boundary: the MoE on z,
 then the next sublayer's boundary fused into the combine, as a decode loop runs
 it; --step boundary-first times beam_sublayer_forward (the boundary, then the MoE
-on its z). Both are bit-identical to the separate calls. Inputs are seeded synthetic tensors already resident
-in HBM when the timed region starts; decode steps rotate over distinct token sets
-so the experts touched change from step to step.
+on its z). Both are bit-identical to the separate calls. Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts; decode
+steps rotate over distinct token sets so the experts touched change from step to
+step.
+
+Without --workload the run measures every configuration of the metric in one
+process — batch-1 decode (the headline `value`), decode batches of 32 and 128,
+the 8 x 2048-token prefill and the skewed 32K-token prefill — on two layer
+handles (the uniform and the skewed router bias) built once from the same
+weights; each gets an entry under config.workloads. --workload X measures X
+alone (what the rocprofv3 traces run).
 
 Prints one JSON line. `value` is tokens per second for the whole job;
 `roofline` reports the dominant kernel (expert gate/up) against HBM (decode) or
@@ -32,6 +40,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 matrix cores
 METRIC = "MoE-layer tokens/s (decode T=1/32/128, prefill 16K) + % HBM/MFMA peak"
+SUITE = ("decode1", "decode32", "decode128", "prefill16k", "skew32k")
 
 
 def parse():
@@ -39,11 +48,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="decode1",
+    p.add_argument("--workload", default=None,
                    choices=["decode1", "decode32", "decode128", "prefill16k", "skew32k",
                             "skew32k_half", "tiny", "dense1", "dense16k"],
-                   help="dense1 / dense16k: Beam's dense SwiGLU layer (d_ff 20480) instead of "
-                        "the MoE; a step is that layer, then the next boundary on its output")
+                   help="measure one workload only (default: every configuration of the "
+                        "metric). dense1 / dense16k: Beam's dense SwiGLU layer (d_ff 20480) "
+                        "instead of the MoE; a step is that layer, then the next boundary")
     p.add_argument("--rotations", type=int, default=None, help="distinct token sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
@@ -108,72 +118,51 @@ def read_traffic(kernel: str, workload: str, src_hash: str):
         return None
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
-              "no multi-GPU path; the per-GPU kernels are what one GPU shows.", file=sys.stderr)
-        sys.exit(2)
+class GraphMismatch(RuntimeError):
+    pass
+
+
+def timed(step, n):
+    """Mean ms per call of step(i), i < n, between two events on the current stream."""
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def measure(wl, moe, dense_h, args, mx):
+    """Time one workload on an existing handle; returns its entry (dict)."""
     import numpy as np
     import torch
 
-    import synth
-    from synth import device as sd
     import sparse_moe_decoder_amd as beam
+    from synth import device as sd
 
-    wl = synth.WORKLOADS[args.workload]
     T = wl.T
     decode = T <= 128
+    dense = dense_h is not None
     steps = args.steps or (200 if decode else 10)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
     R = args.rotations or (32 if decode else 1)
-    torch.cuda.set_device(0)
-    dev = torch.cuda.current_device()
     log(f"workload {wl.name}: T={T} d={wl.d} E={wl.E} f={wl.f}; steps {steps} warmup {warmup} "
         f"rotations {R}")
-
-    t0 = time.time()
     wpost, wpre = sd.norm_weights(wl)
-    W, b = sd.router(wl)
-    wg, wu, wd = sd.experts(wl)
-    mx = args.experts == "mxfp4"
-    dense = wl.name.startswith("dense")
-    if mx and dense:
-        print("--experts mxfp4 applies to the MoE workloads", file=sys.stderr)
-        sys.exit(2)
-    if dense:
-        moe = None
-        dense_h = beam.beam_dense_init(wl.d, wl.f, T, wg[0], wu[0], wd[0])
-    elif mx:
-        fp4 = []
-        for t in (wg, wu, wd):
-            fp4 += list(beam.beam_mxfp4_quantize(t))
-        moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, None, None, None,
-                           mxfp4=tuple(fp4))
-        del fp4
-    else:
-        moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=T), W, b, wg, wu, wd)
-    del wg, wu, wd
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
     hs = [sd.tokens(wl, "h", token_set=s) for s in range(R)]
     xs = [sd.tokens(wl, "x", token_set=s) for s in range(R)]
     h_out = torch.empty((T, wl.d), dtype=torch.bfloat16, device="cuda")
     z = torch.empty_like(h_out)
     y = torch.empty_like(h_out)
-    torch.cuda.synchronize()
-    log(f"setup {time.time() - t0:.1f}s")
+    # each token set's z from its boundary, before the timed region
+    z_in = [beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps)[1]
+            for s in range(R)]
 
     if dense:
-        # each token set's z from its boundary, before the timed region; a step is the dense
-        # layer on it, then the next boundary with its output as the branch
-        z_in = [beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps)[1]
-                for s in range(R)]
-
-        def step(i):
+        def step(i):  # the dense layer, then the next boundary with its output as the branch
             s = i % R
             beam.beam_dense_forward(dense_h, z_in[s], y)
             beam.beam_sublayer_norm_residual(hs[s], y, wpost, wpre, wl.n, wl.eps, h_out=h_out,
@@ -184,52 +173,40 @@ def main():
             beam.beam_sublayer_forward(moe.handle, hs[s], xs[s], wpost, wpre, wl.n, wl.eps, y,
                                        h_out=h_out, z_out=z)
     else:
-        # each token set's z from its boundary, before the timed region; a step is the MoE on
-        # it and the next boundary (x = the MoE output), whose outputs are h_out and z
-        z_in = []
-        for s in range(R):
-            z_in.append(beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n,
-                                                         wl.eps)[1])
-
-        def step(i):
+        def step(i):  # the MoE on z, then the next boundary (x = the MoE output)
             s = i % R
             beam.beam_moe_forward_boundary(moe.handle, z_in[s], hs[s], wpost, wpre, wl.n, wl.eps,
                                            h_out=h_out, z_out=z)
+    last_out = y if (args.step == "boundary-first" and not dense) else z
 
-    # distinct experts per token set (for the algorithmic byte count)
-    distinct = []
-    ids_buf = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
-    w_buf = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
-    for s in range(R if not dense else 0):
-        beam.beam_sublayer_norm_residual(hs[s], xs[s], wpost, wpre, wl.n, wl.eps, h_out=h_out,
-                                         z_out=z)
-        beam.beam_router_topk(moe.handle, z, ids_buf, w_buf)
-        distinct.append(len(np.unique(ids_buf.cpu().numpy())))
-    if dense:
-        distinct = [1]
+    # distinct experts per token set (for the algorithmic byte count) and rows per expert
+    distinct, max_rows, hot_share = [1], None, None
+    if not dense:
+        distinct = []
+        ids_buf = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+        w_buf = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+        for s in range(R):
+            beam.beam_router_topk(moe.handle, z_in[s], ids_buf, w_buf)
+            ids_np = ids_buf.cpu().numpy()
+            distinct.append(len(np.unique(ids_np)))
+        counts = np.bincount(ids_np.ravel(), minlength=wl.E)
+        max_rows = int(counts.max())
+        if wl.hot_experts:
+            hot_share = round(float(counts[list(wl.hot_experts)].sum() / counts.sum()), 4)
     mean_distinct = float(np.mean(distinct))
-
-    def timed(fn, n):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
 
     # 1) eager
     for i in range(warmup):
         step(i)
     ms_eager = timed(step, steps)
-    log(f"eager: {ms_eager * 1e3:.1f} us/step")
+    log(f"{wl.name} eager: {ms_eager * 1e3:.1f} us/step")
 
-    # 2) HIP graph of one step per token set (no allocation, no host sync inside)
-    ms_graph = None
+    # 2) HIP graph of one step per token set (no allocation, no host sync inside); its
+    # result must equal the eager result bit for bit
+    ms_graph, graph_ok = None, None
     if not args.no_graph:
+        graphs = []
         try:
-            graphs = []
             cs = torch.cuda.Stream()
             cs.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(cs):
@@ -242,24 +219,26 @@ def main():
                 with torch.cuda.graph(g):
                     step(s)
                 graphs.append(g)
+        except Exception as exc:  # capture not available: report the eager number
+            log(f"{wl.name}: graph capture unavailable: {exc!r}")
+            graphs = []
+        if graphs:
             for i in range(warmup):
                 graphs[i % R].replay()
             ms_graph = timed(lambda i: graphs[i % R].replay(), steps)
-            log(f"graph: {ms_graph * 1e3:.1f} us/step")
-            # graph result equals the eager result
+            log(f"{wl.name} graph: {ms_graph * 1e3:.1f} us/step")
             step(0)
-            out = y if (args.step == "boundary-first" and not dense) else z  # last output
-            out_eager = out.clone()
+            torch.cuda.synchronize()
+            out_eager = last_out.clone()
+            last_out.zero_()
             graphs[0].replay()
             torch.cuda.synchronize()
-            assert torch.equal(out.view(torch.int16), out_eager.view(torch.int16)), "graph != eager"
-        except Exception as exc:  # report, fall back to the eager number
-            log(f"graph capture unavailable: {exc!r}")
-            ms_graph = None
+            graph_ok = bool(torch.equal(last_out.view(torch.int16), out_eager.view(torch.int16)))
+            if not graph_ok:
+                raise GraphMismatch(f"{wl.name}: graph replay differs from the eager step")
+            del graphs
 
-    # per-step spread: events around each eager step (a separate pass; the value above is
-    # the whole timed region divided by the step count)
-    per = []
+    # per-step spread: events around each eager step (a separate pass)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(min(steps, 200))]
     torch.cuda.synchronize()
@@ -270,7 +249,6 @@ def main():
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b_) for a, b_ in ev)
     pct = {f"p{q}": round(float(np.percentile(per, q)), 5) for q in (10, 50, 90)}
-    log(f"per-step ms: {pct}")
 
     # 3) per-kernel durations from HIP events around each launch, over a timed region
     beam.profile_reset()
@@ -280,15 +258,13 @@ def main():
     kern = beam.profile_read()
     beam.profile_reset()
     kernel_us = {k: (v[0] / v[1] * 1e3 if v[1] else None) for k, v in kern.items()}
-    log("kernel avg us: " + ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items() if v))
+    log(f"{wl.name} kernel avg us: " + ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items() if v))
 
     best_ms = ms_eager if ms_graph is None else min(ms_eager, ms_graph)
     mode = "hipgraph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"
-    value = T / (best_ms / 1e3)
 
     # roofline of the dominant kernel (expert gate/up)
     gu_us = kernel_us.get("gate_up")
-    # the sources of the gate/up kernels (4-bit: streams in experts_mxfp4.hip, GEMM in experts.hip)
     src = source_hash(*(("experts.hip", "experts_mxfp4.hip", "common.h") if mx
                         else ("experts.hip", "common.h")))
     wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
@@ -298,84 +274,169 @@ def main():
         bytes_gu = mean_distinct * 2 * wl.f * wl.d * wbytes + T * wl.d * 2 + T * wl.k * wl.f * 2
         achieved = bytes_gu / (gu_us * 1e-6) / 1e9
         roof = dict(kernel="gate_up", bound="hbm", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4))
-        traffic = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
-        roof["traffic"] = traffic
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    algorithmic_bytes=round(bytes_gu))
+        roof["traffic"] = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
         step_bytes = (mean_distinct * 3 * wl.f * wl.d * wbytes + (0 if dense else wl.E * wl.d * 4)
                       + T * wl.d * 2 * 6 + T * wl.k * (wl.f * 4 + wl.d * 4))
         whole = dict(algorithmic_bytes=round(step_bytes), hbm_frac=round(
             step_bytes / (best_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
     else:
-        flops_gu = 2.0 * T * wl.k * (2 * wl.f) * wl.d
+        kk = 1 if dense else wl.k
+        flops_gu = 2.0 * T * kk * (2 * wl.f) * wl.d
         achieved = flops_gu / (gu_us * 1e-6) / 1e12
         roof = dict(kernel="gate_up", bound="mfma", achieved=round(achieved, 1),
                     peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4))
-        roof["traffic"] = read_traffic("gate_up", wl.name, src)
-        step_flops = 2.0 * T * wl.k * 3 * wl.f * wl.d
-        whole = dict(expert_flops=step_flops, mfma_frac=round(
-            step_flops / (best_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4))
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), algorithmic_flops=flops_gu)
+        roof["traffic"] = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
+        step_flops = 2.0 * T * kk * 3 * wl.f * wl.d
+        gemm_us = gu_us + (kernel_us.get("down") or 0.0)
+        whole = dict(expert_flops=step_flops,
+                     mfma_frac=round(step_flops / (best_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     expert_gemms_mfma_frac=round(
+                         step_flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4))
+    entry = {
+        "tokens": T, "ms_per_step": round(best_ms, 5), "tokens_per_s": round(T / (best_ms / 1e3), 2),
+        "mode": mode, "ms_eager": round(ms_eager, 5),
+        "ms_graph": None if ms_graph is None else round(ms_graph, 5),
+        "graph_matches_eager": graph_ok, "ms_profiled": round(ms_prof, 5),
+        "ms_per_step_eager_percentiles": pct, "steps": steps, "warmup": warmup,
+        "token_sets": R, "distinct_experts_per_step": round(mean_distinct, 1),
+        "kernel_us": {k: (None if v is None else round(v, 2)) for k, v in kernel_us.items()},
+        "roofline": roof, "whole_step": whole,
+    }
+    if max_rows is not None:
+        entry["max_rows_per_expert"] = max_rows
+    if hot_share is not None:
+        entry["hot_share"] = hot_share
+    del hs, xs, z_in, h_out, z, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return entry
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
+              "no multi-GPU path; the per-GPU kernels are what one GPU shows.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from synth import device as sd
+    import sparse_moe_decoder_amd as beam
+
+    torch.cuda.set_device(0)
+    mx = args.experts == "mxfp4"
+    names = [args.workload] if args.workload else list(SUITE)
+    wls = [synth.WORKLOADS[n] for n in names]
+    dense = names[0].startswith("dense")
+    if mx and dense:
+        print("--experts mxfp4 applies to the MoE workloads", file=sys.stderr)
+        sys.exit(2)
+    head = wls[0]
+    t0 = time.time()
+
+    # one handle per router bias, each sized for the largest batch that uses it
+    W, _ = sd.router(head)
+    wg, wu, wd = sd.experts(head)
+    fp4 = None
+    if mx:
+        fp4 = []
+        for t in (wg, wu, wd):
+            fp4 += list(beam.beam_mxfp4_quantize(t))
+        fp4 = tuple(fp4)
+    handles, dense_h = {}, None
+    if dense:
+        dense_h = beam.beam_dense_init(head.d, head.f, head.T, wg[0], wu[0], wd[0])
+    else:
+        for wl in wls:
+            key = wl.hot_bias if wl.hot_experts else 0.0
+            need = max(w.T for w in wls if (w.hot_bias if w.hot_experts else 0.0) == key)
+            if key in handles:
+                continue
+            _, b = sd.router(wl)
+            cfg = sd.moe_config(wl, max_tokens=need)
+            handles[key] = (beam.BeamMoE(cfg, W, b, None, None, None, mxfp4=fp4) if mx
+                            else beam.BeamMoE(cfg, W, b, wg, wu, wd))
+    del wg, wu, wd, fp4
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"setup {time.time() - t0:.1f}s ({len(handles) or 1} handle(s))")
+
+    entries = {}
+    try:
+        for wl in wls:
+            moe = None if dense else handles[wl.hot_bias if wl.hot_experts else 0.0]
+            entries[wl.name] = measure(wl, moe, dense_h, args, mx)
+    except GraphMismatch as exc:
+        log(f"FAILED: {exc}")
+        sys.exit(3)
+    finally:
+        for h in handles.values():
+            h.close()
+        if dense_h is not None:
+            beam.beam_moe_destroy(dense_h)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_sample, mxfp4=mx)
+        cpu = cpu_baseline(head, args.cpu_sample, mxfp4=mx)
 
+    e = entries[head.name]
+    config = {
+        "workload": head.name, "tokens": head.T, "hidden": head.d, "experts": head.E,
+        "groups": head.G, "groups_kept": head.kg, "topk": head.k, "d_ff": head.f,
+        "experts_format": args.experts, "step": args.step,
+    }
+    config.update({k: v for k, v in e.items() if k != "roofline"})
+    if len(entries) > 1:
+        config["workloads"] = entries
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": e["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(best_ms, 5),
+        "steps": e["steps"],
+        "warmup": e["warmup"],
+        "ms_per_step": e["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if not mx else "bf16 (mxfp4 expert weights)",
         "data": "synthetic (seeded counter-based generator; random-init weights of Beam's MoE layer)",
-        "config": {
-            "workload": wl.name, "tokens": T, "hidden": wl.d, "experts": wl.E,
-            "groups": wl.G, "groups_kept": wl.kg, "topk": wl.k, "d_ff": wl.f,
-            "experts_format": args.experts,
-            "token_sets": R, "distinct_experts_per_step": round(mean_distinct, 1),
-            "step": args.step, "mode": mode, "ms_eager": round(ms_eager, 5),
-            "ms_graph": None if ms_graph is None else round(ms_graph, 5),
-            "ms_profiled": round(ms_prof, 5),
-            "ms_per_step_eager_percentiles": pct,
-            "kernel_us": {k: (None if v is None else round(v, 2)) for k, v in kernel_us.items()},
-            "whole_step": whole,
-        },
-        "roofline": roof,
+        "config": config,
+        "roofline": e["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    if dense:
-        beam.beam_moe_destroy(dense_h)
-    else:
-        moe.close()
 
 
 def cpu_baseline(wl, sample=None, mxfp4=False):
     """The CPU oracle, as it is, on a bounded sample of the same workload: each
     sampled token goes through boundary, router, routing, its experts and the
-    combine, single-threaded per token; tokens run in a thread pool. With mxfp4 the
-    experts' weights are the oracle's MXFP4 quantisation, dequantised (not timed)."""
+    combine, single-threaded per token; tokens run in a thread pool of the machine's CPU
+    share, and a few tokens also run alone on one thread (the single-core figure).
+    With mxfp4 the experts' weights are the oracle's MXFP4 quantisation, dequantised
+    (not timed)."""
     from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
 
     import oracle
     import synth
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    n = sample or (threads if (mxfp4 or wl.name.startswith("dense")) else 2 * threads)
-    rows = list(range(min(n, wl.T))) if wl.T >= n else list(range(wl.T))
+    light = mxfp4 or wl.name.startswith("dense")
+    n = sample or (2 * threads if light else 16 * threads)
+    n1 = max(2, n // (2 * threads))  # tokens timed on one thread
+    rows = list(range(min(n, wl.T)))
+    rot = []
     if len(rows) < n:  # decode: also take tokens of the rotation sets
         extra = n - len(rows)
         rot = [(s, t) for s in range(1, 1 + (extra + wl.T - 1) // wl.T) for t in range(wl.T)]
         rot = rot[:extra]
-    else:
-        rot = []
     hh = [synth.token_rows(wl, [t], "h") for t in rows] + \
          [synth.token_rows(wl, [t], "h", token_set=s) for s, t in rot]
     xx = [synth.token_rows(wl, [t], "x") for t in rows] + \
@@ -385,53 +446,58 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
     if wl.name.startswith("dense"):
         W = synth.expert_weights(wl, 0)
 
-        def one_dense(i):
+        def one(i):
             _, z = oracle.boundary(hh[i], xx[i], wpost, wpre, wl.n, wl.eps)
             return oracle.dense_swiglu(z, *W)
+        what = "the boundary and the dense SwiGLU layer"
+    else:
+        # routing first (cheap) to know which experts to draw; drawing inputs is not timed
+        routes = []
+        for h, x in zip(hh, xx):
+            _, z = oracle.boundary(h, x, wpost, wpre, wl.n, wl.eps)
+            ids, w, _, _ = oracle.topk(oracle.router(z, Wr), bias, wl.G, wl.kg, wl.k, wl.scale)
+            routes.append(ids)
+        need = sorted(set(int(e) for r in routes for e in r.ravel()))
+        log(f"cpu baseline: drawing {len(need)} experts for {len(hh)} tokens")
+        weights = {e: synth.expert_weights(wl, e) for e in need}  # each draw is threaded
+        if mxfp4:
+            def quant(e):
+                return e, tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m))
+                                for m in weights[e])
+            with ThreadPoolExecutor(threads) as ex:
+                for i, (e, ws) in enumerate(ex.map(quant, need)):
+                    weights[e] = ws
+                    if i % 16 == 15 or i + 1 == len(need):
+                        log(f"cpu baseline: quantised {i + 1} of {len(need)} experts")
 
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(threads) as ex:
-            list(ex.map(one_dense, range(len(hh))))
-        dt = time.perf_counter() - t0
-        log(f"cpu baseline: {len(hh)} tokens in {dt:.2f}s on {threads} threads")
-        return dict(value=round(len(hh) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                    sample=f"{len(hh)} tokens of {wl.name}, each through the boundary and the "
-                           f"dense SwiGLU layer single-threaded, {threads} tokens at a time; "
-                           f"{dt:.1f} s wall")
-    # routing first (cheap) to know which experts to draw; drawing inputs is not timed
-    zs, routes = [], []
-    for h, x in zip(hh, xx):
-        _, z = oracle.boundary(h, x, wpost, wpre, wl.n, wl.eps)
-        ids, w, _, _ = oracle.topk(oracle.router(z, Wr), bias, wl.G, wl.kg, wl.k, wl.scale)
-        zs.append(z)
-        routes.append(ids)
-    need = sorted(set(int(e) for r in routes for e in r.ravel()))
-    log(f"cpu baseline: drawing {len(need)} experts for {len(hh)} tokens")
-    weights = {e: synth.expert_weights(wl, e) for e in need}  # each draw is threaded
-    if mxfp4:
-        def quant(e):
-            return e, tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m)) for m in weights[e])
-        with ThreadPoolExecutor(threads) as ex:
-            for i, (e, ws) in enumerate(ex.map(quant, need)):
-                weights[e] = ws
-                if i % 16 == 15 or i + 1 == len(need):
-                    log(f"cpu baseline: quantised {i + 1} of {len(need)} experts")
-
-    def one(i):
-        out = oracle.sublayer(hh[i], xx[i], wpost, wpre, wl.n, wl.eps, Wr, bias, wl.G, wl.kg,
-                              wl.k, wl.scale, weights.__getitem__)
-        return out["y"]
+        def one(i):
+            out = oracle.sublayer(hh[i], xx[i], wpost, wpre, wl.n, wl.eps, Wr, bias, wl.G, wl.kg,
+                                  wl.k, wl.scale, weights.__getitem__)
+            return out["y"]
+        what = (f"the whole path (boundary, FP32 router, grouped top-k, {wl.k} SwiGLU experts, "
+                f"combine)")
 
     t0 = time.perf_counter()
+    for i in range(n1):
+        one(i)
+    dt1 = time.perf_counter() - t0
+    log(f"cpu baseline: {n1} tokens in {dt1:.2f}s on one thread")
+    t0 = time.perf_counter()
+    done = 0
     with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(one, range(len(hh))))
+        for _ in ex.map(one, range(len(hh))):
+            done += 1
+            if done % (4 * threads) == 0:
+                log(f"cpu baseline: {done} of {len(hh)} tokens")
     dt = time.perf_counter() - t0
     log(f"cpu baseline: {len(hh)} tokens in {dt:.2f}s on {threads} threads")
+    fmt = " (mxfp4 experts)" if mxfp4 else ""
     return dict(value=round(len(hh) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{len(hh)} tokens of {wl.name}{' (mxfp4 experts)' if mxfp4 else ''}, "
-                       f"each through the whole path "
-                       f"(boundary, FP32 router, grouped top-k, {wl.k} SwiGLU experts, combine) "
-                       f"single-threaded, {threads} tokens at a time; {dt:.1f} s wall")
+                sample=f"{len(hh)} tokens of {wl.name}{fmt}, each through {what} "
+                       f"single-threaded, {threads} tokens at a time; {dt:.1f} s wall",
+                single_core=dict(value=round(n1 / dt1, 3), unit="tokens/s", cores=1,
+                                 sample=f"{n1} tokens of {wl.name}{fmt} one after another on "
+                                        f"one thread; {dt1:.1f} s"))
 
 
 if __name__ == "__main__":

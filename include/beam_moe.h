@@ -53,7 +53,9 @@ enum {
  * Supported here: hidden % 256 == 0 and hidden <= 16384; d_ff % 256 == 0 and
  * d_ff <= 32768; n_experts <= 256 and a multiple of n_groups; n_groups <= 64;
  * 1 <= topk_groups <= n_groups; 1 <= topk <= min(32, topk_groups * E/G);
- * 1 <= max_tokens and max_tokens * topk < 2^31; routed_scale finite. */
+ * 1 <= max_tokens and max_tokens * topk < 2^31; routed_scale finite. Activations are
+ * addressed with 32-bit element offsets, so max_tokens * topk * max(hidden, d_ff) < 2^31
+ * (about 52K tokens at Beam's shape), else BEAM_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t hidden;      /* d */
   int32_t n_experts;   /* E */
@@ -227,6 +229,7 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
                      const int32_t* ids_in, const float* w_in, float* logits_out,
                      int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
                      void* stream);
+
 
 /*
  * beam_moe_forward_boundary — beam_moe_forward on z, then the NEXT sublayer's

@@ -121,13 +121,13 @@ hipError_t launch_repack_mxfp4_gemm(const uint8_t* gq, const uint8_t* gs, const 
                                     const uint8_t* us, const uint8_t* dq, const uint8_t* ds,
                                     int E, int f, int d, uint8_t* pqgu, uint8_t* psgu,
                                     uint8_t* pqd, uint8_t* psd, hipStream_t s);
-// Dense SwiGLU layer as one expert taking every token with weight 1: with init, rows
-// 0..max_tokens-1 get the identity order and weight 1; always, the counts, offsets,
-// active list and tile table of a T-token call (one expert, tiles of bm rows)
 // dense layer down pass for T <= 16 with K split over P workgroups per column tile
 // (FP32 partials in part [P][16][d], then the finishing pass writes a.yk = y);
 // needs (f / 32) % (4 P) == 0
 hipError_t launch_down_splitk_dense(const ExpertArgs& a, int P, float* part, hipStream_t s);
+// Dense SwiGLU layer as one expert taking every token with weight 1: with init, rows
+// 0..max_tokens-1 get the identity order and weight 1; always, the counts, offsets,
+// active list and tile table of a T-token call (one expert, tiles of bm rows)
 hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a, float* w,
                              hipStream_t s);
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
@@ -156,7 +156,6 @@ hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t
 // down for T <= kSplitDownMaxT with K split over four waves (then launch_combine)
 hipError_t launch_down_split(const ExpertArgs& a, int max_active, hipStream_t s);
 hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s);
-// T == 1, k <= 16: down projection and combine in one pass
 hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,

@@ -33,9 +33,14 @@ def to_dev(a: np.ndarray, dtype=None):
 
 def compare_bf16(got: np.ndarray, want: np.ndarray, rel_max=REL_L2_MAX, abs_max=ABS_MAX,
                  two_ulp=None):
-    """two_ulp: optional mask of elements whose input already differs by a final
-    rounding flip upstream (e.g. z where h' differs); there the flip allowance is
-    two ulps of the larger magnitude (the inherited one plus this rounding)."""
+    """Reading of the max-abs bar (3e-2): one BF16 ulp at |v| in [4, 8) is 0.03125, so a
+    single final-rounding flip there exceeds it whatever the FP32 summation order. An
+    element over the bar that is within one ulp of the larger of the two magnitudes is
+    counted as such a flip; anything else over the bar fails; rel-L2 stays strict.
+    two_ulp: optional mask of elements whose input already differs by a final
+    rounding flip upstream (z where h' differs: z = bf16(h' r w), so a one-ulp h'
+    difference carries into z before z's own rounding); there the allowance is two
+    ulps of the larger magnitude (the inherited one plus this rounding)."""
     g = F(got).astype(np.float64)
     w = F(want).astype(np.float64)
     diff = np.abs(g - w)

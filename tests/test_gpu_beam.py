@@ -51,15 +51,16 @@ def beam_gpu():
     W, b = sd.router(BASE)
     wg, wu, wd = sd.experts(BASE)
     d["moe"] = beam.BeamMoE(sd.moe_config(BASE, max_tokens=32768), W, b, wg, wu, wd)
-    skew = synth.WORKLOADS["skew32k"]
-    _, b_skew = sd.router(skew)
-    d["moe_skew"] = beam.BeamMoE(sd.moe_config(skew, max_tokens=32768), W, b_skew, wg, wu, wd)
+    for key in ("skew32k", "skew32k_half"):
+        skew = synth.WORKLOADS[key]
+        _, b_skew = sd.router(skew)
+        d[key] = beam.BeamMoE(sd.moe_config(skew, max_tokens=32768), W, b_skew, wg, wu, wd)
     del wg, wu, wd
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     yield d
-    d["moe"].close()
-    d["moe_skew"].close()
+    for key in ("moe", "skew32k", "skew32k_half"):
+        d[key].close()
 
 
 @pytest.fixture(scope="module")
@@ -89,9 +90,10 @@ def gpu_run(d, moe, wl, T, ref_z):
     h_out, z = beam.beam_sublayer_norm_residual(h, x, d["wpost"], d["wpre"], wl.n, wl.eps)
     out = {"h_out": P.bits(h_out), "z": P.bits(z)}
     del h, x, h_out
-    y_chain = moe.forward(z)
+    y_chain, rc = moe.forward(z, want_routing=True)
     out["y_chain"] = P.bits(y_chain)
-    del z, y_chain
+    out["ids_chain"] = rc["ids_out"].cpu().numpy()
+    del z, y_chain, rc
     zo = P.to_dev(ref_z)
     y, r = moe.forward(zo, want_routing=True)
     torch.cuda.synchronize()
@@ -118,11 +120,29 @@ def compare_front(g, ref, wl, what):
     return same
 
 
-def report_chain(g_chain, y_ref, what):
-    """Composed chain (each side from its own z): reported; asserted only against
-    gross error, since one-ulp z differences legitimately move logits, weights and
-    final roundings downstream."""
-    ok, st = P.compare_bf16(g_chain, y_ref)
+def oracle_y(ref, g, rows, same, wl, experts):
+    """The oracle's MoE output for tokens `rows` on the oracle's z: with the oracle's own
+    routing where the two sides selected the same experts, and with the GPU's routing
+    replayed where a near tie flipped the selection (the GPU's y of such a token was
+    computed with its own routing, so the experts' arithmetic is still compared)."""
+    keep = same[rows][:, None]
+    ids = np.where(keep, ref["ids"][rows], g["ids_out"][rows])
+    w = np.where(keep, ref["w"][rows], g["w_out"][rows])
+    experts.prefetch(ids.ravel())
+    y, _ = oracle.moe_experts(ref["z"][rows], ids, w, wl.E, experts, threads=THREADS)
+    return y
+
+
+def report_chain(g, ref, y_ref, rows, what):
+    """Composed chain (each side from its own z) on tokens `rows` (y_ref: the oracle's
+    output for them): reported; asserted only against gross error, since one-ulp z
+    differences legitimately move logits, weights and final roundings downstream. A
+    token whose chain routing (from the GPU's own z) selects other experts than the
+    oracle's is counted, not compared: its output is a different mixture."""
+    keep = np.all(g["ids_chain"][rows] == ref["ids"][rows], axis=1)
+    keep &= np.all(g["ids_out"][rows] == ref["ids"][rows], axis=1)  # y_ref used these ids
+    ok, st = P.compare_bf16(g["y_chain"][rows][keep], y_ref[keep])
+    st["routing_flips_from_own_z"] = int(np.count_nonzero(~keep))
     print(f"[parity] {what} composed chain (own z each side): {st}", flush=True)
     assert st["rel_l2"] < 1e-2
 
@@ -134,12 +154,13 @@ def test_decode_full(beam_gpu, experts, T):
     ref = host_front(wl, T)
     g = gpu_run(beam_gpu, beam_gpu["moe"], wl, T, ref["z"])
     same = compare_front(g, ref, wl, f"decode T={T}")
-    experts.prefetch(ref["ids"].ravel())
-    y, _ = oracle.moe_experts(ref["z"], ref["ids"], ref["w"], wl.E, experts, threads=THREADS)
+    rows = np.arange(T)
+    y = oracle_y(ref, g, rows, same, wl, experts)
     n_exp = len(set(ref["ids"].ravel().tolist()))
-    print(f"[beam] decode T={T}: {n_exp} distinct experts", flush=True)
-    P.assert_bf16_close(g["y"][same], y[same], f"decode T={T} y")
-    report_chain(g["y_chain"][same], y[same], f"decode T={T} y")
+    print(f"[beam] decode T={T}: {n_exp} distinct experts, {int(np.sum(~same))} replayed",
+          flush=True)
+    P.assert_bf16_close(g["y"], y, f"decode T={T} y")
+    report_chain(g, ref, y, rows, f"decode T={T} y")
 
 
 def test_sublayer_forward_decode1(beam_gpu):
@@ -197,21 +218,34 @@ def test_forward_boundary_beam(beam_gpu, T):
     assert torch.equal(zz.view(torch.int16), z_ref.view(torch.int16))
 
 
-def sampled_tokens(ids, T, hot=(), n_rand=32, seed=0):
+def sampled_tokens(offsets, perm, k, T, n_rand=32, seed=0):
+    """Tokens whose outputs are checked: the first and last 8, n_rand random ones, and one
+    row of every row tile of the grouped GEMMs (an expert's rows in the expert-grouped
+    order are cut into ceil(rows / 256) equal tiles of a multiple of 64 rows; every tile
+    of both GEMMs then has a checked row in every column tile). The row is random within
+    the tile, except in an expert's last tile, where it is the last row (the ragged tail)."""
     rng = np.random.default_rng(seed)
     pick = set(range(8)) | set(range(T - 8, T)) | set(rng.choice(T, n_rand, replace=False).tolist())
-    for e in hot:  # at least one token routed to each hot expert
-        rows = np.nonzero(np.any(ids == e, axis=1))[0]
-        if len(rows):
-            pick.add(int(rows[0]))
-    return np.array(sorted(pick))
+    tiles = 0
+    for e in range(len(offsets) - 1):
+        cnt = int(offsets[e + 1] - offsets[e])
+        if cnt == 0:
+            continue
+        mt = -(-cnt // 256)
+        per = ((-(-cnt // mt)) + 63) // 64 * 64
+        for i in range(mt):
+            lo, hi = i * per, min(cnt, (i + 1) * per)
+            r = hi - 1 if i == mt - 1 else lo + int(rng.integers(hi - lo))
+            pick.add(int(perm[offsets[e] + r]) // k)
+            tiles += 1
+    return np.array(sorted(pick)), tiles
 
 
-@pytest.mark.parametrize("name", ["prefill16k", "skew32k"])
+@pytest.mark.parametrize("name", ["prefill16k", "skew32k", "skew32k_half"])
 def test_prefill_sampled(beam_gpu, experts, name):
     wl = synth.WORKLOADS[name]
     T = wl.T
-    moe = beam_gpu["moe_skew"] if wl.hot_experts else beam_gpu["moe"]
+    moe = beam_gpu[name] if wl.hot_experts else beam_gpu["moe"]
     print(f"[beam] {name}: oracle boundary/router/routing for all {T} tokens", flush=True)
     ref = host_front(wl, T)
     print(f"[beam] {name}: GPU run T={T}", flush=True)
@@ -221,10 +255,111 @@ def test_prefill_sampled(beam_gpu, experts, name):
     hot_share = counts[list(wl.hot_experts)].sum() / counts.sum() if wl.hot_experts else 0.0
     print(f"[beam] {name}: rows per expert min {counts.min()} max {counts.max()}, "
           f"hot share {hot_share:.3f}", flush=True)
-    rows = sampled_tokens(ref["ids"], T, wl.hot_experts)
-    rows = rows[same[rows]]
-    experts.prefetch(ref["ids"][rows].ravel())
-    y, _ = oracle.moe_experts(ref["z"][rows], ref["ids"][rows], ref["w"][rows], wl.E, experts,
-                              threads=THREADS)
+    rows, tiles = sampled_tokens(g["offsets_out"], g["perm_out"], wl.k, T)
+    print(f"[beam] {name}: {len(rows)} sampled tokens cover {tiles} row tiles, "
+          f"{int(np.sum(~same[rows]))} with replayed routing", flush=True)
+    y = oracle_y(ref, g, rows, same, wl, experts)
     P.assert_bf16_close(g["y"][rows], y, f"{name} y ({len(rows)} sampled tokens)")
-    report_chain(g["y_chain"][rows], y, f"{name} y ({len(rows)} sampled tokens)")
+    report_chain(g, ref, y, rows, f"{name} y ({len(rows)} sampled tokens)")
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_forward_boundary_beam_oracle(beam_gpu, experts, T):
+    """beam_moe_forward_boundary (the step bench.py times by default) against the oracle
+    at Beam's shapes: the MoE on the oracle's z with the GPU's routing checked as the
+    oracle's top-k of the GPU's logits, then the next boundary (residual = another seeded
+    stream) with the oracle's MoE output as its branch. Every element of y, h' and z."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    wl = BASE.with_tokens(T)
+    print(f"[beam] forward+boundary vs oracle T={T}", flush=True)
+    ref = host_front(wl, T)
+    h_next = synth.token_rows(wl, range(T), "h", token_set=2)
+    moe = beam_gpu["moe"]
+    zz, hh = P.to_dev(ref["z"]), P.to_dev(h_next)
+    y = torch.empty_like(zz)
+    lg = torch.empty((T, wl.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+    h_out, z_out = beam.beam_moe_forward_boundary(moe.handle, zz, hh, beam_gpu["wpost"],
+                                                  beam_gpu["wpre"], wl.n, wl.eps, y_out=y,
+                                                  logits_out=lg, ids_out=ids, w_out=w)
+    torch.cuda.synchronize()
+    g_lg, g_ids, g_w = lg.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    assert P.logit_rel_rows(g_lg, ref["logits"]).max() <= P.LOGIT_REL_MAX
+    o_ids, o_w, _, _ = oracle.topk(g_lg, synth.router_bias(wl), wl.G, wl.kg, wl.k, wl.scale)
+    assert np.array_equal(g_ids, o_ids)
+    assert np.max(np.abs(g_w.view(np.int32).astype(np.int64) - o_w.view(np.int32))) <= 1
+    experts.prefetch(o_ids.ravel())
+    o_y, _ = oracle.moe_experts(ref["z"], o_ids, o_w, wl.E, experts, threads=THREADS)
+    o_h, o_z = oracle.boundary(h_next, o_y, synth.norm_weight(wl, "post"),
+                               synth.norm_weight(wl, "pre"), wl.n, wl.eps)
+    g_h = P.bits(h_out)
+    P.assert_bf16_close(P.bits(y), o_y, f"fused T={T} y")
+    P.assert_bf16_close(g_h, o_h, f"fused T={T} h'")
+    P.assert_bf16_close(P.bits(z_out), o_z, f"fused T={T} z", two_ulp=g_h != o_h)
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_sublayer_forward_beam_oracle(beam_gpu, experts, T):
+    """beam_sublayer_forward at Beam's shapes against the oracle, stage by stage: h' and z
+    from the seeded h, x; logits from the GPU's z; ids bit-exact with the oracle's top-k of
+    the GPU's logits; y = the oracle's experts on the GPU's z and that routing."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    wl = BASE.with_tokens(T)
+    print(f"[beam] sublayer forward vs oracle T={T}", flush=True)
+    hh = synth.token_rows(wl, range(T), "h", token_set=3)
+    xx = synth.token_rows(wl, range(T), "x", token_set=3)
+    o_h, o_z = oracle.boundary(hh, xx, synth.norm_weight(wl, "post"),
+                               synth.norm_weight(wl, "pre"), wl.n, wl.eps)
+    moe = beam_gpu["moe"]
+    y = torch.empty((T, wl.d), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((T, wl.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+    h_out, z = beam.beam_sublayer_forward(moe.handle, P.to_dev(hh), P.to_dev(xx),
+                                          beam_gpu["wpost"], beam_gpu["wpre"], wl.n, wl.eps, y,
+                                          logits_out=lg, ids_out=ids, w_out=w)
+    torch.cuda.synchronize()
+    g_h, g_z = P.bits(h_out), P.bits(z)
+    P.assert_bf16_close(g_h, o_h, f"one-call T={T} h'")
+    P.assert_bf16_close(g_z, o_z, f"one-call T={T} z", two_ulp=g_h != o_h)
+    g_lg = lg.cpu().numpy()
+    assert P.logit_rel_rows(g_lg, oracle.router_threaded(g_z, synth.router_weight(wl),
+                                                         THREADS)).max() <= P.LOGIT_REL_MAX
+    o_ids, o_w, _, _ = oracle.topk(g_lg, synth.router_bias(wl), wl.G, wl.kg, wl.k, wl.scale)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    experts.prefetch(o_ids.ravel())
+    o_y, _ = oracle.moe_experts(g_z, o_ids, o_w, wl.E, experts, threads=THREADS)
+    P.assert_bf16_close(P.bits(y), o_y, f"one-call T={T} y")
+
+
+def test_routing_identical_across_batch_paths(beam_gpu, experts):
+    """A token's logits, experts and weights are the same bits whether it is routed alone
+    (the one-launch small-batch routing), in a batch of 16 (the same launch with 16 tokens)
+    or in a batch of 128 (the separate FP32 router and top-k): all three use one dot-product
+    order. Its MoE output differs at most by final-rounding flips between the expert paths
+    (T <= 16 and 17..128 sum K in different orders), and each matches the oracle."""
+    import torch
+    wl = BASE.with_tokens(128)
+    ref = host_front(wl, 128)
+    moe = beam_gpu["moe"]
+    z = P.to_dev(ref["z"])
+    outs = {}
+    for T in (1, 16, 128):
+        y, r = moe.forward(z[:T].contiguous(), want_routing=True)
+        torch.cuda.synchronize()
+        outs[T] = (P.bits(y), {k: v.cpu().numpy() for k, v in r.items()})
+    for key in ("logits_out", "ids_out", "w_out"):
+        for T in (16, 128):
+            assert np.array_equal(outs[T][1][key][:1].view(np.uint32),
+                                  outs[1][1][key][:1].view(np.uint32)), (T, key)
+        assert np.array_equal(outs[128][1][key][:16].view(np.uint32),
+                              outs[16][1][key].view(np.uint32)), key
+    experts.prefetch(outs[1][1]["ids_out"].ravel())
+    o_y, _ = oracle.moe_experts(ref["z"][:1], outs[1][1]["ids_out"], outs[1][1]["w_out"], wl.E,
+                                experts)
+    for T in (1, 16, 128):
+        P.assert_bf16_close(outs[T][0][:1], o_y, f"token 0 of T={T}")

@@ -465,3 +465,97 @@ def test_prefill_path_ragged_tiles():
         P.assert_bf16_close(P.bits(y2), ref["y"], "tiny@1536 y (replay)")
     finally:
         moe.close()
+
+
+def _front(T, token_set=0):
+    """Oracle boundary of seeded tokens 0..T-1: (h, x, h', z) as BF16 bits."""
+    hh = synth.token_rows(WL, range(T), "h", token_set=token_set)
+    xx = synth.token_rows(WL, range(T), "x", token_set=token_set)
+    h_out, z = oracle.boundary(hh, xx, synth.norm_weight(WL, "post"), synth.norm_weight(WL, "pre"),
+                               WL.n, WL.eps)
+    return hh, xx, h_out, z
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+@pytest.mark.parametrize("replay", [False, True])
+def test_forward_boundary_matches_oracle(gpu, host, T, replay):
+    """beam_moe_forward_boundary against the oracle: the MoE on z (routing from the GPU's
+    logits must be the oracle's top-k of those logits, bit for bit; replayed routing with an
+    invalid slot contributes nothing), then the next boundary with the MoE output as its
+    branch: oracle.moe_experts followed by oracle.boundary on the same inputs."""
+    import torch
+    print(f"[tiny] forward+boundary vs oracle T={T} replay={replay}", flush=True)
+    _, _, h_next, z = _front(T)          # z: the MoE input; h_next: the residual stream
+    ids_in = w_in = None
+    if replay:
+        ids, w, _, _ = oracle.topk(oracle.router(z, synth.router_weight(WL)),
+                                   synth.router_bias(WL), WL.G, WL.kg, WL.k, WL.scale)
+        ids[T // 2, 1] = -1
+        ids_in, w_in = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    got = _forward_boundary(gpu["moe"], P.to_dev(z), P.to_dev(h_next), gpu["wpost"], gpu["wpre"],
+                            WL.n, WL.eps, ids_in, w_in)
+    if replay:
+        o_ids, o_w = ids, w
+        assert np.array_equal(got["ids"], o_ids)
+    else:
+        rel = P.logit_rel_rows(got["logits"], oracle.router(z, synth.router_weight(WL)))
+        assert rel.max() <= P.LOGIT_REL_MAX
+        o_ids, o_w, _, _ = oracle.topk(got["logits"], synth.router_bias(WL), WL.G, WL.kg, WL.k,
+                                       WL.scale)
+        assert np.array_equal(got["ids"], o_ids)
+        assert np.max(np.abs(got["w"].view(np.int32).astype(np.int64) - o_w.view(np.int32))) <= 1
+    o_y, _ = oracle.moe_experts(z, o_ids, o_w, WL.E, host["experts"].__getitem__)
+    o_h, o_z = oracle.boundary(h_next, o_y, synth.norm_weight(WL, "post"),
+                               synth.norm_weight(WL, "pre"), WL.n, WL.eps)
+    P.assert_bf16_close(got["y"], o_y, f"tiny fused y T={T}")
+    P.assert_bf16_close(got["h"], o_h, f"tiny fused h' T={T}")
+    P.assert_bf16_close(got["z"], o_z, f"tiny fused z T={T}", two_ulp=got["h"] != o_h)
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_sublayer_forward_stages_match_oracle(gpu, host, T):
+    """beam_sublayer_forward against the oracle stage by stage: h' and z from the seeded
+    h, x; logits from the GPU's z; ids = the oracle's top-k of the GPU's logits (bit-exact);
+    y = the oracle's experts on the GPU's z and routing."""
+    print(f"[tiny] sublayer forward vs oracle T={T}", flush=True)
+    hh, xx, o_h, o_z = _front(T, token_set=1)
+    got = _one_call(gpu["moe"], P.to_dev(hh), P.to_dev(xx), gpu["wpost"], gpu["wpre"], WL.n,
+                    WL.eps)
+    g_h, g_z, g_y, g_lg, g_ids, g_w = got
+    P.assert_bf16_close(g_h, o_h, f"tiny one-call h' T={T}")
+    P.assert_bf16_close(g_z, o_z, f"tiny one-call z T={T}", two_ulp=g_h != o_h)
+    rel = P.logit_rel_rows(g_lg, oracle.router(g_z, synth.router_weight(WL)))
+    assert rel.max() <= P.LOGIT_REL_MAX
+    o_ids, o_w, _, _ = oracle.topk(g_lg, synth.router_bias(WL), WL.G, WL.kg, WL.k, WL.scale)
+    assert np.array_equal(g_ids, o_ids)
+    o_y, _ = oracle.moe_experts(g_z, o_ids, o_w, WL.E, host["experts"].__getitem__)
+    P.assert_bf16_close(g_y, o_y, f"tiny one-call y T={T}")
+
+
+def test_boundary_closed_forms_bit_exact(gpu):
+    """Rows whose norm factors are exact (eps = 0): branch rows of small odd integers with
+    mean square 16 (factor 1/4, so the post-norm output x w / 4 is exact before its BF16
+    rounding) and constant rows. Every sum of squares is exact in any order, so the GPU's
+    h' must equal the closed form bf16(c2 * bf16(x w / 4)) bit for bit (h = 0, n = 20), and
+    a constant branch row c gives sign(c) * w_post / 2 at n = 4."""
+    import sparse_moe_decoder_amd as beam
+    from tests.test_oracle_pins import power_of_four_rows, to_bf16
+    d = WL.d
+    x = np.concatenate([power_of_four_rows(6, 41 + j) for j in range(d // 64)], axis=1)
+    rng = np.random.default_rng(44)
+    w_post = to_bf16(rng.uniform(0.9, 1.1, d))
+    ones = to_bf16(np.ones(d))
+    c2 = np.float32(1.0 / np.sqrt(20.0))
+    want = P.F(to_bf16(c2 * P.F(to_bf16((P.F(x) * np.float32(0.25)) * P.F(w_post)))))
+    zero = np.zeros_like(x)
+    hp, _ = beam.beam_sublayer_norm_residual(P.to_dev(zero), P.to_dev(x), P.to_dev(w_post),
+                                             P.to_dev(ones), 20, 0.0)
+    assert np.array_equal(P.F(P.bits(hp)), want)
+    o_h, _ = oracle.boundary(zero, x, w_post, ones, 20, 0.0)
+    assert np.array_equal(P.bits(hp), o_h)
+    for c in (1.5, -3.0):
+        xc = np.full((2, d), to_bf16(np.float32(c)), np.uint16)
+        hp, _ = beam.beam_sublayer_norm_residual(P.to_dev(np.zeros_like(xc)), P.to_dev(xc),
+                                                 P.to_dev(w_post), P.to_dev(ones), 4, 0.0)
+        want_c = np.float32(0.5 * np.sign(c)) * P.F(w_post)
+        assert np.array_equal(P.F(P.bits(hp)), np.broadcast_to(want_c, (2, d)))
