@@ -19,6 +19,9 @@ Parity status of each step (how it is pinned is listed in ``tests/test_oracle_pi
   O7 MXFP4 weights ... pinned (hand-derived blocks from the OCP MX v1.0 definitions: scale
                         rule, every rounding tie, saturation, signed zero; exact round trip
                         of representable blocks; the half-step error bound; sign symmetry)
+  O8 4-bit act. ...... pinned (permutation-matrix closed forms over hand-derived MXFP4
+                        blocks: z and act quantised per row along their contraction, not
+                        g, u or y; identity on representable rows; the half-step bound)
 """
 from __future__ import annotations
 
@@ -69,9 +72,10 @@ def lib():
         L.oracle_combine.argtypes = [i64, i64, i64, i64, vp, vp, vp]
         L.oracle_mxfp4_quantize.argtypes = [i64, i64, vp, vp, vp]
         L.oracle_mxfp4_dequantize.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_expert_rows_mx.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
         for name in ("oracle_boundary", "oracle_router", "oracle_topk", "oracle_permute",
                      "oracle_expert_rows", "oracle_combine", "oracle_mxfp4_quantize",
-                     "oracle_mxfp4_dequantize"):
+                     "oracle_mxfp4_dequantize", "oracle_expert_rows_mx"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +188,20 @@ def expert_rows(zrows, Wg, Wu, Wd, wrow):
     return out
 
 
+def expert_rows_mx(zrows, Wg, Wu, Wd, wrow):
+    """O8: O5 with the token rows and the activation rows MXFP4-quantised (O7, blocks of 32
+    along each GEMM's contraction) and used at their dequantised values."""
+    zrows = _c(zrows, np.uint16)
+    R, d = zrows.shape
+    f = Wg.shape[0]
+    assert Wg.shape == (f, d) and Wu.shape == (f, d) and Wd.shape == (d, f)
+    out = np.empty((R, d), dtype=np.uint16)
+    _check(lib().oracle_expert_rows_mx(R, d, f, _p(zrows), _p(_c(Wg, np.uint16)),
+                                       _p(_c(Wu, np.uint16)), _p(_c(Wd, np.uint16)),
+                                       _p(_c(wrow, np.float32)), _p(out)), "oracle_expert_rows_mx")
+    return out
+
+
 def dense_swiglu(z, Wg, Wu, Wd):
     """A dense SwiGLU MLP layer ([vLLM page, §Modellarchitektur]: Beam's layers 0-2, d_ff
     20480) on rows z [T, d]: O5 with routing weight 1, i.e. g = bf16(z.Wg^T), u = bf16(z.Wu^T),
@@ -231,13 +249,14 @@ def mxfp4_dequantize(codes, scales):
 
 # ---- composition -------------------------------------------------------------------------------
 
-def moe_experts(z, ids, w, E, get_expert, threads=1):
+def moe_experts(z, ids, w, E, get_expert, threads=1, mx_act=False):
     """O5 + O6 for tokens z [T, d] with routing (ids [T, k], w [T, k]).
 
     get_expert(e) -> (Wg [f, d], Wu [f, d], Wd [d, f]) as BF16 bits. The loop is
     expert-major (each expert's rows computed by O5 with its own per-element
     sequential arithmetic), so the result does not depend on `threads`.
-    Slots with an id outside [0, E) contribute nothing.
+    Slots with an id outside [0, E) contribute nothing. mx_act: O8 (4-bit activations)
+    instead of O5.
     """
     z = _c(z, np.uint16)
     ids = _c(ids, np.int32)
@@ -250,7 +269,7 @@ def moe_experts(z, ids, w, E, get_expert, threads=1):
     def run(e):
         tt, jj = np.nonzero(ids == e)
         wg, wu, wd = get_expert(e)
-        rows = expert_rows(z[tt], wg, wu, wd, w[tt, jj])
+        rows = (expert_rows_mx if mx_act else expert_rows)(z[tt], wg, wu, wd, w[tt, jj])
         return tt, jj, rows
 
     if threads > 1 and len(experts) > 1:

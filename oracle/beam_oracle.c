@@ -380,3 +380,66 @@ int oracle_mxfp4_dequantize(int64_t rows, int64_t K, const uint8_t* codes, const
     }
   return 0;
 }
+
+/*
+ * O8 — experts with 4-bit activations.
+ * [vLLM §Der fusionierte Graph]: the 4-bit MoE path at batch-1 decode is an activation
+ *   quantisation, two routing kernels and two grouped GEMMs, i.e. the GEMMs multiply
+ *   quantised activations by the 4-bit experts; [SGLang §BF16、NVFP4 和 FP8 模型支持]: the
+ *   4-bit checkpoints are served on that path.
+ * Reading: both GEMM inputs an expert multiplies by its weights are MXFP4-quantised by O7's
+ *   rule, blocks of 32 consecutive values along the contraction: the token row z (blocks
+ *   along d) before gate/up, and the activation row act (blocks along f) before down. They
+ *   enter at their exact dequantised values; everything else is O5: g and u rounded to
+ *   BF16, act = bf16(silu(g) * u), FP32 accumulation, the FP32 routing weight on the
+ *   FP32 down sum, one rounding.
+ */
+int oracle_expert_rows_mx(int64_t R, int64_t d, int64_t f, const uint16_t* zrows,
+                          const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                          const float* wrow, uint16_t* yk) {
+  if (R < 0 || d <= 0 || f <= 0 || d % 32 != 0 || f % 32 != 0) return -1;
+  const int64_t big = d > f ? d : f;
+  uint16_t* zq = (uint16_t*)malloc((size_t)d * sizeof(uint16_t));
+  uint16_t* act = (uint16_t*)malloc((size_t)f * sizeof(uint16_t));
+  uint16_t* actq = (uint16_t*)malloc((size_t)f * sizeof(uint16_t));
+  uint8_t* codes = (uint8_t*)malloc((size_t)big / 2);
+  uint8_t* scales = (uint8_t*)malloc((size_t)big / 32);
+  int rc = 0;
+  if (!zq || !act || !actq || !codes || !scales) rc = -3;
+  for (int64_t r = 0; r < R && rc == 0; ++r) {
+    /* the token row, quantised along d */
+    if (oracle_mxfp4_quantize(1, d, zrows + r * d, codes, scales) != 0 ||
+        oracle_mxfp4_dequantize(1, d, codes, scales, zq) != 0) {
+      rc = -1;
+      break;
+    }
+    for (int64_t q = 0; q < f; ++q) {
+      float ag = 0.0f, au = 0.0f;
+      for (int64_t i = 0; i < d; ++i) {
+        float zi = oracle_f32(zq[i]);
+        ag = ag + zi * oracle_f32(Wg[q * d + i]);
+        au = au + zi * oracle_f32(Wu[q * d + i]);
+      }
+      float gq = oracle_f32(oracle_bf16(ag));
+      float uq = oracle_f32(oracle_bf16(au));
+      act[q] = oracle_bf16(oracle_silu(gq) * uq);
+    }
+    /* the activation row, quantised along f */
+    if (oracle_mxfp4_quantize(1, f, act, codes, scales) != 0 ||
+        oracle_mxfp4_dequantize(1, f, codes, scales, actq) != 0) {
+      rc = -1;
+      break;
+    }
+    for (int64_t o = 0; o < d; ++o) {
+      float acc = 0.0f;
+      for (int64_t q = 0; q < f; ++q) acc = acc + oracle_f32(actq[q]) * oracle_f32(Wd[o * f + q]);
+      yk[r * d + o] = oracle_bf16(wrow[r] * acc);
+    }
+  }
+  free(zq);
+  free(act);
+  free(actq);
+  free(codes);
+  free(scales);
+  return rc;
+}

@@ -78,6 +78,13 @@ int oracle_mxfp4_quantize(int64_t rows, int64_t K, const uint16_t* v, uint8_t* c
 int oracle_mxfp4_dequantize(int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
                             uint16_t* out);
 
+/* O8: O5 with 4-bit activations: each token row z and each activation row act is
+ * MXFP4-quantised (O7, blocks of 32 along its K) and used at its dequantised value.
+ * Arguments as in O5 (the weights are the experts' dequantised 4-bit weights). */
+int oracle_expert_rows_mx(int64_t R, int64_t d, int64_t f, const uint16_t* zrows,
+                          const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                          const float* wrow, uint16_t* yk);
+
 #ifdef __cplusplus
 }
 #endif

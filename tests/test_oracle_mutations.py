@@ -43,6 +43,25 @@ MUTATIONS = [
      "acc = oracle_f32(oracle_bf16(acc + oracle_f32(yk[(t * k + j) * d + o])));"),
     ("sigmoid in FP32", "(float)(1.0 / (1.0 + exp(-(double)logit)))",
      "1.0f / (1.0f + expf(-logit))"),
+    ("mx token row not quantised", "float zi = oracle_f32(zq[i]);",
+     "float zi = oracle_f32(zrows[r * d + i]);"),
+    ("mx activation not quantised", "acc = acc + oracle_f32(actq[q]) * oracle_f32(Wd[o * f + q]);",
+     "acc = acc + oracle_f32(act[q]) * oracle_f32(Wd[o * f + q]);"),
+    ("mx gate quantised instead of the activation", [
+        ("float gq = oracle_f32(oracle_bf16(ag));\n      float uq = oracle_f32(oracle_bf16(au));\n"
+         "      act[q] = oracle_bf16(oracle_silu(gq) * uq);\n    }\n    /* the activation row",
+         "float gq = oracle_f32(oracle_bf16(ag));\n      float uq = oracle_f32(oracle_bf16(au));\n"
+         "      act[q] = oracle_bf16(gq);\n      actq[q] = oracle_bf16(uq);\n    }\n"
+         "    if (oracle_mxfp4_quantize(1, f, act, codes, scales) != 0 ||\n"
+         "        oracle_mxfp4_dequantize(1, f, codes, scales, act) != 0) { rc = -1; break; }\n"
+         "    for (int64_t q = 0; q < f; ++q)\n"
+         "      act[q] = oracle_bf16(oracle_silu(oracle_f32(act[q])) * oracle_f32(actq[q]));\n"
+         "    /* the activation row"),
+        ("oracle_mxfp4_dequantize(1, f, codes, scales, actq) != 0) {\n      rc = -1;",
+         "0) {\n      rc = -1;"),
+        ("acc = acc + oracle_f32(actq[q]) * oracle_f32(Wd[o * f + q]);",
+         "acc = acc + oracle_f32(act[q]) * oracle_f32(Wd[o * f + q]);"),
+    ]),
     # the branch scaled from the unrounded post-norm output (norm factor recomputed per row)
     ("post-norm output not rounded", [
         ("rmsnorm_row(d, xr, w_post, eps, xn); /* post-norm of the branch, rounded */",

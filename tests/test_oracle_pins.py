@@ -448,6 +448,58 @@ def test_expert_permutation_closed_form():
         assert np.mean(got == want) > 0.97
 
 
+def _mx_round_trip(v):
+    """O7 quantise-dequantise of BF16 rows (blocks of 32 along the row); O7 itself is pinned
+    by the hand-derived blocks below."""
+    return oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(v))
+
+
+def test_mx_activations_permutation_closed_form():
+    """O8 ([vLLM page, Der fusionierte Graph]: the 4-bit MoE path quantises the activations
+    before its grouped GEMMs). With one-hot weight rows every GEMM sum has one term, so
+      g_q = zq[pg(q)], u_q = zq[pu(q)], act = bf16(silu(g) * u), y_o = bf16(w * actq[pd(o)])
+    where zq and actq are the MXFP4 round trips of the token row and the activation row,
+    blocks of 32 along each row. The rows differ in magnitude by 2^10 and 2^-10, so blocks
+    that straddle rows, a skipped quantisation, or quantising g, u or y instead fail."""
+    d = f = 64
+    rng = np.random.default_rng(46)
+    pg, pu, pd = rng.permutation(f), rng.permutation(f), rng.permutation(d)
+    Wg = _perm_matrix(f, d, pg, 1.0)
+    Wu = _perm_matrix(f, d, pu, 1.0)
+    Wd = _perm_matrix(d, f, pd, 1.0)
+    z = to_bf16(rng.standard_normal((3, d)).astype(np.float32) *
+                np.array([[1.0], [1024.0], [1.0 / 1024]], np.float32))
+    wrow = np.array([2.5, 0.75, 1.25], np.float32)
+    yk = oracle.expert_rows_mx(z, Wg, Wu, Wd, wrow)
+    zq = F(_mx_round_trip(z))
+    g, u = zq[:, pg], zq[:, pu]
+    act = to_bf16(np.array([[oracle.silu(a) for a in row] for row in g], np.float32) * u)
+    actq = F(_mx_round_trip(act))
+    want = to_bf16(wrow[:, None] * actq[:, pd])
+    # values (the FP32 sums start at +0, so a -0 term leaves +0: compare as numbers)
+    assert np.array_equal(F(yk), F(want))
+    # the case tells the readings apart: both quantisations change many outputs
+    no_act_q = to_bf16(wrow[:, None] * F(act)[:, pd])
+    assert np.mean(no_act_q != want) > 0.5
+    assert np.mean(zq != F(z)) > 0.5
+
+
+def test_mx_activations_half_step_bound():
+    """Random layer: O8 differs from O5 (BF16 activations) by about the MXFP4 quantisation
+    noise of the activations, far more than rounding and far less than the signal."""
+    d, f, R = 128, 96, 8
+    rng = np.random.default_rng(47)
+    z = _rows(R, d, 48)
+    Wg = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wu = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wd = to_bf16(rng.standard_normal((d, f)) * 0.1)
+    w = np.ones(R, np.float32)
+    a = F(oracle.expert_rows_mx(z, Wg, Wu, Wd, w)).astype(np.float64)
+    b = F(oracle.expert_rows(z, Wg, Wu, Wd, w)).astype(np.float64)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert 0.02 < rel < 0.5, rel
+
+
 def _dense_swiglu_fp64(z, Wg, Wu, Wd, w):
     """Independent FP64 dense SwiGLU with the BF16 rounding points (test-side)."""
     zf = F(z).astype(np.float64)
