@@ -230,6 +230,25 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
                      int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
                      void* stream);
 
+/*
+ * beam_moe_forward_noalloc — beam_moe_forward for callers that cannot allocate device
+ * memory at all (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation), including the handle's per-call workspace: the logits, routing, grouping
+ * tables, activations and expert rows of the call live in a static scratch area of the
+ * library (32 MiB per GPU, held by every GPU the library runs on until the process ends)
+ * instead of the handle's workspace. Same arguments, results (bit for bit) and errors as
+ * beam_moe_forward; additionally BEAM_ERR_CAPACITY when the call's workspace does not fit
+ * the scratch area: T * k * 2 * (d_ff + hidden) bytes plus T * E * 4 and small tables,
+ * i.e. up to 256 tokens at Beam's shape (hidden 5120, d_ff 2560, k 8, E 256), and
+ * BEAM_ERR_HIP if the area's device address could not be looked up when the handle was
+ * created. Allocates nothing and synchronises nothing. Every such call on one GPU uses the
+ * same area, which keeps the last call's contents: calls that overlap in time on one GPU
+ * (two streams, or two host threads) race and must not be issued.
+ */
+int beam_moe_forward_noalloc(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                             const int32_t* ids_in, const float* w_in, float* logits_out,
+                             int32_t* ids_out, float* w_out, int32_t* perm_out,
+                             int32_t* offsets_out, void* stream);
 
 /*
  * beam_moe_forward_boundary — beam_moe_forward on z, then the NEXT sublayer's

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     beam_grouped_topk,
     beam_moe_destroy,
     beam_moe_forward,
+    beam_moe_forward_noalloc,
     beam_moe_forward_boundary,
     beam_moe_init,
     beam_moe_init_mxfp4,

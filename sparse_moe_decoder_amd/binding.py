@@ -48,6 +48,7 @@ def lib():
         L.beam_router_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.beam_grouped_topk.argtypes = [vp, i32, vp, vp, vp, vp]
         L.beam_moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.beam_moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.beam_sublayer_forward.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp,
                                             vp, vp]
         L.beam_moe_forward_boundary.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp,
@@ -64,6 +65,7 @@ def lib():
                      "beam_dense_init", "beam_dense_forward",
                      "beam_moe_destroy", "beam_sublayer_norm_residual",
                      "beam_router_topk", "beam_grouped_topk", "beam_moe_forward",
+                     "beam_moe_forward_noalloc",
                      "beam_sublayer_forward", "beam_moe_forward_boundary",
                      "beam_profile_enable", "beam_profile_reset", "beam_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -216,6 +218,18 @@ def beam_moe_forward(handle, z, y_out, ids_in=None, w_in=None, logits_out=None, 
                      w_out=None, perm_out=None, offsets_out=None, stream=None):
     T = z.shape[0]
     _check("beam_moe_forward", lib().beam_moe_forward(
+        handle, T, _ptr(z, name="z"), _ptr(y_out, name="y_out"), _ptr(ids_in, name="ids_in"),
+        _ptr(w_in, name="w_in"), _ptr(logits_out, name="logits_out"),
+        _ptr(ids_out, name="ids_out"), _ptr(w_out, name="w_out"),
+        _ptr(perm_out, name="perm_out"), _ptr(offsets_out, name="offsets_out"),
+        _stream(stream)))
+
+
+def beam_moe_forward_noalloc(handle, z, y_out, ids_in=None, w_in=None, logits_out=None,
+                             ids_out=None, w_out=None, perm_out=None, offsets_out=None,
+                             stream=None):
+    T = z.shape[0]
+    _check("beam_moe_forward_noalloc", lib().beam_moe_forward_noalloc(
         handle, T, _ptr(z, name="z"), _ptr(y_out, name="y_out"), _ptr(ids_in, name="ids_in"),
         _ptr(w_in, name="w_in"), _ptr(logits_out, name="logits_out"),
         _ptr(ids_out, name="ids_out"), _ptr(w_out, name="w_out"),

@@ -8,6 +8,7 @@
 
 #include <mutex>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/beam_moe.h"
@@ -91,6 +92,28 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BEAM_OK : BEAM_ERR_HIP; 
 // ---------------------------------------------------------------------------------------------
 // Handle
 
+// Per-call device buffers of the MoE forward for T tokens (slots = T * k). A handle owns
+// one set sized for max_tokens; the allocation-free entry point carves one out of the
+// library's static scratch area instead.
+struct Workspace {
+  float* logits = nullptr;     // [T, E]
+  int32_t* ids = nullptr;      // [T, k]
+  float* w = nullptr;          // [T, k]
+  int32_t* counts = nullptr;   // [E]
+  int32_t* offsets = nullptr;  // [E + 1]
+  int32_t* active = nullptr;   // [E]
+  int32_t* n_active = nullptr; // [1]
+  int32_t* tile_start = nullptr;  // [E + 1]
+  int32_t* perm = nullptr;        // [T * k]
+  uint32_t* route_done = nullptr;  // [1] workgroup counter of the fused small-batch routing:
+                                   // zero before its first launch, left zero by every launch
+  uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
+  int32_t* block_cnt = nullptr;   // [nb * E], nb = ceil(slots / kPermChunk)
+  int32_t* block_base = nullptr;  // [nb * E]
+  uint16_t* act = nullptr;        // [T * k, f]
+  uint16_t* yk = nullptr;         // [T * k, d]
+};
+
 struct beam_moe_ctx {
   beam_moe_config cfg;
   int device = 0;
@@ -111,24 +134,84 @@ struct beam_moe_ctx {
   uint8_t* pqd = nullptr;
   uint8_t* psd = nullptr;
   float* dense_part = nullptr;  // dense layers: FP32 partials of the split-K down pass [4][16][d]
-  // workspace (owned), sized for max_tokens
-  float* logits = nullptr;     // [maxT, E]
-  int32_t* ids = nullptr;      // [maxT, k]
-  float* w = nullptr;          // [maxT, k]
-  int32_t* counts = nullptr;   // [E]
-  int32_t* offsets = nullptr;  // [E + 1]
-  int32_t* active = nullptr;   // [E]
-  int32_t* n_active = nullptr; // [1]
-  int32_t* tile_start = nullptr;  // [E + 1]
-  int32_t* perm = nullptr;        // [maxT * k]
-  uint32_t* route_done = nullptr;  // [1] workgroup counter of the fused small-batch routing
-  uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
-  int32_t* block_cnt = nullptr;   // [nb * E]
-  int32_t* block_base = nullptr;  // [nb * E]
-  uint16_t* act = nullptr;        // [maxT * k, f]
-  uint16_t* yk = nullptr;         // [maxT * k, d]
+  Workspace ws;                 // owned, sized for max_tokens
   std::vector<void*> allocations;
 };
+
+// ---------------------------------------------------------------------------------------------
+// Static scratch area for beam_moe_forward_noalloc (callers that cannot allocate device
+// memory). Every GPU the library runs on holds one copy, for the life of the process; every
+// such call on that GPU shares it. Host code never passes the array's name to a kernel or a
+// copy (on the host it only names the symbol): it uses the device address looked up once per
+// device by hipGetSymbolAddress while that device is current.
+//   bytes [0, 256): the fused small-batch routing's workgroup counter (zeroed when the address
+//                   is looked up; every launch that uses it leaves it zero again)
+//   bytes [256, kScratchBytes): the per-call workspace of one forward (carve_scratch)
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+
+// Look up (once per device) the device address of `scratch` on the current device and zero
+// its counter on stream s. Returns the address, or null on failure.
+void* scratch_setup(int device, hipStream_t s) {
+  if (device < 0 || device >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[device]) return g_scratch_ptr[device];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (hipMemsetAsync(ptr, 0, 256, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[device] = ptr;
+  return ptr;
+}
+
+void* scratch_of(int device) {
+  if (device < 0 || device >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
+
+// Lay out the workspace of a T-token forward in the scratch area at `base` (256-byte
+// aligned pieces after the counter). Returns the bytes used (base may be null to size it).
+size_t carve_scratch(const beam_moe_config& c, int T, char* base, Workspace* ws) {
+  const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, slots = (size_t)T * c.topk;
+  const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
+  size_t off = 256;
+  auto take = [&](auto** p, size_t bytes) {
+    if (base) *p = reinterpret_cast<std::remove_pointer_t<decltype(p)>>(base + off);
+    off += (bytes + 255) & ~(size_t)255;
+  };
+  Workspace w;
+  if (base) w.route_done = reinterpret_cast<uint32_t*>(base);
+  take(&w.logits, (size_t)T * E * 4);
+  take(&w.ids, slots * 4);
+  take(&w.w, slots * 4);
+  take(&w.counts, E * 4);
+  take(&w.offsets, (E + 1) * 4);
+  take(&w.active, E * 4);
+  take(&w.n_active, 4);
+  take(&w.tile_start, (E + 1) * 4);
+  take(&w.perm, slots * 4);
+  take(&w.route_sc, (size_t)kFusedRouteMaxT * E * 8);
+  take(&w.block_cnt, nb * E * 4);
+  take(&w.block_base, nb * E * 4);
+  take(&w.act, slots * f * 2);
+  take(&w.yk, slots * d * 2);
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace
 
 namespace {
 
@@ -181,19 +264,19 @@ int run_router(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, hipStre
   return hip_status(launch_router_fp32(ra, s));
 }
 
-TopkArgs topk_args(beam_moe_ctx* h, int T, const float* logits, int32_t* ids_copy,
-                   float* w_copy) {
+TopkArgs topk_args(beam_moe_ctx* h, const Workspace& ws, int T, const float* logits,
+                   int32_t* ids_copy, float* w_copy) {
   const beam_moe_config& c = h->cfg;
   return TopkArgs{T, c.n_experts, c.n_groups, c.topk_groups, c.topk, c.routed_scale,
-                  logits, h->bias, h->ids, h->w, ids_copy, w_copy};
+                  logits, h->bias, ws.ids, ws.w, ids_copy, w_copy};
 }
 
-int route(beam_moe_ctx* h, int T, const uint16_t* z, float* logits, int32_t* ids_copy,
-          float* w_copy, hipStream_t s) {
+int route(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z, float* logits,
+          int32_t* ids_copy, float* w_copy, hipStream_t s) {
   int st = run_router(h, T, z, logits, s);
   if (st != BEAM_OK) return st;
   ProfScope ps(K_TOPK, s);
-  return hip_status(launch_topk(topk_args(h, T, logits, ids_copy, w_copy), s));
+  return hip_status(launch_topk(topk_args(h, ws, T, logits, ids_copy, w_copy), s));
 }
 
 bool overlaps(const void* a, const void* b, int64_t bytes) {
@@ -206,34 +289,34 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
 // post: the next sublayer's boundary with x = the MoE output runs in the combine
 // launch (d <= kBoundaryWgMaxD; y_out may then be null) or after it (wider rows,
 // through y_out).
-int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, const int32_t* ids_in,
-                 const float* w_in, float* logits_out, int32_t* ids_out, float* w_out,
-                 int32_t* perm_out, int32_t* offsets_out, hipStream_t s, const BoundaryArgs* bnd,
-                 const BoundaryArgs* post) {
+int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z, uint16_t* y_out,
+                 const int32_t* ids_in, const float* w_in, float* logits_out, int32_t* ids_out,
+                 float* w_out, int32_t* perm_out, int32_t* offsets_out, hipStream_t s,
+                 const BoundaryArgs* bnd, const BoundaryArgs* post) {
   const beam_moe_config& c = h->cfg;
   const int k = c.topk, E = c.n_experts;
   const int slots = T * k;
 
   const int32_t* ids = ids_in;
   const float* w = w_in;
-  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, h->counts,
-              h->offsets, h->perm, h->block_cnt, h->block_base, h->active, h->n_active,
-              h->tile_start, perm_out, offsets_out};
+  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, ws.counts,
+              ws.offsets, ws.perm, ws.block_cnt, ws.block_base, ws.active, ws.n_active,
+              ws.tile_start, perm_out, offsets_out};
   if (!ids_in) {
-    float* lg = logits_out ? logits_out : h->logits;
-    ids = h->ids;
-    w = h->w;
+    float* lg = logits_out ? logits_out : ws.logits;
+    ids = ws.ids;
+    w = ws.w;
     pa.ids = ids;
-    TopkArgs ta = topk_args(h, T, lg, ids_out, w_out);
+    TopkArgs ta = topk_args(h, ws, T, lg, ids_out, w_out);
     if (bnd) {
       ProfScope ps(K_ROUTER, s);  // boundary, router, top-k and grouping in one launch
       RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_boundary_route_fused(*bnd, ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
+      if (launch_boundary_route_fused(*bnd, ra, ta, pa, ws.route_done, ws.route_sc, s) != hipSuccess)
         return BEAM_ERR_HIP;
     } else if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
       ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
       RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_route_fused_tiny(ra, ta, pa, h->route_done, h->route_sc, s) != hipSuccess)
+      if (launch_route_fused_tiny(ra, ta, pa, ws.route_done, ws.route_sc, s) != hipSuccess)
         return BEAM_ERR_HIP;
     } else if (slots <= kPermChunk) {
       int st = run_router(h, T, z, lg, s);
@@ -261,8 +344,8 @@ int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, con
     ProfScope ps(K_PERMUTE, s);
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
   }
-  ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, w, h->act, h->yk, h->qgu, h->sgu, h->qd, h->sd,
+  ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, ws.perm, ws.offsets, ws.active,
+                ws.n_active, ws.tile_start, w, ws.act, ws.yk, h->qgu, h->sgu, h->qd, h->sd,
                 h->pqgu, h->psgu, h->pqd, h->psd};
   if (h->mxfp4 && T > kStreamMaxT) {  // 4-bit grouped GEMMs
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
@@ -304,10 +387,10 @@ int forward_impl(beam_moe_ctx* h, int T, const uint16_t* z, uint16_t* y_out, con
     }
   }
   ProfScope ps(K_COMBINE, s);
-  if (!post) return hip_status(launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s));
+  if (!post) return hip_status(launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s));
   if (c.hidden <= kBoundaryWgMaxD)
-    return hip_status(launch_combine_boundary(*post, CombineArgs{k, E, ids, h->yk, y_out}, s));
-  if (launch_combine(T, k, c.hidden, E, ids, h->yk, y_out, s) != hipSuccess) return BEAM_ERR_HIP;
+    return hip_status(launch_combine_boundary(*post, CombineArgs{k, E, ids, ws.yk, y_out}, s));
+  if (launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s) != hipSuccess) return BEAM_ERR_HIP;
   BoundaryArgs pb = *post;
   pb.x = y_out;
   return hip_status(launch_boundary(pb, s));
@@ -348,20 +431,23 @@ int init_handle(const beam_moe_config* cfg, const float* router_w, const float* 
     delete h;
     return BEAM_ERR_HIP;
   }
+  // the allocation-free forward's scratch address on this device (its own failure only
+  // makes that entry point return BEAM_ERR_HIP)
+  (void)scratch_setup(h->device, s);
   const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, k = c.topk, T = c.max_tokens;
   const size_t slots = T * k;
   const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
   bool ok = dev_alloc(h, &h->router_w, E * d) && dev_alloc(h, &h->router_x3, 3 * E * d) &&
             dev_alloc(h, &h->bias, E) &&
-            dev_alloc(h, &h->logits, T * E) && dev_alloc(h, &h->ids, slots) &&
-            dev_alloc(h, &h->w, slots) && dev_alloc(h, &h->counts, E) &&
-            dev_alloc(h, &h->offsets, E + 1) && dev_alloc(h, &h->active, E) &&
-            dev_alloc(h, &h->n_active, 1) && dev_alloc(h, &h->tile_start, E + 1) &&
-            dev_alloc(h, &h->perm, slots) && dev_alloc(h, &h->route_done, 1) &&
-            dev_alloc(h, &h->route_sc, (size_t)kFusedRouteMaxT * E) &&
-            dev_alloc(h, &h->block_cnt, nb * E) &&
-            dev_alloc(h, &h->block_base, nb * E) && dev_alloc(h, &h->act, slots * f) &&
-            dev_alloc(h, &h->yk, slots * d);
+            dev_alloc(h, &h->ws.logits, T * E) && dev_alloc(h, &h->ws.ids, slots) &&
+            dev_alloc(h, &h->ws.w, slots) && dev_alloc(h, &h->ws.counts, E) &&
+            dev_alloc(h, &h->ws.offsets, E + 1) && dev_alloc(h, &h->ws.active, E) &&
+            dev_alloc(h, &h->ws.n_active, 1) && dev_alloc(h, &h->ws.tile_start, E + 1) &&
+            dev_alloc(h, &h->ws.perm, slots) && dev_alloc(h, &h->ws.route_done, 1) &&
+            dev_alloc(h, &h->ws.route_sc, (size_t)kFusedRouteMaxT * E) &&
+            dev_alloc(h, &h->ws.block_cnt, nb * E) &&
+            dev_alloc(h, &h->ws.block_base, nb * E) && dev_alloc(h, &h->ws.act, slots * f) &&
+            dev_alloc(h, &h->ws.yk, slots * d);
   hipError_t e = hipSuccess;
   if (ok) {
     const int st = experts(h, s);
@@ -381,7 +467,7 @@ int init_handle(const beam_moe_config* cfg, const float* router_w, const float* 
     e = router_bias ? hipMemcpyAsync(h->bias, router_bias, E * sizeof(float),
                                      hipMemcpyDeviceToDevice, s)
                     : hipMemsetAsync(h->bias, 0, E * sizeof(float), s);
-  if (e == hipSuccess) e = hipMemsetAsync(h->route_done, 0, sizeof(uint32_t), s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->ws.route_done, 0, sizeof(uint32_t), s);
   if (e == hipSuccess && E % 64 == 0 && router_w)
     e = launch_repack_router(router_w, h->router_x3, (int)E, (int)d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -476,9 +562,10 @@ int beam_dense_init(int32_t hidden, int32_t d_ff, int32_t max_tokens, const uint
       return BEAM_ERR_OOM;
     if (launch_repack(w_gate, w_up, w_down, h->wgu, h->wdp, 1, (int)f, (int)d, s) != hipSuccess)
       return BEAM_ERR_HIP;
-    PermArgs pa{max_tokens, 1, 1, kGemmBM, nullptr, h->counts, h->offsets, h->perm, nullptr,
-                nullptr, h->active, h->n_active, h->tile_start, nullptr, nullptr};
-    return hip_status(launch_dense_plan(0, max_tokens, true, pa, h->w, s));
+    const Workspace& ws = h->ws;
+    PermArgs pa{max_tokens, 1, 1, kGemmBM, nullptr, ws.counts, ws.offsets, ws.perm, nullptr,
+                nullptr, ws.active, ws.n_active, ws.tile_start, nullptr, nullptr};
+    return hip_status(launch_dense_plan(0, max_tokens, true, pa, ws.w, s));
   });
 }
 
@@ -492,15 +579,16 @@ int beam_dense_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t
       overlaps(z, y_out, (int64_t)T * c.hidden * 2))
     return BEAM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  PermArgs pa{T, 1, 1, kGemmBM, nullptr, h->counts, h->offsets, h->perm, nullptr, nullptr,
-              h->active, h->n_active, h->tile_start, nullptr, nullptr};
+  const Workspace& ws = h->ws;
+  PermArgs pa{T, 1, 1, kGemmBM, nullptr, ws.counts, ws.offsets, ws.perm, nullptr, nullptr,
+              ws.active, ws.n_active, ws.tile_start, nullptr, nullptr};
   {
     ProfScope ps(K_PERMUTE, s);
-    if (launch_dense_plan(T, c.max_tokens, false, pa, h->w, s) != hipSuccess) return BEAM_ERR_HIP;
+    if (launch_dense_plan(T, c.max_tokens, false, pa, ws.w, s) != hipSuccess) return BEAM_ERR_HIP;
   }
   // the down pass writes each row's bf16(1 * sum) straight to y (one slot per token)
-  ExpertArgs ea{T, 1, c.hidden, c.d_ff, 1, z, h->wgu, h->wdp, h->perm, h->offsets, h->active,
-                h->n_active, h->tile_start, h->w, h->act, y_out};
+  ExpertArgs ea{T, 1, c.hidden, c.d_ff, 1, z, h->wgu, h->wdp, ws.perm, ws.offsets, ws.active,
+                ws.n_active, ws.tile_start, ws.w, ws.act, y_out};
   if (T <= kStreamMaxT) {
     {
       ProfScope ps(K_GATEUP, s);
@@ -555,7 +643,8 @@ int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* log
   if (!z || !ids_out || !w_out || !aligned16(z) || ((uintptr_t)ids_out & 3u) ||
       ((uintptr_t)w_out & 3u) || (logits_out && ((uintptr_t)logits_out & 3u)))
     return BEAM_ERR_INVALID_ARG;
-  return route(h, T, z, logits_out ? logits_out : h->logits, ids_out, w_out, (hipStream_t)stream);
+  return route(h, h->ws, T, z, logits_out ? logits_out : h->ws.logits, ids_out, w_out,
+               (hipStream_t)stream);
 }
 
 int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t* ids_out,
@@ -568,7 +657,7 @@ int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t
     return BEAM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   ProfScope ps(K_TOPK, s);
-  TopkArgs ta = topk_args(h, T, logits, nullptr, nullptr);
+  TopkArgs ta = topk_args(h, h->ws, T, logits, nullptr, nullptr);
   ta.ids = ids_out;
   ta.w = w_out;
   return hip_status(launch_topk(ta, s));
@@ -589,7 +678,31 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
   const beam_moe_config& c = h->cfg;
   if (overlaps(y_out, z, (int64_t)T * c.hidden * 2)) return BEAM_ERR_INVALID_ARG;
-  return forward_impl(h, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
+  return forward_impl(h, h->ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
+                      offsets_out, (hipStream_t)stream, nullptr, nullptr);
+}
+
+int beam_moe_forward_noalloc(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* y_out,
+                             const int32_t* ids_in, const float* w_in, float* logits_out,
+                             int32_t* ids_out, float* w_out, int32_t* perm_out,
+                             int32_t* offsets_out, void* stream) {
+  if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  if (carve_scratch(h->cfg, T, nullptr, nullptr) > kScratchBytes) return BEAM_ERR_CAPACITY;
+  if (!z || !y_out || !aligned16(z) || !aligned16(y_out)) return BEAM_ERR_INVALID_ARG;
+  if ((ids_in == nullptr) != (w_in == nullptr)) return BEAM_ERR_INVALID_ARG;
+  if (ids_in && logits_out) return BEAM_ERR_INVALID_ARG;
+  const void* ptrs4[] = {ids_in, w_in, logits_out, ids_out, w_out, perm_out, offsets_out};
+  for (const void* p : ptrs4)
+    if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
+  const beam_moe_config& c = h->cfg;
+  if (overlaps(y_out, z, (int64_t)T * c.hidden * 2)) return BEAM_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(scratch_of(h->device));
+  if (!base) return BEAM_ERR_HIP;
+  Workspace ws;
+  carve_scratch(c, T, base, &ws);
+  return forward_impl(h, ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
                       offsets_out, (hipStream_t)stream, nullptr, nullptr);
 }
 
@@ -630,8 +743,8 @@ int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
   const float c1 = (float)sqrt((double)(n - 1) / (double)n);
   const float c2 = (float)(1.0 / sqrt((double)n));
   BoundaryArgs post{T, d, h_in, nullptr, w_post, w_pre, h_out, z_out, c1, c2, eps};
-  return forward_impl(h, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, nullptr, nullptr,
-                      (hipStream_t)stream, nullptr, &post);
+  return forward_impl(h, h->ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, nullptr,
+                      nullptr, (hipStream_t)stream, nullptr, &post);
 }
 
 int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, const uint16_t* x,
@@ -665,14 +778,14 @@ int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, co
   hipStream_t s = (hipStream_t)stream;
   BoundaryArgs ba{T, d, h_in, x, w_post, w_pre, h_out, z_out, c1, c2, eps};
   if (T == 1 && d <= kBoundaryWgMaxD && c.topk <= kFusedRouteMaxSlots)
-    return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
-                        nullptr, s, &ba, nullptr);
+    return forward_impl(h, h->ws, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out,
+                        nullptr, nullptr, s, &ba, nullptr);
   {
     ProfScope ps(K_BOUNDARY, s);
     if (launch_boundary(ba, s) != hipSuccess) return BEAM_ERR_HIP;
   }
-  return forward_impl(h, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out, nullptr,
-                      nullptr, s, nullptr, nullptr);
+  return forward_impl(h, h->ws, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out,
+                      nullptr, nullptr, s, nullptr, nullptr);
 }
 
 int beam_profile_enable(int enable) {

@@ -93,6 +93,8 @@ def test_handle_calls_reject_null_handle(L):
     assert L.beam_router_topk(None, 1, p, None, p, p, None) == -1
     assert L.beam_grouped_topk(None, 1, p, p, p, None) == -1
     assert L.beam_moe_forward(None, 1, p, p, None, None, None, None, None, None, None, None) == -1
+    assert L.beam_moe_forward_noalloc(None, 1, p, p, None, None, None, None, None, None, None,
+                                      None) == -1
     assert L.beam_sublayer_forward(None, 1, p, p, p, p, 20, 1e-6, p, p, p, None, None, None,
                                    None) == -1
     assert L.beam_moe_forward_boundary(None, 1, p, p, p, p, 20, 1e-6, p, p, None, None, None,
