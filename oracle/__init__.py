@@ -73,9 +73,12 @@ def lib():
         L.oracle_mxfp4_quantize.argtypes = [i64, i64, vp, vp, vp]
         L.oracle_mxfp4_dequantize.argtypes = [i64, i64, vp, vp, vp]
         L.oracle_expert_rows_mx.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.oracle_expert_act.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+        L.oracle_expert_down.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         for name in ("oracle_boundary", "oracle_router", "oracle_topk", "oracle_permute",
                      "oracle_expert_rows", "oracle_combine", "oracle_mxfp4_quantize",
-                     "oracle_mxfp4_dequantize", "oracle_expert_rows_mx"):
+                     "oracle_mxfp4_dequantize", "oracle_expert_rows_mx", "oracle_expert_act",
+                     "oracle_expert_down"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,6 +202,30 @@ def expert_rows_mx(zrows, Wg, Wu, Wd, wrow):
     _check(lib().oracle_expert_rows_mx(R, d, f, _p(zrows), _p(_c(Wg, np.uint16)),
                                        _p(_c(Wu, np.uint16)), _p(_c(Wd, np.uint16)),
                                        _p(_c(wrow, np.float32)), _p(out)), "oracle_expert_rows_mx")
+    return out
+
+
+def expert_act(zrows, Wg, Wu):
+    """O5's first half: act [R, f] = bf16(silu(bf16(z Wg^T)) * bf16(z Wu^T))."""
+    zrows = _c(zrows, np.uint16)
+    R, d = zrows.shape
+    f = Wg.shape[0]
+    assert Wg.shape == (f, d) and Wu.shape == (f, d)
+    out = np.empty((R, f), dtype=np.uint16)
+    _check(lib().oracle_expert_act(R, d, f, _p(zrows), _p(_c(Wg, np.uint16)),
+                                   _p(_c(Wu, np.uint16)), _p(out)), "oracle_expert_act")
+    return out
+
+
+def expert_down(act, Wd, wrow):
+    """O5's second half: yk [R, d] = bf16(wrow * (act Wd^T))."""
+    act = _c(act, np.uint16)
+    R, f = act.shape
+    d = Wd.shape[0]
+    assert Wd.shape == (d, f)
+    out = np.empty((R, d), dtype=np.uint16)
+    _check(lib().oracle_expert_down(R, d, f, _p(act), _p(_c(Wd, np.uint16)),
+                                    _p(_c(wrow, np.float32)), _p(out)), "oracle_expert_down")
     return out
 
 

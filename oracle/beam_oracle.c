@@ -443,3 +443,43 @@ int oracle_expert_rows_mx(int64_t R, int64_t d, int64_t f, const uint16_t* zrows
   free(scales);
   return rc;
 }
+
+/*
+ * O5 in two halves, so a GPU path whose activation leaves one kernel for the next can be
+ * checked stage by stage on identical inputs (the halves compose to O5, and with the two
+ * MXFP4 round trips between them to O8; pinned by those identities):
+ *   oracle_expert_act:  act[r] = bf16(silu(bf16(z_r . Wg^T)) * bf16(z_r . Wu^T))
+ *   oracle_expert_down: yk[r]  = bf16(wrow[r] * (act_r . Wd^T))
+ */
+int oracle_expert_act(int64_t R, int64_t d, int64_t f, const uint16_t* zrows, const uint16_t* Wg,
+                      const uint16_t* Wu, uint16_t* act) {
+  if (R < 0 || d <= 0 || f <= 0) return -1;
+  for (int64_t r = 0; r < R; ++r) {
+    const uint16_t* z = zrows + r * d;
+    for (int64_t q = 0; q < f; ++q) {
+      float ag = 0.0f, au = 0.0f;
+      for (int64_t i = 0; i < d; ++i) {
+        float zi = oracle_f32(z[i]);
+        ag = ag + zi * oracle_f32(Wg[q * d + i]);
+        au = au + zi * oracle_f32(Wu[q * d + i]);
+      }
+      float gq = oracle_f32(oracle_bf16(ag));
+      float uq = oracle_f32(oracle_bf16(au));
+      act[r * f + q] = oracle_bf16(oracle_silu(gq) * uq);
+    }
+  }
+  return 0;
+}
+
+int oracle_expert_down(int64_t R, int64_t d, int64_t f, const uint16_t* act, const uint16_t* Wd,
+                       const float* wrow, uint16_t* yk) {
+  if (R < 0 || d <= 0 || f <= 0) return -1;
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t o = 0; o < d; ++o) {
+      float acc = 0.0f;
+      for (int64_t q = 0; q < f; ++q)
+        acc = acc + oracle_f32(act[r * f + q]) * oracle_f32(Wd[o * f + q]);
+      yk[r * d + o] = oracle_bf16(wrow[r] * acc);
+    }
+  return 0;
+}

@@ -85,6 +85,13 @@ int oracle_expert_rows_mx(int64_t R, int64_t d, int64_t f, const uint16_t* zrows
                           const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
                           const float* wrow, uint16_t* yk);
 
+/* O5's halves: act [R, f] BF16 from z rows (gate/up, SiLU * up), and yk [R, d] from act
+ * rows (down, routing weight, one rounding). down(act(z)) is O5. */
+int oracle_expert_act(int64_t R, int64_t d, int64_t f, const uint16_t* zrows, const uint16_t* Wg,
+                      const uint16_t* Wu, uint16_t* act);
+int oracle_expert_down(int64_t R, int64_t d, int64_t f, const uint16_t* act, const uint16_t* Wd,
+                       const float* wrow, uint16_t* yk);
+
 #ifdef __cplusplus
 }
 #endif

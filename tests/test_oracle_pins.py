@@ -500,6 +500,30 @@ def test_mx_activations_half_step_bound():
     assert 0.02 < rel < 0.5, rel
 
 
+def test_expert_halves_compose_to_o5_and_o8():
+    """The stage functions used to check GPU kernels one stage at a time: down(act(z)) is O5
+    bit for bit, and with MXFP4 round trips of z and act between them, O8; act alone is O5's
+    output through an identity down projection with weight 1."""
+    d, f, R = 128, 96, 5
+    rng = np.random.default_rng(49)
+    z = _rows(R, d, 50)
+    Wg = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wu = to_bf16(rng.standard_normal((f, d)) * 0.1)
+    Wd = to_bf16(rng.standard_normal((d, f)) * 0.1)
+    w = np.array([2.5, 0.5, 1.0, 0.25, 1.75], np.float32)
+    act = oracle.expert_act(z, Wg, Wu)
+    assert np.array_equal(oracle.expert_down(act, Wd, w), oracle.expert_rows(z, Wg, Wu, Wd, w))
+    act_mx = oracle.expert_act(_mx_round_trip(z), Wg, Wu)
+    assert np.array_equal(oracle.expert_down(_mx_round_trip(act_mx), Wd, w),
+                          oracle.expert_rows_mx(z, Wg, Wu, Wd, w))
+    # d = f: an identity down projection with weight 1 passes act through unchanged
+    zs = z[:, :f].copy()
+    Wg2, Wu2 = Wg[:, :f].copy(), Wu[:, :f].copy()
+    ident = to_bf16(np.eye(f, dtype=np.float32))
+    assert np.array_equal(F(oracle.expert_rows(zs, Wg2, Wu2, ident, np.ones(R, np.float32))),
+                          F(oracle.expert_act(zs, Wg2, Wu2)))
+
+
 def _dense_swiglu_fp64(z, Wg, Wu, Wd, w):
     """Independent FP64 dense SwiGLU with the BF16 rounding points (test-side)."""
     zf = F(z).astype(np.float64)
