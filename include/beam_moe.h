@@ -127,6 +127,48 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
                         const uint8_t* up_scales, const uint8_t* down_codes,
                         const uint8_t* down_scales, void* stream, beam_moe_handle* out);
 
+/* Activation formats of the expert GEMMs (beam_moe_set_activation_format). */
+enum { BEAM_ACT_BF16 = 0, BEAM_ACT_MXFP4 = 1 };
+
+/*
+ * beam_moe_set_activation_format — choose what the expert GEMMs of a handle multiply its
+ * weights with. BEAM_ACT_BF16 (the default): BF16 activations. BEAM_ACT_MXFP4 (handles from
+ * beam_moe_init_mxfp4 only): 4-bit activations as well as 4-bit weights (W4A4), the pages'
+ * 4-bit MoE path ([vLLM §Der fusionierte Graph]: an activation quantisation ahead of the
+ * two grouped GEMMs on the 4-bit experts). Every MoE compute call then quantises each
+ * token row z to MXFP4 (blocks of 32 along d, the rule of beam_mxfp4_quantize) and the
+ * activation act = bf16(silu(g) * u) to MXFP4 (blocks of 32 along f), and the grouped GEMMs
+ * multiply the 4-bit operands on the scaled FP4 matrix cores (each 32-value block's
+ * products are exact; FP32 accumulation); g, u, the routing weight, the BF16 rounding of
+ * each expert row and the combine are as in beam_moe_forward. The format applies to every
+ * T. Takes effect for calls made after it returns; allocates and enqueues nothing.
+ * Returns BEAM_ERR_UNSUPPORTED for BEAM_ACT_MXFP4 on a BF16-weight handle and
+ * BEAM_ERR_INVALID_ARG for a dense handle or another format.
+ */
+int beam_moe_set_activation_format(beam_moe_handle h, int32_t format);
+
+/* Intermediate buffers of the last compute call (beam_moe_inspect). */
+enum {
+  BEAM_INSPECT_ACT = 0,        /* BF16 activations [T*k, f], rows in the expert-grouped order */
+  BEAM_INSPECT_ACT_CODES = 1,  /* 4-bit activations: codes [T*k, f/2] (see below) */
+  BEAM_INSPECT_ACT_SCALES = 2, /* 4-bit activations: E8M0 scales [T*k, f/32] */
+  BEAM_INSPECT_Z_CODES = 3,    /* 4-bit activations: token-row codes [T, d/2] */
+  BEAM_INSPECT_Z_SCALES = 4    /* 4-bit activations: token-row scales [T, d/32] */
+};
+
+/*
+ * beam_moe_inspect — the device address of one of a handle's intermediate buffers, for
+ * tests and tools that check the expert stages separately. The contents are those of the
+ * last compute call on the handle (rows 0 .. T*k-1 or T-1 of it) once that call has
+ * completed on its stream. 4-bit codes are stored per 32-value block as 16 bytes whose
+ * dword p holds block elements 8 q .. 8 q + 7, q = (0, 2, 1, 3)[p] (element 2i of a dword's
+ * eight in its low nibble). BEAM_INSPECT_ACT holds BF16 activations only after BF16-
+ * activation calls. Returns BEAM_ERR_UNSUPPORTED when the handle has no such buffer (4-bit
+ * codes of an activation-BF16 handle), BEAM_ERR_INVALID_ARG for an unknown `what`. The
+ * buffer is owned by the handle; the caller only reads it.
+ */
+int beam_moe_inspect(beam_moe_handle h, int32_t what, const void** ptr);
+
 /*
  * beam_dense_init — a handle for one dense SwiGLU MLP layer.
  * [vLLM §Modellarchitektur]: Beam's layers 0-2 use a dense SwiGLU MLP (d_ff 20480)

@@ -15,6 +15,10 @@ from .binding import (  # noqa: F401
     beam_moe_destroy,
     beam_moe_forward,
     beam_moe_forward_noalloc,
+    beam_moe_set_activation_format,
+    beam_moe_inspect,
+    ACT_BF16,
+    ACT_MXFP4,
     beam_moe_forward_boundary,
     beam_moe_init,
     beam_moe_init_mxfp4,

@@ -49,6 +49,8 @@ def lib():
         L.beam_grouped_topk.argtypes = [vp, i32, vp, vp, vp, vp]
         L.beam_moe_forward.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.beam_moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.beam_moe_set_activation_format.argtypes = [vp, i32]
+        L.beam_moe_inspect.argtypes = [vp, i32, ctypes.POINTER(vp)]
         L.beam_sublayer_forward.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp,
                                             vp, vp]
         L.beam_moe_forward_boundary.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp,
@@ -65,7 +67,8 @@ def lib():
                      "beam_dense_init", "beam_dense_forward",
                      "beam_moe_destroy", "beam_sublayer_norm_residual",
                      "beam_router_topk", "beam_grouped_topk", "beam_moe_forward",
-                     "beam_moe_forward_noalloc",
+                     "beam_moe_forward_noalloc", "beam_moe_set_activation_format",
+                     "beam_moe_inspect",
                      "beam_sublayer_forward", "beam_moe_forward_boundary",
                      "beam_profile_enable", "beam_profile_reset", "beam_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -225,6 +228,21 @@ def beam_moe_forward(handle, z, y_out, ids_in=None, w_in=None, logits_out=None, 
         _stream(stream)))
 
 
+ACT_BF16, ACT_MXFP4 = 0, 1
+INSPECT = {"act": 0, "act_codes": 1, "act_scales": 2, "z_codes": 3, "z_scales": 4}
+
+
+def beam_moe_set_activation_format(handle, fmt):
+    _check("beam_moe_set_activation_format", lib().beam_moe_set_activation_format(handle, fmt))
+
+
+def beam_moe_inspect(handle, what):
+    """Device address (int) of one of the handle's intermediate buffers (see beam_moe.h)."""
+    p = ctypes.c_void_p()
+    _check("beam_moe_inspect", lib().beam_moe_inspect(handle, INSPECT[what], ctypes.byref(p)))
+    return p.value
+
+
 def beam_moe_forward_noalloc(handle, z, y_out, ids_in=None, w_in=None, logits_out=None,
                              ids_out=None, w_out=None, perm_out=None, offsets_out=None,
                              stream=None):
@@ -303,6 +321,19 @@ def profile_read():
     return out
 
 
+def lib_copy(dst, src, nbytes):
+    """Device-to-device copy of nbytes (plain HIP copy through torch's runtime)."""
+    import torch
+    # a view of the source address: torch copies between two device tensors
+    from torch.cuda import current_stream  # noqa: F401
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    torch.cuda.synchronize()
+    rc = hip.hipMemcpy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, 3)
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed: {rc}")
+
+
 # ---- convenience object ----------------------------------------------------------------
 
 class BeamMoE:
@@ -319,6 +350,17 @@ class BeamMoE:
             self.handle = beam_moe_init_mxfp4(cfg, router_w, router_bias, *mxfp4, stream=stream)
         else:
             self.handle = beam_moe_init(cfg, router_w, router_bias, w_gate, w_up, w_down, stream)
+
+    def set_activation_format(self, fmt):
+        beam_moe_set_activation_format(self.handle, fmt)
+
+    def inspect(self, what, nbytes):
+        """Copy nbytes of an intermediate buffer to a new uint8 device tensor."""
+        import torch
+        src = beam_moe_inspect(self.handle, what)
+        out = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        lib_copy(out.data_ptr(), src, nbytes)
+        return out
 
     def close(self):
         if self.handle is not None and self.handle.value:

@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbeam_moe.so")
 SOURCES = ["api.hip", "boundary.hip", "router.hip", "permute.hip", "experts.hip",
-           "experts_mxfp4.hip"]
+           "experts_mxfp4.hip", "experts_w4a4.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed-FP32 instructions in device code

@@ -110,8 +110,12 @@ struct Workspace {
   uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
   int32_t* block_cnt = nullptr;   // [nb * E], nb = ceil(slots / kPermChunk)
   int32_t* block_base = nullptr;  // [nb * E]
-  uint16_t* act = nullptr;        // [T * k, f]
+  uint16_t* act = nullptr;        // [T * k, f]; with 4-bit activations: their codes
+                                  // [T * k, f/2], then scales [T * k, f/32]
   uint16_t* yk = nullptr;         // [T * k, d]
+  uint8_t* zq = nullptr;          // 4-bit activations: token-row codes [T, d/2]
+  uint8_t* zqs = nullptr;         //   and scales [T, d/32]
+  uint8_t* aqs = nullptr;         // 4-bit activations: where the activation scales start in act
 };
 
 struct beam_moe_ctx {
@@ -124,6 +128,7 @@ struct beam_moe_ctx {
   uint16_t* wgu = nullptr;    // packed gate/up (BF16 experts)
   uint16_t* wdp = nullptr;    // packed down (BF16 experts)
   bool mxfp4 = false;         // 4-bit experts: the four arrays below instead of wgu, wdp
+  bool act_mx = false;        // 4-bit experts with 4-bit activations (the W4A4 GEMMs)
   bool dense = false;         // a dense SwiGLU layer (beam_dense_init): one expert, no routing
   uint8_t* qgu = nullptr;     // gate/up codes, decode layout
   uint8_t* sgu = nullptr;     // gate/up scales
@@ -183,7 +188,7 @@ void* scratch_of(int device) {
 
 // Lay out the workspace of a T-token forward in the scratch area at `base` (256-byte
 // aligned pieces after the counter). Returns the bytes used (base may be null to size it).
-size_t carve_scratch(const beam_moe_config& c, int T, char* base, Workspace* ws) {
+size_t carve_scratch(const beam_moe_config& c, bool mx, int T, char* base, Workspace* ws) {
   const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, slots = (size_t)T * c.topk;
   const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
   size_t off = 256;
@@ -207,6 +212,11 @@ size_t carve_scratch(const beam_moe_config& c, int T, char* base, Workspace* ws)
   take(&w.block_base, nb * E * 4);
   take(&w.act, slots * f * 2);
   take(&w.yk, slots * d * 2);
+  if (mx) {
+    take(&w.zq, (size_t)T * d / 2);
+    take(&w.zqs, (size_t)T * d / 32);
+    if (base) w.aqs = reinterpret_cast<uint8_t*>(w.act) + slots * f / 2;
+  }
   if (ws) *ws = w;
   return off;
 }
@@ -347,7 +357,22 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, ws.perm, ws.offsets, ws.active,
                 ws.n_active, ws.tile_start, w, ws.act, ws.yk, h->qgu, h->sgu, h->qd, h->sd,
                 h->pqgu, h->psgu, h->pqd, h->psd};
-  if (h->mxfp4 && T > kStreamMaxT) {  // 4-bit grouped GEMMs
+  if (h->act_mx) {  // 4-bit activations: quantise the token rows, then the W4A4 GEMMs
+    ea.zq = ws.zq;
+    ea.zqs = ws.zqs;
+    ea.aq = reinterpret_cast<uint8_t*>(ws.act);
+    ea.aqs = ws.aqs;
+    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+    {
+      ProfScope ps(K_GATEUP, s);
+      if (launch_quantize_rows_a4((int64_t)T * (c.hidden / 32), z, ws.zq, ws.zqs, s) !=
+              hipSuccess ||
+          launch_gateup_gemm_a4(ea, max_tiles, s) != hipSuccess)
+        return BEAM_ERR_HIP;
+    }
+    ProfScope ps(K_DOWN, s);
+    if (launch_down_gemm_a4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+  } else if (h->mxfp4 && T > kStreamMaxT) {  // 4-bit grouped GEMMs
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
     {
       ProfScope ps(K_GATEUP, s);
@@ -525,7 +550,10 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
     if (launch_repack_mxfp4(gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales,
                             (int)E, (int)f, (int)d, h->qgu, h->sgu, h->qd, h->sd, s) != hipSuccess)
       return BEAM_ERR_HIP;
-    if (cfg->max_tokens <= kStreamMaxT) return BEAM_OK;
+    const size_t T = cfg->max_tokens;
+    if (!dev_alloc(h, &h->ws.zq, T * d / 2) || !dev_alloc(h, &h->ws.zqs, T * d / 32))
+      return BEAM_ERR_OOM;
+    h->ws.aqs = reinterpret_cast<uint8_t*>(h->ws.act) + T * cfg->topk * f / 2;
     if (!dev_alloc(h, &h->pqgu, E * 2 * f * d / 2) || !dev_alloc(h, &h->psgu, E * 2 * f * d / 32) ||
         !dev_alloc(h, &h->pqd, E * d * f / 2) || !dev_alloc(h, &h->psd, E * d * f / 32))
       return BEAM_ERR_OOM;
@@ -544,6 +572,28 @@ int beam_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t* src, uint8_t* c
     return BEAM_ERR_INVALID_ARG;
   return hip_status(launch_mxfp4_quantize(rows * (K / 32), src, codes_out, scales_out,
                                           (hipStream_t)stream));
+}
+
+int beam_moe_set_activation_format(beam_moe_handle h, int32_t format) {
+  if (!h || h->dense || (format != BEAM_ACT_BF16 && format != BEAM_ACT_MXFP4))
+    return BEAM_ERR_INVALID_ARG;
+  if (format == BEAM_ACT_MXFP4 && !h->mxfp4) return BEAM_ERR_UNSUPPORTED;
+  h->act_mx = format == BEAM_ACT_MXFP4;
+  return BEAM_OK;
+}
+
+int beam_moe_inspect(beam_moe_handle h, int32_t what, const void** ptr) {
+  if (!h || !ptr) return BEAM_ERR_INVALID_ARG;
+  const Workspace& ws = h->ws;
+  switch (what) {
+    case BEAM_INSPECT_ACT: *ptr = ws.act; break;
+    case BEAM_INSPECT_ACT_CODES: *ptr = h->act_mx ? (const void*)ws.act : nullptr; break;
+    case BEAM_INSPECT_ACT_SCALES: *ptr = h->act_mx ? (const void*)ws.aqs : nullptr; break;
+    case BEAM_INSPECT_Z_CODES: *ptr = ws.zq; break;
+    case BEAM_INSPECT_Z_SCALES: *ptr = ws.zqs; break;
+    default: return BEAM_ERR_INVALID_ARG;
+  }
+  return *ptr ? BEAM_OK : BEAM_ERR_UNSUPPORTED;
 }
 
 int beam_dense_init(int32_t hidden, int32_t d_ff, int32_t max_tokens, const uint16_t* w_gate,
@@ -689,7 +739,7 @@ int beam_moe_forward_noalloc(beam_moe_handle h, int32_t T, const uint16_t* z, ui
   if (!h || h->dense || T < 0) return BEAM_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return BEAM_ERR_CAPACITY;
   if (T == 0) return BEAM_OK;
-  if (carve_scratch(h->cfg, T, nullptr, nullptr) > kScratchBytes) return BEAM_ERR_CAPACITY;
+  if (carve_scratch(h->cfg, h->mxfp4, T, nullptr, nullptr) > kScratchBytes) return BEAM_ERR_CAPACITY;
   if (!z || !y_out || !aligned16(z) || !aligned16(y_out)) return BEAM_ERR_INVALID_ARG;
   if ((ids_in == nullptr) != (w_in == nullptr)) return BEAM_ERR_INVALID_ARG;
   if (ids_in && logits_out) return BEAM_ERR_INVALID_ARG;
@@ -701,7 +751,7 @@ int beam_moe_forward_noalloc(beam_moe_handle h, int32_t T, const uint16_t* z, ui
   char* base = static_cast<char*>(scratch_of(h->device));
   if (!base) return BEAM_ERR_HIP;
   Workspace ws;
-  carve_scratch(c, T, base, &ws);
+  carve_scratch(c, h->mxfp4, T, base, &ws);
   return forward_impl(h, ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
                       offsets_out, (hipStream_t)stream, nullptr, nullptr);
 }

@@ -34,15 +34,7 @@ __device__ __forceinline__ uint32_t ld_stream_u32(const void* p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Quantisation: one thread per block of 32 values of a row.
-//   X = floor(log2 max|v|) - 2, clamped to [-127, 127]: for a BF16 maximum with
-//   exponent field ex (0 for zero and subnormals), X = max(ex - 129, -127), so the
-//   stored scale is max(ex - 2, 0).
-//   q = |v| * 2^-X (exact: a power-of-two scaling, q < 8) is rounded to the nearest
-//   E2M1 magnitude with ties to the even code and saturation at 6: the code counts
-//   the decision points q passes, strictly past a point where the lower neighbour
-//   has the even code (0.25, 1.25, 2.5, 5) and from the point on where the upper one
-//   has it (0.75, 1.75, 3.5). The sign bit is the input's.
+// Quantisation: one thread per block of 32 values of a row (mxfp4_quantize32).
 __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(int64_t nblocks, const uint16_t* __restrict__ src,
                                                              uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
@@ -51,32 +43,8 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(int64_t nblocks, co
     u32x4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld_u32x4(src + b * 32 + i * 8);
-    uint32_t amax = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = v[i][j];
-        amax = max_u32(amax, max_u32(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
-      }
-    const int ex = (int)(amax >> 7);                      // BF16 exponent field (< 255: finite)
-    const int sbyte = ex > 2 ? ex - 2 : 0;                // X + 127
-    const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-X
-    u32x4 out = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint32_t bits = hh ? (v[i][j] >> 16) : (v[i][j] & 0xFFFFu);
-          const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
-          const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
-                             (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
-          const uint32_t code = m | ((bits >> 12) & 8u);
-          const int e = i * 8 + j * 2 + hh;  // element of the block
-          out[e >> 3] |= code << (4 * (e & 7));
-        }
+    u32x4 out;
+    const uint32_t sbyte = mxfp4_quantize32(v, out);
     st_u32x4(codes + b * 16, out);
     scales[b] = (uint8_t)sbyte;
   }

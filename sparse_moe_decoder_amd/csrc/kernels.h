@@ -101,6 +101,12 @@ struct ExpertArgs {
   const uint8_t* psgu = nullptr;
   const uint8_t* pqd = nullptr;
   const uint8_t* psd = nullptr;
+  // 4-bit activations (experts_w4a4.hip): token-row codes [T, d/2] and scales [T, d/32];
+  // activation codes [T*k, f/2] and scales [T*k, f/32] by row (expert-grouped order)
+  const uint8_t* zq = nullptr;
+  const uint8_t* zqs = nullptr;
+  uint8_t* aq = nullptr;
+  uint8_t* aqs = nullptr;
 };
 
 hipError_t launch_boundary(const BoundaryArgs& a, hipStream_t s);
@@ -160,5 +166,11 @@ hipError_t launch_gateup_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s)
 hipError_t launch_down_gemm(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const uint16_t* yk,
                           uint16_t* y, hipStream_t s);
+// 4-bit activations: MXFP4 quantisation of token rows (nblocks blocks of 32) into the codes
+// and scales the W4A4 GEMM reads, and the W4A4 grouped GEMMs (d, f multiples of 512)
+hipError_t launch_quantize_rows_a4(int64_t nblocks, const uint16_t* src, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t s);
+hipError_t launch_gateup_gemm_a4(const ExpertArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm_a4(const ExpertArgs& a, int max_tiles, hipStream_t s);
 
 }  // namespace beam

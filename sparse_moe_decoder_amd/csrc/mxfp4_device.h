@@ -24,4 +24,45 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
   return r;
 }
 
+// MXFP4 quantisation of one block of 32 BF16 values (v[i] holds elements 8 i .. 8 i + 7,
+// element e in half-word e % 8) by the OCP MX v1.0 rule; returns the scale byte X + 127
+// and the codes in out (element e in nibble e % 8 of dword e / 8).
+//   X = floor(log2 max|v|) - 2, clamped to [-127, 127]: for a BF16 maximum with
+//   exponent field ex (0 for zero and subnormals), X = max(ex - 129, -127), so the
+//   stored scale is max(ex - 2, 0).
+//   q = |v| * 2^-X (exact: a power-of-two scaling, q < 8) is rounded to the nearest
+//   E2M1 magnitude with ties to the even code and saturation at 6: the code counts
+//   the decision points q passes, strictly past a point where the lower neighbour
+//   has the even code (0.25, 1.25, 2.5, 5) and from the point on where the upper one
+//   has it (0.75, 1.75, 3.5). The sign bit is the input's.
+__device__ __forceinline__ uint32_t mxfp4_quantize32(const u32x4 v[4], u32x4& out) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = v[i][j];
+      amax = max_u32(amax, max_u32(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+    }
+  const int ex = (int)(amax >> 7);                      // BF16 exponent field (< 255: finite)
+  const int sbyte = ex > 2 ? ex - 2 : 0;                // X + 127
+  const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-X
+  out = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t bits = hh ? (v[i][j] >> 16) : (v[i][j] & 0xFFFFu);
+        const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+        const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
+                           (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
+        const uint32_t code = m | ((bits >> 12) & 8u);
+        const int e = i * 8 + j * 2 + hh;  // element of the block
+        out[e >> 3] |= code << (4 * (e & 7));
+      }
+  return (uint32_t)sbyte;
+}
+
 }  // namespace beam
