@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 matrix cores
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4 matrix cores
 METRIC = "MoE-layer tokens/s (decode T=1/32/128, prefill 16K) + % HBM/MFMA peak"
 SUITE = ("decode1", "decode32", "decode128", "prefill16k", "skew32k")
 
@@ -66,6 +67,9 @@ def parse():
                    help="expert weight format: BF16, or MXFP4 (4-bit E2M1 codes with one E8M0 "
                         "scale per 32 values, quantised on the device from the BF16 weights; "
                         "BF16 activations)")
+    p.add_argument("--act", choices=("bf16", "mxfp4"), default="bf16",
+                   help="activation format of the expert GEMMs: BF16, or MXFP4 (4-bit activations "
+                        "on the FP4 matrix cores; needs --experts mxfp4)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies of BYTES (for scaling HBM "
                         "counter readings) and exit")
@@ -265,8 +269,11 @@ def measure(wl, moe, dense_h, args, mx):
 
     # roofline of the dominant kernel (expert gate/up)
     gu_us = kernel_us.get("gate_up")
-    src = source_hash(*(("experts.hip", "experts_mxfp4.hip", "common.h") if mx
+    a4 = args.act == "mxfp4"
+    src = source_hash(*(("experts_w4a4.hip", "gemm_device.h", "mxfp4_device.h", "common.h") if a4
+                        else ("experts.hip", "experts_mxfp4.hip", "common.h") if mx
                         else ("experts.hip", "common.h")))
+    ctr_name = "gate_up_w4a4" if a4 else "gate_up_mxfp4" if mx else "gate_up"
     wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
     if decode:
         # algorithmic bytes per launch: each touched expert's gate+up weights once, the
@@ -276,7 +283,7 @@ def measure(wl, moe, dense_h, args, mx):
         roof = dict(kernel="gate_up", bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                     algorithmic_bytes=round(bytes_gu))
-        roof["traffic"] = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
+        roof["traffic"] = read_traffic(ctr_name, wl.name, src)
         step_bytes = (mean_distinct * 3 * wl.f * wl.d * wbytes + (0 if dense else wl.E * wl.d * 4)
                       + T * wl.d * 2 * 6 + T * wl.k * (wl.f * 4 + wl.d * 4))
         whole = dict(algorithmic_bytes=round(step_bytes), hbm_frac=round(
@@ -285,16 +292,17 @@ def measure(wl, moe, dense_h, args, mx):
         kk = 1 if dense else wl.k
         flops_gu = 2.0 * T * kk * (2 * wl.f) * wl.d
         achieved = flops_gu / (gu_us * 1e-6) / 1e12
+        peak = FP4_PEAK_TFLOPS if a4 else BF16_PEAK_TFLOPS  # the contraction's own dtype
         roof = dict(kernel="gate_up", bound="mfma", achieved=round(achieved, 1),
-                    peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), algorithmic_flops=flops_gu)
-        roof["traffic"] = read_traffic("gate_up_mxfp4" if mx else "gate_up", wl.name, src)
+                    peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), algorithmic_flops=flops_gu)
+        roof["traffic"] = read_traffic(ctr_name, wl.name, src)
         step_flops = 2.0 * T * kk * 3 * wl.f * wl.d
         gemm_us = gu_us + (kernel_us.get("down") or 0.0)
         whole = dict(expert_flops=step_flops,
-                     mfma_frac=round(step_flops / (best_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     mfma_frac=round(step_flops / (best_ms * 1e-3) / 1e12 / peak, 4),
                      expert_gemms_mfma_frac=round(
-                         step_flops / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4))
+                         step_flops / (gemm_us * 1e-6) / 1e12 / peak, 4))
     entry = {
         "tokens": T, "ms_per_step": round(best_ms, 5), "tokens_per_s": round(T / (best_ms / 1e3), 2),
         "mode": mode, "ms_eager": round(ms_eager, 5),
@@ -332,6 +340,9 @@ def main():
 
     torch.cuda.set_device(0)
     mx = args.experts == "mxfp4"
+    if args.act == "mxfp4" and not mx:
+        print("--act mxfp4 needs --experts mxfp4", file=sys.stderr)
+        sys.exit(2)
     names = [args.workload] if args.workload else list(SUITE)
     wls = [synth.WORKLOADS[n] for n in names]
     dense = names[0].startswith("dense")
@@ -363,6 +374,8 @@ def main():
             cfg = sd.moe_config(wl, max_tokens=need)
             handles[key] = (beam.BeamMoE(cfg, W, b, None, None, None, mxfp4=fp4) if mx
                             else beam.BeamMoE(cfg, W, b, wg, wu, wd))
+            if args.act == "mxfp4":
+                handles[key].set_activation_format(beam.ACT_MXFP4)
     del wg, wu, wd, fp4
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -384,13 +397,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(head, args.cpu_sample, mxfp4=mx)
+        cpu = cpu_baseline(head, args.cpu_sample, mxfp4=mx, act4=args.act == "mxfp4")
 
     e = entries[head.name]
     config = {
         "workload": head.name, "tokens": head.T, "hidden": head.d, "experts": head.E,
         "groups": head.G, "groups_kept": head.kg, "topk": head.k, "d_ff": head.f,
-        "experts_format": args.experts, "step": args.step,
+        "experts_format": args.experts, "activations_format": args.act, "step": args.step,
     }
     config.update({k: v for k, v in e.items() if k != "roofline"})
     if len(entries) > 1:
@@ -406,7 +419,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not mx else "bf16 (mxfp4 expert weights)",
+        "dtype": ("mxfp4 (4-bit activations and weights, FP32 accumulation)" if args.act == "mxfp4"
+                  else "bf16 (mxfp4 expert weights)" if mx else "bf16"),
         "data": "synthetic (seeded counter-based generator; random-init weights of Beam's MoE layer)",
         "config": config,
         "roofline": e["roofline"],
@@ -415,7 +429,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, sample=None, mxfp4=False):
+def cpu_baseline(wl, sample=None, mxfp4=False, act4=False):
     """The CPU oracle, as it is, on a bounded sample of the same workload: each
     sampled token goes through boundary, router, routing, its experts and the
     combine, single-threaded per token; tokens run in a thread pool of the machine's CPU
@@ -471,9 +485,9 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
                         log(f"cpu baseline: quantised {i + 1} of {len(need)} experts")
 
         def one(i):
-            out = oracle.sublayer(hh[i], xx[i], wpost, wpre, wl.n, wl.eps, Wr, bias, wl.G, wl.kg,
-                                  wl.k, wl.scale, weights.__getitem__)
-            return out["y"]
+            _, z = oracle.boundary(hh[i], xx[i], wpost, wpre, wl.n, wl.eps)
+            ids, w, _, _ = oracle.topk(oracle.router(z, Wr), bias, wl.G, wl.kg, wl.k, wl.scale)
+            return oracle.moe_experts(z, ids, w, wl.E, weights.__getitem__, mx_act=act4)[0]
         what = (f"the whole path (boundary, FP32 router, grouped top-k, {wl.k} SwiGLU experts, "
                 f"combine)")
 
@@ -491,7 +505,7 @@ def cpu_baseline(wl, sample=None, mxfp4=False):
                 log(f"cpu baseline: {done} of {len(hh)} tokens")
     dt = time.perf_counter() - t0
     log(f"cpu baseline: {len(hh)} tokens in {dt:.2f}s on {threads} threads")
-    fmt = " (mxfp4 experts)" if mxfp4 else ""
+    fmt = " (mxfp4 activations and experts)" if act4 else " (mxfp4 experts)" if mxfp4 else ""
     return dict(value=round(len(hh) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{len(hh)} tokens of {wl.name}{fmt}, each through {what} "
                        f"single-threaded, {threads} tokens at a time; {dt:.1f} s wall",
