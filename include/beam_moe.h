@@ -141,7 +141,10 @@ enum { BEAM_ACT_BF16 = 0, BEAM_ACT_MXFP4 = 1 };
  * multiply the 4-bit operands on the scaled FP4 matrix cores (each 32-value block's
  * products are exact; FP32 accumulation); g, u, the routing weight, the BF16 rounding of
  * each expert row and the combine are as in beam_moe_forward. The format applies to every
- * T. Takes effect for calls made after it returns; allocates and enqueues nothing.
+ * T; for T <= 128 the same values are multiplied on the 4-bit weight-streaming passes (the
+ * round trips of z and act, which are BF16 numbers, times the exactly dequantised weights),
+ * since there the weight stream, not the arithmetic, bounds the step. Takes effect for calls
+ * made after it returns; allocates and enqueues nothing.
  * Returns BEAM_ERR_UNSUPPORTED for BEAM_ACT_MXFP4 on a BF16-weight handle and
  * BEAM_ERR_INVALID_ARG for a dense handle or another format.
  */

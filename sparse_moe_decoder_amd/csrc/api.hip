@@ -29,10 +29,11 @@ enum KernelId {
   K_GATEUP,
   K_DOWN,
   K_COMBINE,
+  K_QUANT,  // 4-bit activations: the token rows' and activations' quantisation
   K_COUNT
 };
-const char* const kKernelNames[K_COUNT] = {"boundary", "router", "topk",   "permute",
-                                           "gate_up",  "down",   "combine"};
+const char* const kKernelNames[K_COUNT] = {"boundary", "router",  "topk",    "permute",
+                                           "gate_up",  "down",    "combine", "quantize"};
 
 struct ProfRecord {
   int id;
@@ -110,12 +111,14 @@ struct Workspace {
   uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
   int32_t* block_cnt = nullptr;   // [nb * E], nb = ceil(slots / kPermChunk)
   int32_t* block_base = nullptr;  // [nb * E]
-  uint16_t* act = nullptr;        // [T * k, f]; with 4-bit activations: their codes
-                                  // [T * k, f/2], then scales [T * k, f/32]
+  uint16_t* act = nullptr;        // [T * k, f]
   uint16_t* yk = nullptr;         // [T * k, d]
   uint8_t* zq = nullptr;          // 4-bit activations: token-row codes [T, d/2]
   uint8_t* zqs = nullptr;         //   and scales [T, d/32]
-  uint8_t* aqs = nullptr;         // 4-bit activations: where the activation scales start in act
+  uint8_t* aq = nullptr;          // 4-bit activations: activation codes [T * k, f/2]
+  uint8_t* aqs = nullptr;         //   and scales [T * k, f/32]
+  uint16_t* zr = nullptr;         // 4-bit activations, T <= kStreamMaxT: the token rows' MXFP4
+                                  //   round trip [T, d] BF16 (the weight streams' input)
 };
 
 struct beam_moe_ctx {
@@ -215,7 +218,9 @@ size_t carve_scratch(const beam_moe_config& c, bool mx, int T, char* base, Works
   if (mx) {
     take(&w.zq, (size_t)T * d / 2);
     take(&w.zqs, (size_t)T * d / 32);
-    if (base) w.aqs = reinterpret_cast<uint8_t*>(w.act) + slots * f / 2;
+    take(&w.aq, slots * f / 2);
+    take(&w.aqs, slots * f / 32);
+    if (T <= kStreamMaxT) take(&w.zr, (size_t)T * d * 2);
   }
   if (ws) *ws = w;
   return off;
@@ -360,18 +365,42 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
   if (h->act_mx) {  // 4-bit activations: quantise the token rows, then the W4A4 GEMMs
     ea.zq = ws.zq;
     ea.zqs = ws.zqs;
-    ea.aq = reinterpret_cast<uint8_t*>(ws.act);
+    ea.aq = ws.aq;
     ea.aqs = ws.aqs;
-    const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+    const bool stream = T <= kStreamMaxT;
     {
-      ProfScope ps(K_GATEUP, s);
-      if (launch_quantize_rows_a4((int64_t)T * (c.hidden / 32), z, ws.zq, ws.zqs, s) !=
-              hipSuccess ||
-          launch_gateup_gemm_a4(ea, max_tiles, s) != hipSuccess)
+      ProfScope ps(K_QUANT, s);
+      if (launch_quantize_rows_a4((int64_t)T * (c.hidden / 32), z, ws.zq, ws.zqs,
+                                  stream ? ws.zr : nullptr, s) != hipSuccess)
         return BEAM_ERR_HIP;
     }
-    ProfScope ps(K_DOWN, s);
-    if (launch_down_gemm_a4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    if (stream) {
+      // the 4-bit weight streams on the rows' round trip, the activations' round trip between
+      // them: the same values the W4A4 GEMMs multiply
+      const int max_active = slots < E ? slots : E;
+      ExpertArgs es = ea;
+      es.z = ws.zr;
+      {
+        ProfScope ps(K_GATEUP, s);
+        if (launch_gateup_fp4(es, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+      }
+      {
+        ProfScope ps(K_QUANT, s);
+        if (launch_act_round_trip_a4(slots, c.d_ff, ws.offsets + E, ws.act, ws.aq, ws.aqs, s) !=
+            hipSuccess)
+          return BEAM_ERR_HIP;
+      }
+      ProfScope ps(K_DOWN, s);
+      if (launch_down_fp4(es, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
+    } else {
+      const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
+      {
+        ProfScope ps(K_GATEUP, s);
+        if (launch_gateup_gemm_a4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+      }
+      ProfScope ps(K_DOWN, s);
+      if (launch_down_gemm_a4(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
   } else if (h->mxfp4 && T > kStreamMaxT) {  // 4-bit grouped GEMMs
     const int max_tiles = (slots + kGemmBM - 1) / kGemmBM + (slots < E ? slots : E);
     {
@@ -551,9 +580,11 @@ int beam_moe_init_mxfp4(const beam_moe_config* cfg, const float* router_w,
                             (int)E, (int)f, (int)d, h->qgu, h->sgu, h->qd, h->sd, s) != hipSuccess)
       return BEAM_ERR_HIP;
     const size_t T = cfg->max_tokens;
-    if (!dev_alloc(h, &h->ws.zq, T * d / 2) || !dev_alloc(h, &h->ws.zqs, T * d / 32))
+    const size_t S = T * cfg->topk, Ts = T < (size_t)kStreamMaxT ? T : (size_t)kStreamMaxT;
+    if (!dev_alloc(h, &h->ws.zq, T * d / 2) || !dev_alloc(h, &h->ws.zqs, T * d / 32) ||
+        !dev_alloc(h, &h->ws.aq, S * f / 2) || !dev_alloc(h, &h->ws.aqs, S * f / 32) ||
+        !dev_alloc(h, &h->ws.zr, Ts * d))
       return BEAM_ERR_OOM;
-    h->ws.aqs = reinterpret_cast<uint8_t*>(h->ws.act) + T * cfg->topk * f / 2;
     if (!dev_alloc(h, &h->pqgu, E * 2 * f * d / 2) || !dev_alloc(h, &h->psgu, E * 2 * f * d / 32) ||
         !dev_alloc(h, &h->pqd, E * d * f / 2) || !dev_alloc(h, &h->psd, E * d * f / 32))
       return BEAM_ERR_OOM;
@@ -587,7 +618,7 @@ int beam_moe_inspect(beam_moe_handle h, int32_t what, const void** ptr) {
   const Workspace& ws = h->ws;
   switch (what) {
     case BEAM_INSPECT_ACT: *ptr = ws.act; break;
-    case BEAM_INSPECT_ACT_CODES: *ptr = h->act_mx ? (const void*)ws.act : nullptr; break;
+    case BEAM_INSPECT_ACT_CODES: *ptr = h->act_mx ? (const void*)ws.aq : nullptr; break;
     case BEAM_INSPECT_ACT_SCALES: *ptr = h->act_mx ? (const void*)ws.aqs : nullptr; break;
     case BEAM_INSPECT_Z_CODES: *ptr = ws.zq; break;
     case BEAM_INSPECT_Z_SCALES: *ptr = ws.zqs; break;

@@ -39,12 +39,22 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 // Block codes in natural order (dword q = K values 8 q ..) -> GEMM order
 __device__ __forceinline__ u32x4 gemm_order(u32x4 c) { return u32x4{c[0], c[2], c[1], c[3]}; }
 
+// The exact BF16 values of one block's codes (natural order) and scale byte: v[i] holds
+// elements 8 i .. 8 i + 7 (every E2M1 value times a power of two is a BF16 number).
+__device__ __forceinline__ void mxfp4_dequantize32(const u32x4& codes, uint32_t sbyte, u32x4 v[4]) {
+  const float sc = e8m0_scale(sbyte);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = fp4x8_to_bf16(codes[i], sc);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Token-row quantisation: z [T, d] BF16 -> codes [T, d/2] (GEMM order) and scales [T, d/32];
-// one thread per block of 32 values.
+// with rt, also the rows' exact round trip (the dequantised codes) as BF16 [T, d]. One thread
+// per block of 32 values.
 __global__ __launch_bounds__(256) void quantize_rows_a4_kernel(int64_t nblocks, const uint16_t* __restrict__ src,
                                                                uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ scales) {
+                                                               uint8_t* __restrict__ scales,
+                                                               uint16_t* __restrict__ rt) {
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
        b += (int64_t)gridDim.x * blockDim.x) {
     u32x4 v[4];
@@ -54,16 +64,58 @@ __global__ __launch_bounds__(256) void quantize_rows_a4_kernel(int64_t nblocks, 
     const uint32_t sbyte = mxfp4_quantize32(v, out);
     st_u32x4(codes + b * 16, gemm_order(out));
     scales[b] = (uint8_t)sbyte;
+    if (rt) {
+      mxfp4_dequantize32(out, sbyte, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_u32x4(rt + b * 32 + i * 8, v[i]);
+    }
   }
 }
 
 hipError_t launch_quantize_rows_a4(int64_t nblocks, const uint16_t* src, uint8_t* codes,
-                                   uint8_t* scales, hipStream_t s) {
+                                   uint8_t* scales, uint16_t* rt, hipStream_t s) {
   int64_t g = (nblocks + 255) / 256;
   if (g > 65536) g = 65536;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(quantize_rows_a4_kernel, dim3((unsigned)g), dim3(256), 0, s, nblocks, src,
-                     codes, scales);
+                     codes, scales, rt);
+  return hipGetLastError();
+}
+
+// The activations of the weight-streaming passes (T <= 128), quantised in place: each valid
+// row of act [rows, f] BF16 (expert-grouped order; *nvalid rows are valid) is replaced by its
+// MXFP4 round trip, and its codes (GEMM order) and scales are kept in codes / scales — the
+// values and codes the W4A4 GEMM epilogue produces from the same BF16 activations.
+__global__ __launch_bounds__(256) void act_round_trip_a4_kernel(int64_t nblocks, int f,
+                                                                const int32_t* __restrict__ nvalid,
+                                                                uint16_t* __restrict__ act,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales) {
+  const int64_t bpr = f / 32;
+  const int64_t nb = (int64_t)(*nvalid) * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks && b < nb;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld_u32x4(act + b * 32 + i * 8);
+    u32x4 out;
+    const uint32_t sbyte = mxfp4_quantize32(v, out);
+    st_u32x4(codes + b * 16, gemm_order(out));
+    scales[b] = (uint8_t)sbyte;
+    mxfp4_dequantize32(out, sbyte, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_u32x4(act + b * 32 + i * 8, v[i]);
+  }
+}
+
+hipError_t launch_act_round_trip_a4(int64_t rows, int f, const int32_t* nvalid, uint16_t* act,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nblocks = rows * (f / 32);
+  int64_t g = (nblocks + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(act_round_trip_a4_kernel, dim3((unsigned)g), dim3(256), 0, s, nblocks, f,
+                     nvalid, act, codes, scales);
   return hipGetLastError();
 }
 

@@ -169,7 +169,11 @@ hipError_t launch_combine(int T, int k, int d, int E, const int32_t* ids, const 
 // 4-bit activations: MXFP4 quantisation of token rows (nblocks blocks of 32) into the codes
 // and scales the W4A4 GEMM reads, and the W4A4 grouped GEMMs (d, f multiples of 512)
 hipError_t launch_quantize_rows_a4(int64_t nblocks, const uint16_t* src, uint8_t* codes,
-                                   uint8_t* scales, hipStream_t s);
+                                   uint8_t* scales, uint16_t* rt, hipStream_t s);
+// the weight-streaming passes' activations [rows, f] replaced by their MXFP4 round trip (the
+// first *nvalid rows), codes and scales kept
+hipError_t launch_act_round_trip_a4(int64_t rows, int f, const int32_t* nvalid, uint16_t* act,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_gateup_gemm_a4(const ExpertArgs& a, int max_tiles, hipStream_t s);
 hipError_t launch_down_gemm_a4(const ExpertArgs& a, int max_tiles, hipStream_t s);
 

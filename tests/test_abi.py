@@ -103,7 +103,7 @@ def test_handle_calls_reject_null_handle(L):
 
 
 def test_profile_api_without_records(L):
-    assert L.beam_kernel_count() == 7
+    assert L.beam_kernel_count() == 8
     assert L.beam_kernel_name(4) == b"gate_up"
     assert L.beam_kernel_name(99) is None
     ms, n = ctypes.c_double(), ctypes.c_int64()

@@ -10,7 +10,8 @@ matrix cores) against oracle O8, stage by stage on identical inputs:
   3. down + weight + combine: the GPU's y equals the oracle's down half and combine on the
      GPU's own activation codes, to the BF16 bar (rel-L2 <= 2e-3, max-abs rule);
 and the composed O8 (oracle from z alone) reported, asserted only against gross error.
-All calls go through the C ABI."""
+T <= 128 runs on the 4-bit weight-streaming passes (with the round trips of z and act), larger
+T on the W4A4 GEMMs; both are checked the same way. All calls go through the C ABI."""
 import numpy as np
 import pytest
 
