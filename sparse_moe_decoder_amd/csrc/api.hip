@@ -106,7 +106,7 @@ struct Workspace {
   int32_t* n_active = nullptr; // [1]
   int32_t* tile_start = nullptr;  // [E + 1]
   int32_t* perm = nullptr;        // [T * k]
-  uint32_t* route_done = nullptr;  // [1] workgroup counter of the fused small-batch routing:
+  uint32_t* route_done = nullptr;  // [kRouteDoneWords] arrival counters of the fused routing:
                                    // zero before its first launch, left zero by every launch
   uint64_t* route_sc = nullptr;    // [16 * E] its published (score, biased score) pairs
   int32_t* block_cnt = nullptr;   // [nb * E], nb = ceil(slots / kPermChunk)
@@ -152,10 +152,12 @@ struct beam_moe_ctx {
 // such call on that GPU shares it. Host code never passes the array's name to a kernel or a
 // copy (on the host it only names the symbol): it uses the device address looked up once per
 // device by hipGetSymbolAddress while that device is current.
-//   bytes [0, 256): the fused small-batch routing's workgroup counter (zeroed when the address
-//                   is looked up; every launch that uses it leaves it zero again)
-//   bytes [256, kScratchBytes): the per-call workspace of one forward (carve_scratch)
+//   bytes [0, kScratchCounterBytes): the fused small-batch routing's arrival counters (zeroed
+//                   when the address is looked up; every launch that uses them leaves them zero)
+//   bytes [kScratchCounterBytes, kScratchBytes): the per-call workspace of one forward
+//                   (carve_scratch)
 constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchCounterBytes = (kRouteDoneWords * 4 + 255) & ~(size_t)255;
 constexpr int kScratchMaxDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -175,7 +177,8 @@ void* scratch_setup(int device, hipStream_t s) {
     (void)hipGetLastError();
     return nullptr;
   }
-  if (hipMemsetAsync(ptr, 0, 256, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+  if (hipMemsetAsync(ptr, 0, kScratchCounterBytes, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
@@ -190,11 +193,11 @@ void* scratch_of(int device) {
 }
 
 // Lay out the workspace of a T-token forward in the scratch area at `base` (256-byte
-// aligned pieces after the counter). Returns the bytes used (base may be null to size it).
+// aligned pieces after the counters). Returns the bytes used (base may be null to size it).
 size_t carve_scratch(const beam_moe_config& c, bool mx, int T, char* base, Workspace* ws) {
   const size_t E = c.n_experts, d = c.hidden, f = c.d_ff, slots = (size_t)T * c.topk;
   const size_t nb = (slots + kPermChunk - 1) / kPermChunk;
-  size_t off = 256;
+  size_t off = kScratchCounterBytes;
   auto take = [&](auto** p, size_t bytes) {
     if (base) *p = reinterpret_cast<std::remove_pointer_t<decltype(p)>>(base + off);
     off += (bytes + 255) & ~(size_t)255;
@@ -497,7 +500,7 @@ int init_handle(const beam_moe_config* cfg, const float* router_w, const float* 
             dev_alloc(h, &h->ws.w, slots) && dev_alloc(h, &h->ws.counts, E) &&
             dev_alloc(h, &h->ws.offsets, E + 1) && dev_alloc(h, &h->ws.active, E) &&
             dev_alloc(h, &h->ws.n_active, 1) && dev_alloc(h, &h->ws.tile_start, E + 1) &&
-            dev_alloc(h, &h->ws.perm, slots) && dev_alloc(h, &h->ws.route_done, 1) &&
+            dev_alloc(h, &h->ws.perm, slots) && dev_alloc(h, &h->ws.route_done, kRouteDoneWords) &&
             dev_alloc(h, &h->ws.route_sc, (size_t)kFusedRouteMaxT * E) &&
             dev_alloc(h, &h->ws.block_cnt, nb * E) &&
             dev_alloc(h, &h->ws.block_base, nb * E) && dev_alloc(h, &h->ws.act, slots * f) &&
@@ -521,7 +524,7 @@ int init_handle(const beam_moe_config* cfg, const float* router_w, const float* 
     e = router_bias ? hipMemcpyAsync(h->bias, router_bias, E * sizeof(float),
                                      hipMemcpyDeviceToDevice, s)
                     : hipMemsetAsync(h->bias, 0, E * sizeof(float), s);
-  if (e == hipSuccess) e = hipMemsetAsync(h->ws.route_done, 0, sizeof(uint32_t), s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->ws.route_done, 0, kRouteDoneWords * sizeof(uint32_t), s);
   if (e == hipSuccess && E % 64 == 0 && router_w)
     e = launch_repack_router(router_w, h->router_x3, (int)E, (int)d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);

@@ -12,6 +12,10 @@ constexpr int kSplitDownMaxT = 16;  // largest T whose down pass splits K over f
 constexpr int kDenseSplitK = 4;     // dense layers, T <= 16: workgroups per down column tile
 constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
 constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
+// its arrival count: a top counter and kRouteSub sub-counters, kRouteCounterStride words apart
+constexpr int kRouteSub = 16;
+constexpr int kRouteCounterStride = 64;
+constexpr int kRouteDoneWords = (1 + kRouteSub) * kRouteCounterStride;
 constexpr int kBoundaryWgMaxD = 8192;   // boundary rows up to this width: a workgroup per row
 
 struct BoundaryArgs {
@@ -147,8 +151,8 @@ hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 // grouped top-k + permutation in one launch; needs T * k <= kPermChunk
 hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipStream_t s);
 // Router + grouped top-k + grouping in one launch for T <= 16 and T * k <= 64 (E
-// workgroups; `done` is a zeroed device counter owned by the caller, left zeroed;
-// `sc` is caller-owned scratch of T * E 64-bit words for the published scores).
+// workgroups; `done` is caller-owned, zeroed device memory of kRouteDoneWords words, left
+// zeroed; `sc` is caller-owned scratch of T * E 64-bit words for the published scores).
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
                                    uint32_t* done, uint64_t* sc, hipStream_t s);
 // one token (d <= 8192): the boundary of that token inside the same launch; z goes to

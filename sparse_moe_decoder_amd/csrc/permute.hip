@@ -361,14 +361,142 @@ __global__ __launch_bounds__(1024) void route_permute_tiny_kernel(TopkArgs ta, P
   group_slots_wave(a, ids_lds, lane, reinterpret_cast<int*>(c_lds[0]), reinterpret_cast<int*>(c_lds[1]));
 }
 
+// Arrival count of the fused routing in two levels: workgroup b counts itself on
+// sub-counter b % kRouteSub, the last arrival there counts that sub-counter on the top
+// counter, and each counter's last arrival resets it for the next launch. Atomics on one
+// address are serialised where they meet, so spreading the E arrivals over sub-counters
+// shortens the wait of the last one. Thread 0 calls it after its workgroup's stores have
+// completed; it returns true in exactly one workgroup, the last of all nb.
+__device__ __forceinline__ bool count_arrival(uint32_t* done, int b, int nb) {
+  const int j = b % kRouteSub;
+  const uint32_t nj = (uint32_t)((nb - j + kRouteSub - 1) / kRouteSub);
+  uint32_t* sub = done + (1 + j) * kRouteCounterStride;
+  if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != nj - 1)
+    return false;
+  __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t nsub = (uint32_t)(nb < kRouteSub ? nb : kRouteSub);
+  if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != nsub - 1)
+    return false;
+  __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Whether one token's top-k and grouping can run on a whole workgroup, one thread per
+// expert: E <= 256, power-of-two groups of 2 to 64 experts, kg * k <= 256.
+__device__ __forceinline__ bool one_token_wg_ok(const TopkArgs& a) {
+  const int gs = a.E / a.G;
+  return a.T == 1 && a.E <= 256 && gs >= 2 && gs <= 64 && (gs & (gs - 1)) == 0 &&
+         a.kg * a.k <= 256;
+}
+
+struct OneTokenLds {
+  uint64_t key[256];   // expert e: order key of its biased score, then ~e
+  uint64_t gkey[128];  // group g: order key of its score, then ~g
+  uint64_t skey[256];  // survivors of the kept groups, at (group rank) * k + (rank in group)
+  float s[64];         // slot j: the selected expert's score
+  int32_t id[64];      //   and its index
+};
+
+// One token's grouped top-k and grouping by the 256 threads of a workgroup, thread e
+// holding expert e. The selection and the weights are topk_token's, found by counting
+// instead of in rounds: an entry's rank is the number of entries ahead of it in (value
+// desc, index asc) order, which the 64-bit keys (order key, then the inverted index)
+// compare directly. The groups' ranks keep kg groups. An expert among the top k of the
+// kept experts is among the top k of its own group, so each expert's rank within its
+// group leaves at most k survivors per kept group, and the survivors' ranks among
+// themselves are the slots. The grouping of the k slots (k distinct experts, one row
+// each) follows in the same pass: a selected expert's row is the number of selected
+// experts below it, and so is every expert's offset.
+__device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const uint64_t* sc,
+                                   OneTokenLds& L) {
+  const int tid = threadIdx.x, E = ta.E, G = ta.G, gs = E / G, k = ta.k, kg = ta.kg;
+  const int nsk = kg * k;
+  const bool valid = tid < E;
+  float s = 0.0f, c = -INFINITY;
+  if (valid) {
+    const uint64_t p = __hip_atomic_load(sc + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s = __uint_as_float((uint32_t)p);
+    c = __uint_as_float((uint32_t)(p >> 32));
+  }
+  if (tid < nsk) L.skey[tid] = 0;
+  const uint64_t key = valid ? ((uint64_t)f32_order_key(c) << 32) | (uint32_t)~tid : 0;
+  L.key[tid] = key;
+  // group score: the sum of the group's two largest biased scores (a group's threads are
+  // adjacent lanes of one wave)
+  float m1 = c, m2 = -INFINITY;
+  for (int off = 1; off < gs; off <<= 1) {
+    const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
+    top2_merge(m1, m2, o1, o2);
+  }
+  const int g = tid / gs;
+  if (valid && tid % gs == 0)
+    L.gkey[g] = ((uint64_t)f32_order_key(m1 + m2) << 32) | (uint32_t)~g;
+  __syncthreads();
+  int rg = kg;
+  if (valid) {
+    const uint64_t mine = L.gkey[g];
+    rg = 0;
+    for (int q = 0; q < G; ++q) rg += L.gkey[q] > mine ? 1 : 0;
+  }
+  bool surv = false;
+  int ri = 0;
+  if (rg < kg) {
+    const uint64_t* gk = L.key + g * gs;
+    for (int q = 0; q < gs; ++q) ri += gk[q] > key ? 1 : 0;
+    surv = ri < k;
+    if (surv) L.skey[rg * k + ri] = key;
+  }
+  __syncthreads();
+  int slot = -1;
+  if (surv) {
+    int r = 0;
+    for (int q = 0; q < nsk; ++q) r += L.skey[q] > key ? 1 : 0;
+    if (r < k) {
+      slot = r;
+      L.s[r] = s;
+      L.id[r] = tid;
+    }
+  }
+  __syncthreads();
+  if (tid < k) {
+    float den = L.s[0];
+    for (int j = 1; j < k; ++j) den = den + L.s[j];  // slot order
+    const float wj = (L.s[tid] / den) * ta.scale;
+    const int e = L.id[tid];
+    ta.ids[tid] = e;
+    ta.w[tid] = wj;
+    if (ta.ids2) ta.ids2[tid] = e;
+    if (ta.w2) ta.w2[tid] = wj;
+  }
+  if (valid) {
+    int off = 0;
+    for (int j = 0; j < k; ++j) off += L.id[j] < tid ? 1 : 0;
+    pa.counts[tid] = slot >= 0 ? 1 : 0;
+    pa.offsets[tid] = off;
+    if (pa.offsets2) pa.offsets2[tid] = off;
+    pa.tile_start[tid] = off;  // one tile per selected expert
+    if (slot >= 0) {
+      pa.active[off] = tid;
+      pa.perm[off] = slot;
+      if (pa.perm2) pa.perm2[off] = slot;
+    }
+  }
+  if (tid == 0) {
+    pa.offsets[E] = k;
+    if (pa.offsets2) pa.offsets2[E] = k;
+    pa.tile_start[E] = k;
+    *pa.n_active = k;
+  }
+}
+
 // Router, grouped top-k and grouping of a small batch (T <= 16 tokens, T * k <= 64
 // slots) in one launch: one workgroup per expert computes its logits exactly as the
 // stand-alone small-batch router does, writes them out, and publishes each token's
 // (score, biased score) pair for its expert (computed as the top-k computes them)
 // with device-coherent (write-through) stores; it waits for those stores to
-// complete, then counts itself done on `done`. The workgroup that counts last
-// (every other one has published) resets the counter for the next launch and runs
-// the top-k (one wave per token, coherent loads of the pairs) and the grouping. No
+// complete, then counts itself done (count_arrival). The workgroup that counts last
+// (every other one has published) runs the top-k (coherent loads of the pairs; one
+// wave per token, or the whole workgroup for one token) and the grouping. No
 // workgroup waits on another.
 // BOUNDARY (one token): the sublayer boundary runs inside the same launch. Each
 // workgroup forms the token's z from h and x itself, in the boundary kernel's exact
@@ -383,6 +511,7 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   __shared__ __attribute__((aligned(16))) float c_lds[4][256];
   __shared__ int32_t sel[4][32];
   __shared__ int32_t ids_lds[64];
+  __shared__ OneTokenLds one;
   __shared__ int is_last;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
@@ -415,16 +544,16 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this workgroup's stores are complete
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == gridDim.x - 1;
-  }
+  if (tid == 0) is_last = count_arrival(done, blockIdx.x, gridDim.x);
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // every workgroup has read h by now, so h_out may be h itself
   if constexpr (BOUNDARY) boundary_row_4waves_store_h(ba, 0, brow);
+  if (one_token_wg_ok(ta)) {
+    route_one_token_wg(ta, pa, sc, one);
+    return;
+  }
   for (int t = wv; t < ta.T; t += 4) {
     topk_token<true>(ta, t, c_lds[wv], sel[wv], lane, sc);
     if (lane < ta.k) ids_lds[t * ta.k + lane] = sel[wv][lane];
