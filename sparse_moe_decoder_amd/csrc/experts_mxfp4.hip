@@ -460,8 +460,9 @@ __global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
 // Every pass uses 16-row MFMA blocks: rows do not interact in an MFMA, so the block
 // height changes no result, and most experts hold few rows at these batch sizes.
 // Tiles per wave and ring depths (measured on Beam's shapes): gate/up one tile per
-// wave up to 16 tokens (more workgroups for the few experts), two above; down four
-// tiles per wave in both ranges, with a ring of two quads from 17 tokens on.
+// wave up to 16 tokens (more workgroups for the few experts), two above; down two
+// tiles per wave up to 16 tokens, four above with a ring of two quads. Deeper rings
+// at one token (five quads, all of a wave's quarter) cost occupancy and measured slower.
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int kqw = a.d / 128 / 4;  // >= 1; U = 2 when it divides
   if (a.T <= 16) {
@@ -482,8 +483,8 @@ hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s)
 
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   if (a.T <= kSplitDownMaxT) {
-    dim3 g((unsigned)(max_active * (a.d / 64))), blk(256);
-    hipLaunchKernelGGL((down_split_fp4_kernel<1, 4>), g, blk, 0, s, a);
+    dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
+    hipLaunchKernelGGL((down_split_fp4_kernel<1, 2>), g, blk, 0, s, a);
   } else {
     const int KQ = a.f / 128;
     dim3 g((unsigned)(max_active * (a.d / 256))), blk(256);

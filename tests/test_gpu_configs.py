@@ -4,6 +4,9 @@
   group, and one expert per group;
 - a single group of 64 experts (16 lanes per group), 64 groups of 4, the largest k (32);
 - E not a multiple of 64 (the FP32 router serves every batch size);
+- the one-token routing by a whole workgroup (power-of-two groups of 2 to 64 experts) with
+  its two-level arrival count: sub-counters with unequal arrivals (24 experts), and fewer
+  experts than sub-counters (8);
 - batch sizes that take each routing, grouping and expert path: the one-launch
   small-batch routing (T <= 16 and T*k <= 64), the one-workgroup grouping, the
   multi-block grouping, the split and the streaming down passes, the grouped GEMMs.
@@ -28,6 +31,8 @@ CONFIGS = [
     Workload("e64g1", T=1, d=512, E=64, G=1, kg=1, k=8, f=256),      # one group, 16 lanes
     Workload("e256g64", T=1, d=256, E=256, G=64, kg=16, k=32, f=256),  # k = 32
     Workload("e128g4", T=1, d=768, E=128, G=4, kg=2, k=8, f=512),    # 8 lanes per group
+    Workload("e24g3", T=1, d=256, E=24, G=3, kg=2, k=3, f=256),      # uneven arrival counts
+    Workload("e8g2", T=1, d=256, E=8, G=2, kg=1, k=2, f=256),        # fewer experts than counters
 ]
 MAX_T = 300
 T_FORWARD = (1, 7, 40, MAX_T)
