@@ -317,6 +317,12 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
 
   const int32_t* ids = ids_in;
   const float* w = w_in;
+  // 4-bit activations on the weight streams: the fused routing launches quantise the rows
+  const bool a4_stream = h->act_mx && T <= kStreamMaxT;
+  const bool fused_route =
+      !ids_in && (bnd || (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots));
+  const RowQuantArgs rq = a4_stream && fused_route ? RowQuantArgs{ws.zq, ws.zqs, ws.zr}
+                                                   : RowQuantArgs{nullptr, nullptr, nullptr};
   PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, ws.counts,
               ws.offsets, ws.perm, ws.block_cnt, ws.block_base, ws.active, ws.n_active,
               ws.tile_start, perm_out, offsets_out};
@@ -329,12 +335,13 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
     if (bnd) {
       ProfScope ps(K_ROUTER, s);  // boundary, router, top-k and grouping in one launch
       RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_boundary_route_fused(*bnd, ra, ta, pa, ws.route_done, ws.route_sc, s) != hipSuccess)
+      if (launch_boundary_route_fused(*bnd, ra, ta, pa, ws.route_done, ws.route_sc, rq, s) !=
+          hipSuccess)
         return BEAM_ERR_HIP;
     } else if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
       ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
       RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_route_fused_tiny(ra, ta, pa, ws.route_done, ws.route_sc, s) != hipSuccess)
+      if (launch_route_fused_tiny(ra, ta, pa, ws.route_done, ws.route_sc, rq, s) != hipSuccess)
         return BEAM_ERR_HIP;
     } else if (slots <= kPermChunk) {
       int st = run_router(h, T, z, lg, s);
@@ -370,8 +377,8 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
     ea.zqs = ws.zqs;
     ea.aq = ws.aq;
     ea.aqs = ws.aqs;
-    const bool stream = T <= kStreamMaxT;
-    {
+    const bool stream = a4_stream;
+    if (!rq.zq) {
       ProfScope ps(K_QUANT, s);
       if (launch_quantize_rows_a4((int64_t)T * (c.hidden / 32), z, ws.zq, ws.zqs,
                                   stream ? ws.zr : nullptr, s) != hipSuccess)

@@ -13,9 +13,10 @@
 // every product of two E2M1 values times the two scales is exact, so each 32-value block
 // contributes its exact dot product and only the FP32 accumulation rounds.
 //
-// Code byte order inside a block's 16 bytes ("GEMM order"): dword p holds K values
-// 8 q .. 8 q + 7 with q = (0, 2, 1, 3)[p] — the order the 4-bit weights of the grouped-GEMM
-// layout (experts.hip) have once a lane undoes their half swap, so A and B lanes agree.
+// Code byte order inside a block's 16 bytes ("GEMM order", gemm_order in mxfp4_device.h):
+// dword p holds K values 8 q .. 8 q + 7 with q = (0, 2, 1, 3)[p] — the order the 4-bit
+// weights of the grouped-GEMM layout (experts.hip) have once a lane undoes their half swap,
+// so A and B lanes agree.
 //
 // The GEMM is the BF16 engine's (experts.hip) with a 128-wide K block per LDS stage
 // instead of 32: 256 x 256 tiles per 8-wave workgroup, wave w = 4 wm + wn owning 32-row
@@ -36,17 +37,6 @@ namespace beam {
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
-// Block codes in natural order (dword q = K values 8 q ..) -> GEMM order
-__device__ __forceinline__ u32x4 gemm_order(u32x4 c) { return u32x4{c[0], c[2], c[1], c[3]}; }
-
-// The exact BF16 values of one block's codes (natural order) and scale byte: v[i] holds
-// elements 8 i .. 8 i + 7 (every E2M1 value times a power of two is a BF16 number).
-__device__ __forceinline__ void mxfp4_dequantize32(const u32x4& codes, uint32_t sbyte, u32x4 v[4]) {
-  const float sc = e8m0_scale(sbyte);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = fp4x8_to_bf16(codes[i], sc);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Token-row quantisation: z [T, d] BF16 -> codes [T, d/2] (GEMM order) and scales [T, d/32];
 // with rt, also the rows' exact round trip (the dequantised codes) as BF16 [T, d]. One thread
@@ -60,15 +50,7 @@ __global__ __launch_bounds__(256) void quantize_rows_a4_kernel(int64_t nblocks, 
     u32x4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld_u32x4(src + b * 32 + i * 8);
-    u32x4 out;
-    const uint32_t sbyte = mxfp4_quantize32(v, out);
-    st_u32x4(codes + b * 16, gemm_order(out));
-    scales[b] = (uint8_t)sbyte;
-    if (rt) {
-      mxfp4_dequantize32(out, sbyte, v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_u32x4(rt + b * 32 + i * 8, v[i]);
-    }
+    mxfp4_block_out(v, codes + b * 16, scales + b, rt ? rt + b * 32 : nullptr);
   }
 }
 
@@ -98,13 +80,7 @@ __global__ __launch_bounds__(256) void act_round_trip_a4_kernel(int64_t nblocks,
     u32x4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld_u32x4(act + b * 32 + i * 8);
-    u32x4 out;
-    const uint32_t sbyte = mxfp4_quantize32(v, out);
-    st_u32x4(codes + b * 16, gemm_order(out));
-    scales[b] = (uint8_t)sbyte;
-    mxfp4_dequantize32(out, sbyte, v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_u32x4(act + b * 32 + i * 8, v[i]);
+    mxfp4_block_out(v, codes + b * 16, scales + b, act + b * 32);
   }
 }
 

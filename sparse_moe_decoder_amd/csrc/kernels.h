@@ -46,6 +46,15 @@ struct RouterArgs {
   float* logits;      // [T, E]
 };
 
+// 4-bit activations: the token rows' MXFP4 codes [T, d/2] (GEMM order), scales [T, d/32]
+// and round trip [T, d] BF16, written by the routing launch that reads the rows anyway;
+// zq null: none
+struct RowQuantArgs {
+  uint8_t* zq;
+  uint8_t* zqs;
+  uint16_t* zr;
+};
+
 struct RouterX3Args {
   int T, d, E;            // E % 64 == 0, d % 128 == 0
   const uint16_t* z;      // [T, d] BF16
@@ -153,13 +162,15 @@ hipError_t launch_route_permute_small(const TopkArgs& t, const PermArgs& a, hipS
 // Router + grouped top-k + grouping in one launch for T <= 16 and T * k <= 64 (E
 // workgroups; `done` is caller-owned, zeroed device memory of kRouteDoneWords words, left
 // zeroed; `sc` is caller-owned scratch of T * E 64-bit words for the published scores).
+// q: the rows' 4-bit quantisation in the same launch (q.zq null: none).
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
-                                   uint32_t* done, uint64_t* sc, hipStream_t s);
+                                   uint32_t* done, uint64_t* sc, const RowQuantArgs& q,
+                                   hipStream_t s);
 // one token (d <= 8192): the boundary of that token inside the same launch; z goes to
 // b.z_out and the router reads it, h' to b.h_out (which may be b.h)
 hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
                                        const PermArgs& a, uint32_t* done, uint64_t* sc,
-                                       hipStream_t s);
+                                       const RowQuantArgs& q, hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);

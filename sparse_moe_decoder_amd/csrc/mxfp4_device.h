@@ -35,34 +35,92 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
 //   the decision points q passes, strictly past a point where the lower neighbour
 //   has the even code (0.25, 1.25, 2.5, 5) and from the point on where the upper one
 //   has it (0.75, 1.75, 3.5). The sign bit is the input's.
+// The largest magnitude (BF16 bits without the sign) of eight values
+__device__ __forceinline__ uint32_t bf16x8_amax(const u32x4& v) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) amax = max_u32(amax, max_u32(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+  return amax;
+}
+
+// The scale byte X + 127 of a block whose largest magnitude has BF16 bits amax
+__device__ __forceinline__ uint32_t mxfp4_scale_byte(uint32_t amax) {
+  const int ex = (int)(amax >> 7);  // BF16 exponent field (< 255: finite)
+  return (uint32_t)(ex > 2 ? ex - 2 : 0);
+}
+
+// Eight values (half-word e of v is element e) to their codes with scale byte sbyte:
+// element e in nibble e
+__device__ __forceinline__ uint32_t mxfp4_codes8(const u32x4& v, uint32_t sbyte) {
+  const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^-X
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t bits = hh ? (v[j] >> 16) : (v[j] & 0xFFFFu);
+      const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
+      const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
+                         (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
+      out |= (m | ((bits >> 12) & 8u)) << (4 * (j * 2 + hh));
+    }
+  return out;
+}
+
 __device__ __forceinline__ uint32_t mxfp4_quantize32(const u32x4 v[4], u32x4& out) {
   uint32_t amax = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) amax = max_u32(amax, bf16x8_amax(v[i]));
+  const uint32_t sbyte = mxfp4_scale_byte(amax);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = v[i][j];
-      amax = max_u32(amax, max_u32(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
-    }
-  const int ex = (int)(amax >> 7);                      // BF16 exponent field (< 255: finite)
-  const int sbyte = ex > 2 ? ex - 2 : 0;                // X + 127
-  const float inv = __uint_as_float((uint32_t)(254 - sbyte) << 23);  // 2^-X
-  out = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 4; ++i) out[i] = mxfp4_codes8(v[i], sbyte);
+  return sbyte;
+}
+
+// Block codes in natural order (dword q = K values 8 q ..) -> the order the scaled FP4
+// matrix-core kernels read them in ("GEMM order"): dword p holds K values 8 q .. 8 q + 7
+// with q = (0, 2, 1, 3)[p]
+__device__ __forceinline__ u32x4 gemm_order(u32x4 c) { return u32x4{c[0], c[2], c[1], c[3]}; }
+
+// The exact BF16 values of one block's codes (natural order) and scale byte: v[i] holds
+// elements 8 i .. 8 i + 7 (every E2M1 value times a power of two is a BF16 number).
+__device__ __forceinline__ void mxfp4_dequantize32(const u32x4& codes, uint32_t sbyte, u32x4 v[4]) {
+  const float sc = e8m0_scale(sbyte);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) v[i] = fp4x8_to_bf16(codes[i], sc);
+}
+
+// One block of 32 BF16 values (v, replaced by its round trip when rt is not null) to its
+// codes (16 bytes at codes, GEMM order), its scale byte (at scale) and, with rt, its round
+// trip (32 BF16 values at rt).
+__device__ __forceinline__ void mxfp4_block_out(u32x4 v[4], uint8_t* codes, uint8_t* scale,
+                                                uint16_t* rt) {
+  u32x4 out;
+  const uint32_t sbyte = mxfp4_quantize32(v, out);
+  st_u32x4(codes, gemm_order(out));
+  *scale = (uint8_t)sbyte;
+  if (rt) {
+    mxfp4_dequantize32(out, sbyte, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t bits = hh ? (v[i][j] >> 16) : (v[i][j] & 0xFFFFu);
-        const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
-        const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
-                           (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
-        const uint32_t code = m | ((bits >> 12) & 8u);
-        const int e = i * 8 + j * 2 + hh;  // element of the block
-        out[e >> 3] |= code << (4 * (e & 7));
-      }
-  return (uint32_t)sbyte;
+    for (int i = 0; i < 4; ++i) st_u32x4(rt + i * 8, v[i]);
+  }
+}
+
+// One block of 32 BF16 values held by four consecutive lanes (lane 4 j + q holds elements
+// 8 q .. 8 q + 7 in v): its codes (16 bytes at codes, GEMM order), its scale byte (at scale)
+// and its round trip (32 BF16 values at rt); every lane of the four passes the block's
+// pointers. The four lanes must be active together.
+__device__ __forceinline__ void mxfp4_block_out_4lanes(const u32x4& v, uint8_t* codes,
+                                                       uint8_t* scale, uint16_t* rt) {
+  const int q = threadIdx.x & 3;
+  uint32_t amax = bf16x8_amax(v);
+  amax = max_u32(amax, (uint32_t)__shfl_xor((int)amax, 1, 4));
+  amax = max_u32(amax, (uint32_t)__shfl_xor((int)amax, 2, 4));
+  const uint32_t sbyte = mxfp4_scale_byte(amax);
+  const uint32_t c = mxfp4_codes8(v, sbyte);
+  reinterpret_cast<uint32_t*>(codes)[q == 1 ? 2 : q == 2 ? 1 : q] = c;  // GEMM order
+  if (q == 0) *scale = (uint8_t)sbyte;
+  st_u32x4(rt + 8 * q, fp4x8_to_bf16(c, e8m0_scale(sbyte)));
 }
 
 }  // namespace beam

@@ -14,6 +14,7 @@
 #include "boundary_device.h"
 #include "router_device.h"
 #include "topk_device.h"
+#include "mxfp4_device.h"
 
 namespace beam {
 
@@ -503,10 +504,15 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
 // order (see boundary_row_4waves_finish), into LDS, with its router weights in
 // flight; workgroup 0 writes z out, and the last workgroup writes h' (by then every
 // workgroup has read h, so h_out may alias h).
-template <bool BOUNDARY>
+// QUANT (4-bit activations, rq): the workgroups also share out the rows' 32-value blocks,
+// four lanes to a block, and write each block's MXFP4 codes, scale and round trip next to
+// their logits (the rows are at hand; the stores complete before the workgroup counts
+// itself).
+template <bool BOUNDARY, bool QUANT>
 __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, TopkArgs ta,
                                                                PermArgs pa, uint32_t* done,
-                                                               uint64_t* sc, BoundaryArgs ba) {
+                                                               uint64_t* sc, BoundaryArgs ba,
+                                                               RowQuantArgs rq) {
   __shared__ float part[3][kRouterRT];
   __shared__ __attribute__((aligned(16))) float c_lds[4][256];
   __shared__ int32_t sel[4][32];
@@ -516,6 +522,16 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x;
   const float bias = ta.bias[e];
+  // QUANT: this workgroup's blocks [q0, q1) of the rows' T * d / 32; thread 4 i + p holds
+  // part p of block q0 + i (+ 64 per round), the first round's values prefetched
+  const int nbq = QUANT ? ra.T * (ra.d >> 5) : 0;
+  const int qper = (nbq + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int q0 = e * qper, q1 = q0 + qper < nbq ? q0 + qper : nbq;
+  const int qb = q0 + (tid >> 2), qp = tid & 3;
+  const bool doq = qb < q1;
+  auto quant_out = [&](int b, const u32x4& qv) {
+    mxfp4_block_out_4lanes(qv, rq.zq + (int64_t)b * 16, rq.zqs + b, rq.zr + (int64_t)b * 32);
+  };
   float v;
   BoundaryRow4 brow;  // BOUNDARY: the token row; its h' is stored by the last workgroup
   if constexpr (BOUNDARY) {
@@ -532,8 +548,17 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
     __builtin_amdgcn_sched_barrier(0);
     boundary_row_4waves_finish(ba, 0, brow, zl, e == 0 ? ba.z_out : nullptr, red);
     v = router_dot_1_lds(ra, w, zl, part);
+    if constexpr (QUANT) {
+      for (int b = qb; b < q1; b += 64) quant_out(b, *(const u32x4*)(zl + b * 32 + qp * 8));
+    }
   } else {
+    u32x4 qv;
+    if (QUANT && doq) qv = ld_u32x4(ra.z + (int64_t)qb * 32 + qp * 8);
     v = router_small_dot(ra, e, 0, ra.T, part);
+    if constexpr (QUANT) {
+      if (doq) quant_out(qb, qv);
+      for (int b = qb + 64; b < q1; b += 64) quant_out(b, ld_u32x4(ra.z + (int64_t)b * 32 + qp * 8));
+    }
   }
   if (tid < ra.T) {
     ra.logits[(int64_t)tid * ra.E + e] = v;
@@ -593,17 +618,26 @@ hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a
 }
 
 hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const PermArgs& a,
-                                   uint32_t* done, uint64_t* sc, hipStream_t s) {
-  hipLaunchKernelGGL(route_fused_tiny_kernel<false>, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a,
-                     done, sc, BoundaryArgs{});
+                                   uint32_t* done, uint64_t* sc, const RowQuantArgs& q,
+                                   hipStream_t s) {
+  if (q.zq)
+    hipLaunchKernelGGL((route_fused_tiny_kernel<false, true>), dim3((unsigned)r.E), dim3(256), 0, s,
+                       r, t, a, done, sc, BoundaryArgs{}, q);
+  else
+    hipLaunchKernelGGL((route_fused_tiny_kernel<false, false>), dim3((unsigned)r.E), dim3(256), 0,
+                       s, r, t, a, done, sc, BoundaryArgs{}, q);
   return hipGetLastError();
 }
 
 hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
                                        const PermArgs& a, uint32_t* done, uint64_t* sc,
-                                       hipStream_t s) {
-  hipLaunchKernelGGL(route_fused_tiny_kernel<true>, dim3((unsigned)r.E), dim3(256), 0, s, r, t, a,
-                     done, sc, b);
+                                       const RowQuantArgs& q, hipStream_t s) {
+  if (q.zq)
+    hipLaunchKernelGGL((route_fused_tiny_kernel<true, true>), dim3((unsigned)r.E), dim3(256), 0, s,
+                       r, t, a, done, sc, b, q);
+  else
+    hipLaunchKernelGGL((route_fused_tiny_kernel<true, false>), dim3((unsigned)r.E), dim3(256), 0, s,
+                       r, t, a, done, sc, b, q);
   return hipGetLastError();
 }
 

@@ -172,6 +172,35 @@ def test_w4a4_replay_and_format_switch(layer):
         moe.set_activation_format(beam.ACT_MXFP4)
 
 
+@pytest.mark.parametrize("T", [1, 8])
+def test_w4a4_fused_entry_points(layer, T):
+    """Up to 16 tokens the routing launch quantises the token rows itself (for one token
+    inside the boundary + routing launch of beam_sublayer_forward, from its LDS copy of z):
+    the z codes equal the oracle's MXFP4 of the GPU's z bit for bit, and the output equals,
+    bit for bit, that of beam_moe_forward on the same z with computed routing and with that
+    routing replayed (rows then quantised by the stand-alone quantiser)."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    moe, host = layer
+    print(f"[w4a4] fused entry points T={T}", flush=True)
+    wpost, wpre = sd.norm_weights(WL)
+    h, x = sd.tokens(WL, "h", T=T), sd.tokens(WL, "x", T=T)
+    y1 = torch.empty_like(h)
+    h1, z1 = beam.beam_sublayer_forward(moe.handle, h, x, wpost, wpre, WL.n, WL.eps, y1)
+    torch.cuda.synchronize()
+    zq = moe.inspect("z_codes", T * WL.d // 2).cpu().numpy().reshape(T, WL.d // 2)
+    zs = moe.inspect("z_scales", T * WL.d // 32).cpu().numpy().reshape(T, WL.d // 32)
+    o_zq, o_zs = oracle.mxfp4_quantize(P.bits(z1))
+    assert np.array_equal(natural_order(zq, WL.d), o_zq)
+    assert np.array_equal(zs, o_zs)
+    y2, r = moe.forward(z1, want_routing=True)
+    y3 = moe.forward(z1, ids_in=r["ids_out"], w_in=r["w_out"])
+    torch.cuda.synchronize()
+    assert np.array_equal(P.bits(y2), P.bits(y1))
+    assert np.array_equal(P.bits(y3), P.bits(y1))
+
+
 def test_w4a4_format_rejected_for_bf16_weights():
     import sparse_moe_decoder_amd as beam
     from synth import device as sd
