@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 matrix cores
 FP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4 matrix cores
+STREAM_MAX_T = 128           # largest batch the library serves with its weight-streaming passes
 METRIC = "MoE-layer tokens/s (decode T=1/32/128, prefill 16K) + % HBM/MFMA peak"
 SUITE = ("decode1", "decode32", "decode128", "prefill16k", "skew32k")
 
@@ -148,7 +149,7 @@ def measure(wl, moe, dense_h, args, mx):
     from synth import device as sd
 
     T = wl.T
-    decode = T <= 128
+    decode = T <= STREAM_MAX_T
     dense = dense_h is not None
     steps = args.steps or (200 if decode else 10)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 3)
@@ -270,10 +271,11 @@ def measure(wl, moe, dense_h, args, mx):
     # roofline of the dominant kernel (expert gate/up)
     gu_us = kernel_us.get("gate_up")
     a4 = args.act == "mxfp4"
-    src = source_hash(*(("experts_w4a4.hip", "gemm_device.h", "mxfp4_device.h", "common.h") if a4
+    a4_gemm = a4 and T > STREAM_MAX_T  # up to 128 tokens W4A4 runs on the 4-bit weight streams
+    src = source_hash(*(("experts_w4a4.hip", "gemm_device.h", "mxfp4_device.h", "common.h") if a4_gemm
                         else ("experts.hip", "experts_mxfp4.hip", "common.h") if mx
                         else ("experts.hip", "common.h")))
-    ctr_name = "gate_up_w4a4" if a4 else "gate_up_mxfp4" if mx else "gate_up"
+    ctr_name = "gate_up_w4a4" if a4_gemm else "gate_up_mxfp4" if mx else "gate_up"
     wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
     if decode:
         # algorithmic bytes per launch: each touched expert's gate+up weights once, the
@@ -292,7 +294,7 @@ def measure(wl, moe, dense_h, args, mx):
         kk = 1 if dense else wl.k
         flops_gu = 2.0 * T * kk * (2 * wl.f) * wl.d
         achieved = flops_gu / (gu_us * 1e-6) / 1e12
-        peak = FP4_PEAK_TFLOPS if a4 else BF16_PEAK_TFLOPS  # the contraction's own dtype
+        peak = FP4_PEAK_TFLOPS if a4_gemm else BF16_PEAK_TFLOPS  # the contraction's own dtype
         roof = dict(kernel="gate_up", bound="mfma", achieved=round(achieved, 1),
                     peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), algorithmic_flops=flops_gu)
