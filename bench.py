@@ -434,7 +434,7 @@ def main():
 def cpu_baseline(wl, sample=None, mxfp4=False, act4=False):
     """The CPU oracle, as it is, on a bounded sample of the same workload: each
     sampled token goes through boundary, router, routing, its experts and the
-    combine, single-threaded per token; tokens run in a thread pool of the machine's CPU
+    combine, single-threaded per token; tokens run in a thread pool of the host's CPU
     share, and a few tokens also run alone on one thread (the single-core figure).
     With mxfp4 the experts' weights are the oracle's MXFP4 quantisation, dequantised
     (not timed)."""
