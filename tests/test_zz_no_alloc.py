@@ -2,8 +2,10 @@
 workspace lives in the library's static scratch area) against beam_moe_forward on the same
 handle: the same outputs bit for bit over consecutive calls of decreasing size that take
 every routing and expert path (grouped GEMMs, weight streams, the one-launch routing whose
-counter lives in the scratch area), computed and replayed routing, and the size limit.
-Both entry points are called through the C ABI."""
+counters live in the scratch area), computed and replayed routing, the size limit, and a
+4-bit handle with 4-bit activations (its extra buffers: token-row and activation codes and
+scales, and the rows' round trip that the weight streams read). Both entry points are called
+through the C ABI."""
 import numpy as np
 import pytest
 
@@ -91,3 +93,35 @@ def test_noalloc_limits(moe):
     b = _outputs(beam.beam_moe_forward_noalloc, moe, zf)
     for key, v in a.items():
         assert np.array_equal(b[key].view(np.uint8), v.view(np.uint8)), key
+
+
+W4 = synth.Workload("noalloc_w4a4", T=1500, d=512, E=32, G=8, kg=4, k=8, f=512)
+
+
+def test_noalloc_w4a4_equals_forward():
+    """A 4-bit-weight handle set to 4-bit activations: 1500 tokens (W4A4 grouped GEMMs), 40
+    (weight streams, rows quantised by the stand-alone quantiser) and 1 (weight streams, rows
+    quantised inside the one-launch routing) in a row, each equal to beam_moe_forward bit for
+    bit, twice."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    print(f"[noalloc] building the 4-bit layer {W4}", flush=True)
+    W, b = sd.router(W4)
+    fp4 = []
+    for t in sd.experts(W4):
+        fp4 += list(beam.beam_mxfp4_quantize(t))
+    m = beam.BeamMoE(sd.moe_config(W4, max_tokens=W4.T), W, b, None, None, None, mxfp4=tuple(fp4))
+    try:
+        m.set_activation_format(beam.ACT_MXFP4)
+        g = torch.Generator(device="cpu").manual_seed(23)
+        for T in (1500, 40, 1):
+            print(f"[noalloc] w4a4 T={T}", flush=True)
+            z = torch.randn((T, W4.d), generator=g).to(torch.bfloat16).cuda()
+            ref = _outputs(beam.beam_moe_forward, m, z)
+            for rep in range(2):
+                got = _outputs(beam.beam_moe_forward_noalloc, m, z)
+                for key, v in ref.items():
+                    assert np.array_equal(got[key].view(np.uint8), v.view(np.uint8)), (T, rep, key)
+    finally:
+        m.close()
