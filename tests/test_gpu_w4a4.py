@@ -201,6 +201,42 @@ def test_w4a4_fused_entry_points(layer, T):
     assert np.array_equal(P.bits(y3), P.bits(y1))
 
 
+WL_FEW = Workload("w4a4_few", T=8, d=4096, E=8, G=2, kg=1, k=2, f=512)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_w4a4_routing_quantiser_rounds(T):
+    """Eight experts and rows of 4096: the routing launch's eight workgroups each quantise up
+    to 128 of the rows' blocks (two rounds of 64 per workgroup). z codes equal the oracle's
+    MXFP4 bit for bit; the output equals the replayed-routing output (stand-alone quantiser)
+    bit for bit."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    print(f"[w4a4] few experts T={T}", flush=True)
+    W, b = sd.router(WL_FEW)
+    fp4 = []
+    for t in sd.experts(WL_FEW):
+        fp4 += list(beam.beam_mxfp4_quantize(t))
+    moe = beam.BeamMoE(sd.moe_config(WL_FEW, max_tokens=WL_FEW.T), W, b, None, None, None,
+                       mxfp4=tuple(fp4))
+    try:
+        moe.set_activation_format(beam.ACT_MXFP4)
+        z = P.to_dev(synth.token_rows(WL_FEW, range(T), "x"))
+        y1, r = moe.forward(z, want_routing=True)
+        torch.cuda.synchronize()
+        zq = moe.inspect("z_codes", T * WL_FEW.d // 2).cpu().numpy().reshape(T, WL_FEW.d // 2)
+        zs = moe.inspect("z_scales", T * WL_FEW.d // 32).cpu().numpy().reshape(T, WL_FEW.d // 32)
+        o_zq, o_zs = oracle.mxfp4_quantize(P.bits(z))
+        assert np.array_equal(natural_order(zq, WL_FEW.d), o_zq)
+        assert np.array_equal(zs, o_zs)
+        y2 = moe.forward(z, ids_in=r["ids_out"], w_in=r["w_out"])
+        torch.cuda.synchronize()
+        assert np.array_equal(P.bits(y2), P.bits(y1))
+    finally:
+        moe.close()
+
+
 def test_w4a4_format_rejected_for_bf16_weights():
     import sparse_moe_decoder_amd as beam
     from synth import device as sd
