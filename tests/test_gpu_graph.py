@@ -2,7 +2,8 @@
 nothing and never synchronises). Each case is captured once and replayed several times with
 the program's own eager work and synchronisations in between; every replay must equal the
 eager result bit for bit. Covers the single-token fused routing, the small-batch and the
-grouped-GEMM expert paths, the fused boundary entry points, 4-bit experts and the dense layer;
+grouped-GEMM expert paths, the fused boundary entry points, 4-bit experts (with BF16 and with
+4-bit activations) and the dense layer;
 all calls go through the C ABI."""
 import dataclasses
 
@@ -109,6 +110,13 @@ def test_graph_mxfp4():
         z = sd.tokens(SMALL4, "h", T=T)
         y = torch.empty_like(z)
         check_graph(lambda: beam.beam_moe_forward(moe.handle, z, y), [y], f"mxfp4 T={T}")
+    # 4-bit activations: the rows quantised inside the routing launch (T = 1), by the
+    # stand-alone quantiser with the activations' round-trip pass (T = 40), the W4A4 GEMMs (300)
+    moe.set_activation_format(beam.ACT_MXFP4)
+    for T in (1, 40, 300):
+        z = sd.tokens(SMALL4, "h", T=T)
+        y = torch.empty_like(z)
+        check_graph(lambda: beam.beam_moe_forward(moe.handle, z, y), [y], f"w4a4 T={T}")
     moe.close()
 
 
