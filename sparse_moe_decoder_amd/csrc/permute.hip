@@ -16,6 +16,8 @@
 #include "topk_device.h"
 #include "mxfp4_device.h"
 
+#include <type_traits>
+
 namespace beam {
 
 __device__ __forceinline__ bool valid_id(int e, int E) { return e >= 0 && e < E; }
@@ -398,6 +400,7 @@ struct OneTokenLds {
   int32_t id[64];      //   and its index
 };
 
+// (The counting loops are unrolled so that their LDS reads are in flight together.)
 // One token's grouped top-k and grouping by the 256 threads of a workgroup, thread e
 // holding expert e. The selection and the weights are topk_token's, found by counting
 // instead of in rounds: an entry's rank is the number of entries ahead of it in (value
@@ -423,12 +426,21 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   const uint64_t key = valid ? ((uint64_t)f32_order_key(c) << 32) | (uint32_t)~tid : 0;
   L.key[tid] = key;
   // group score: the sum of the group's two largest biased scores (a group's threads are
-  // adjacent lanes of one wave)
+  // adjacent lanes of one wave). Each step merges the top two of two disjoint lane sets of
+  // the group, so every lane ends with the group's pair: the quad permutations, the half-row
+  // and row mirrors (within 8 and 16 lanes) by DPP, then shuffles across rows.
   float m1 = c, m2 = -INFINITY;
-  for (int off = 1; off < gs; off <<= 1) {
-    const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
-    top2_merge(m1, m2, o1, o2);
-  }
+  auto merge_dpp = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    top2_merge(m1, m2, __uint_as_float(dpp_u32<C>(__float_as_uint(m1))),
+               __uint_as_float(dpp_u32<C>(__float_as_uint(m2))));
+  };
+  if (gs >= 2) merge_dpp(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  if (gs >= 4) merge_dpp(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  if (gs >= 8) merge_dpp(std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if (gs >= 16) merge_dpp(std::integral_constant<int, 0x140>{}); // row_mirror
+  for (int off = 16; off < gs; off <<= 1)
+    top2_merge(m1, m2, __shfl_xor(m1, off, 64), __shfl_xor(m2, off, 64));
   const int g = tid / gs;
   if (valid && tid % gs == 0)
     L.gkey[g] = ((uint64_t)f32_order_key(m1 + m2) << 32) | (uint32_t)~g;
@@ -437,12 +449,14 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   if (valid) {
     const uint64_t mine = L.gkey[g];
     rg = 0;
+#pragma unroll 8
     for (int q = 0; q < G; ++q) rg += L.gkey[q] > mine ? 1 : 0;
   }
   bool surv = false;
   int ri = 0;
   if (rg < kg) {
     const uint64_t* gk = L.key + g * gs;
+#pragma unroll 8
     for (int q = 0; q < gs; ++q) ri += gk[q] > key ? 1 : 0;
     surv = ri < k;
     if (surv) L.skey[rg * k + ri] = key;
@@ -451,6 +465,7 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   int slot = -1;
   if (surv) {
     int r = 0;
+#pragma unroll 8
     for (int q = 0; q < nsk; ++q) r += L.skey[q] > key ? 1 : 0;
     if (r < k) {
       slot = r;
@@ -461,6 +476,7 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   __syncthreads();
   if (tid < k) {
     float den = L.s[0];
+#pragma unroll 8
     for (int j = 1; j < k; ++j) den = den + L.s[j];  // slot order
     const float wj = (L.s[tid] / den) * ta.scale;
     const int e = L.id[tid];
@@ -471,6 +487,7 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   }
   if (valid) {
     int off = 0;
+#pragma unroll 8
     for (int j = 0; j < k; ++j) off += L.id[j] < tid ? 1 : 0;
     pa.counts[tid] = slot >= 0 ? 1 : 0;
     pa.offsets[tid] = off;
