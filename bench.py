@@ -59,10 +59,13 @@ def parse():
     p.add_argument("--rotations", type=int, default=None, help="distinct token sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
-    p.add_argument("--step", choices=("boundary-first", "boundary-last"), default="boundary-last",
+    p.add_argument("--step", choices=("boundary-first", "boundary-last", "chain"),
+                   default="boundary-last",
                    help="boundary-first: beam_sublayer_forward (the boundary, then the MoE on its z); "
                         "boundary-last: beam_moe_forward_boundary (the MoE on a z computed before the "
-                        "timed region, then the next sublayer's boundary fused into the combine)")
+                        "timed region, then the next sublayer's boundary fused into the combine); "
+                        "chain: beam_moe_forward_boundary_route in a decode loop (each step's h', z' "
+                        "feed the next step, whose routing the step computes after its boundary)")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU sample")
     p.add_argument("--experts", choices=("bf16", "mxfp4"), default="bf16",
                    help="expert weight format: BF16, or MXFP4 (4-bit E2M1 codes with one E8M0 "
@@ -172,6 +175,17 @@ def measure(wl, moe, dense_h, args, mx):
             beam.beam_dense_forward(dense_h, z_in[s], y)
             beam.beam_sublayer_norm_residual(hs[s], y, wpost, wpre, wl.n, wl.eps, h_out=h_out,
                                              z_out=z)
+    elif args.step == "chain":
+        # a decode loop: h and z are updated in place; each step runs the MoE on z with the
+        # routing the previous step left, then the combine, the boundary and the next routing
+        hc, zc = hs[0].clone(), z_in[0].clone()
+
+        def chain_call(routed):
+            beam.beam_moe_forward_boundary_route(moe.handle, moe.handle, zc, hc, wpost, wpre,
+                                                 wl.n, wl.eps, h_out=hc, z_out=zc, routed=routed)
+
+        def step(i):
+            chain_call(True)
     elif args.step == "boundary-first":
         def step(i):
             s = i % R
@@ -182,7 +196,8 @@ def measure(wl, moe, dense_h, args, mx):
             s = i % R
             beam.beam_moe_forward_boundary(moe.handle, z_in[s], hs[s], wpost, wpre, wl.n, wl.eps,
                                            h_out=h_out, z_out=z)
-    last_out = y if (args.step == "boundary-first" and not dense) else z
+    last_out = (y if (args.step == "boundary-first" and not dense)
+                else zc if (args.step == "chain" and not dense) else z)
 
     # distinct experts per token set (for the algorithmic byte count) and rows per expert
     distinct, max_rows, hot_share = [1], None, None
@@ -201,6 +216,8 @@ def measure(wl, moe, dense_h, args, mx):
     mean_distinct = float(np.mean(distinct))
 
     # 1) eager
+    if args.step == "chain" and not dense:
+        chain_call(False)  # the first step routes its own z (and leaves the next routing)
     for i in range(warmup):
         step(i)
     ms_eager = timed(step, steps)
@@ -232,11 +249,23 @@ def measure(wl, moe, dense_h, args, mx):
                 graphs[i % R].replay()
             ms_graph = timed(lambda i: graphs[i % R].replay(), steps)
             log(f"{wl.name} graph: {ms_graph * 1e3:.1f} us/step")
-            step(0)
-            torch.cuda.synchronize()
-            out_eager = last_out.clone()
-            last_out.zero_()
-            graphs[0].replay()
+            if args.step == "chain" and not dense:
+                # from one saved state: the eager steps and (after the same priming step) a replay
+                h_save, z_save = hc.clone(), zc.clone()
+                chain_call(False)
+                step(0)
+                torch.cuda.synchronize()
+                out_eager = last_out.clone()
+                hc.copy_(h_save)
+                zc.copy_(z_save)
+                chain_call(False)
+                graphs[0].replay()
+            else:
+                step(0)
+                torch.cuda.synchronize()
+                out_eager = last_out.clone()
+                last_out.zero_()
+                graphs[0].replay()
             torch.cuda.synchronize()
             graph_ok = bool(torch.equal(last_out.view(torch.int16), out_eager.view(torch.int16)))
             if not graph_ok:

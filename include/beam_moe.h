@@ -318,6 +318,32 @@ int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
                               float* logits_out, int32_t* ids_out, float* w_out, void* stream);
 
 /*
+ * beam_moe_forward_boundary_route — beam_moe_forward_boundary for a loop over MoE layers
+ * (decode): the MoE of handle h on z, then the weighted combine, the NEXT sublayer's
+ * boundary (h_out, z_out) and the NEXT layer's routing of z_out with handle `next` (router,
+ * grouped top-k and grouping into next's workspace; with 4-bit activations also the rows'
+ * quantisation), for one token (T = 1, hidden <= 8192, topk <= 8) all in ONE launch —
+ * the pages' fused graph ([vLLM §Der fusionierte Graph; §Agentengetriebene Optimierung,
+ * changes 1 and 3]: the post-MoE norm combines the top-8 outputs, and the boundary feeds the
+ * router) carried one step further. Other T run the same steps as separate launches.
+ * The call on the next layer passes routed = 1 to use that routing: it must name the same T
+ * and, as z, the z_out of this call (the handle records both; a mismatch returns
+ * BEAM_ERR_INVALID_ARG, as does routed = 1 on a handle with no such routing). Any other
+ * compute call on `next`, or beam_moe_set_activation_format, drops the recorded routing.
+ * With routed = 0 the call routes z itself. next may be h.
+ * Arguments and aliasing as beam_moe_forward_boundary (no routing replay or routing
+ * outputs); next must have the same hidden size; T <= both handles' max_tokens, else
+ * BEAM_ERR_CAPACITY. Results equal, bit for bit,
+ *   beam_moe_forward_boundary(h, T, z, h_in, w_post, w_pre, n, eps, h_out, z_out, y_out, ...)
+ *   followed by the routing of z_out that beam_moe_forward(next, T, z_out, ...) computes.
+ */
+int beam_moe_forward_boundary_route(beam_moe_handle h, beam_moe_handle next, int32_t T,
+                                    const uint16_t* z, const uint16_t* h_in,
+                                    const uint16_t* w_post, const uint16_t* w_pre, int32_t n,
+                                    float eps, uint16_t* h_out, uint16_t* z_out, uint16_t* y_out,
+                                    int32_t routed, void* stream);
+
+/*
  * beam_sublayer_forward — one sublayer step: the boundary of beam_sublayer_norm_residual
  * on (h_in, x) writing h_out and z_out, then beam_moe_forward on z_out with computed
  * routing writing y_out. The results are bit-identical to those two calls in sequence.

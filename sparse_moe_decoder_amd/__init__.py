@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     ACT_BF16,
     ACT_MXFP4,
     beam_moe_forward_boundary,
+    beam_moe_forward_boundary_route,
     beam_moe_init,
     beam_moe_init_mxfp4,
     beam_mxfp4_quantize,

@@ -55,6 +55,8 @@ def lib():
                                             vp, vp]
         L.beam_moe_forward_boundary.argtypes = [vp, i32, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp]
+        L.beam_moe_forward_boundary_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, f32, vp,
+                                                      vp, vp, i32, vp]
         L.beam_status_string.argtypes = [ctypes.c_int]
         L.beam_status_string.restype = ctypes.c_char_p
         L.beam_profile_enable.argtypes = [ctypes.c_int]
@@ -70,6 +72,7 @@ def lib():
                      "beam_moe_forward_noalloc", "beam_moe_set_activation_format",
                      "beam_moe_inspect",
                      "beam_sublayer_forward", "beam_moe_forward_boundary",
+                     "beam_moe_forward_boundary_route",
                      "beam_profile_enable", "beam_profile_reset", "beam_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -293,6 +296,28 @@ def beam_moe_forward_boundary(handle, z, h, w_post, w_pre, n, eps, h_out=None, z
         _ptr(y_out, bf, (T, d), "y_out"), _ptr(ids_in, name="ids_in"), _ptr(w_in, name="w_in"),
         _ptr(logits_out, name="logits_out"), _ptr(ids_out, name="ids_out"),
         _ptr(w_out, name="w_out"), _stream(stream)))
+    return h_out, z_out
+
+
+def beam_moe_forward_boundary_route(handle, next_handle, z, h, w_post, w_pre, n, eps,
+                                    h_out=None, z_out=None, y_out=None, routed=False,
+                                    stream=None):
+    """MoE forward of `handle` on z (routed: its routing of z was left by the previous layer's
+    call), then the combine, the next boundary and `next_handle`'s routing of z_out; returns
+    (h_out, z_out). h_out may be h and z_out may be z; y_out (optional) receives the MoE
+    output."""
+    import torch
+    T, d = h.shape
+    if h_out is None:
+        h_out = torch.empty_like(h)
+    if z_out is None:
+        z_out = torch.empty_like(h)
+    bf = torch.bfloat16
+    _check("beam_moe_forward_boundary_route", lib().beam_moe_forward_boundary_route(
+        handle, next_handle, T, _ptr(z, bf, (T, d), "z"), _ptr(h, bf, (T, d), "h"),
+        _ptr(w_post, bf, (d,), "w_post"), _ptr(w_pre, bf, (d,), "w_pre"), int(n), float(eps),
+        _ptr(h_out, bf, (T, d), "h_out"), _ptr(z_out, bf, (T, d), "z_out"),
+        _ptr(y_out, bf, (T, d), "y_out"), 1 if routed else 0, _stream(stream)))
     return h_out, z_out
 
 

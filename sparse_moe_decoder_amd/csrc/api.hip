@@ -29,11 +29,13 @@ enum KernelId {
   K_GATEUP,
   K_DOWN,
   K_COMBINE,
-  K_QUANT,  // 4-bit activations: the token rows' and activations' quantisation
+  K_QUANT,          // 4-bit activations: the token rows' and activations' quantisation
+  K_COMBINE_ROUTE,  // one token: combine, next boundary and the next layer's routing
   K_COUNT
 };
-const char* const kKernelNames[K_COUNT] = {"boundary", "router",  "topk",    "permute",
-                                           "gate_up",  "down",    "combine", "quantize"};
+const char* const kKernelNames[K_COUNT] = {"boundary", "router",  "topk",     "permute",
+                                           "gate_up",  "down",    "combine",  "quantize",
+                                           "combine_route"};
 
 struct ProfRecord {
   int id;
@@ -132,6 +134,11 @@ struct beam_moe_ctx {
   uint16_t* wdp = nullptr;    // packed down (BF16 experts)
   bool mxfp4 = false;         // 4-bit experts: the four arrays below instead of wgu, wdp
   bool act_mx = false;        // 4-bit experts with 4-bit activations (the W4A4 GEMMs)
+  // routing left in the workspace by beam_moe_forward_boundary_route (the previous layer's
+  // call) for the call on routed_z with routed_T tokens; 0: none
+  int routed_T = 0;
+  const void* routed_z = nullptr;
+  bool routed_quant = false;  // ... with the rows' 4-bit quantisation done in that launch
   bool dense = false;         // a dense SwiGLU layer (beam_dense_init): one expert, no routing
   uint8_t* qgu = nullptr;     // gate/up codes, decode layout
   uint8_t* sgu = nullptr;     // gate/up scales
@@ -301,74 +308,97 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
   return (const char*)a < (const char*)b + bytes && (const char*)b < (const char*)a + bytes;
 }
 
-// The MoE forward after validation. bnd (computed routing, T = 1, d <=
-// kBoundaryWgMaxD, k <= kFusedRouteMaxSlots only): the boundary of the token runs
-// inside the routing launch and writes z (= bnd->z_out, the z read here) and h'.
-// post: the next sublayer's boundary with x = the MoE output runs in the combine
-// launch (d <= kBoundaryWgMaxD; y_out may then be null) or after it (wider rows,
-// through y_out).
+// Any call that rewrites a handle's workspace (or changes what its routing launch does)
+// drops the routing a previous layer's beam_moe_forward_boundary_route left in it.
+void clear_routed(beam_moe_ctx* h) {
+  h->routed_T = 0;
+  h->routed_z = nullptr;
+  h->routed_quant = false;
+}
+
+// Computed routing of T rows z (router, grouped top-k, grouping) into ws. bnd (T = 1, d <=
+// kBoundaryWgMaxD, k <= kFusedRouteMaxSlots only): the boundary of the token runs inside the
+// routing launch and writes z (= bnd->z_out, the z routed) and h'; cb (with bnd): that
+// boundary's x is the combine of a previous MoE's rows. With 4-bit activations, the one-launch
+// routings also quantise the rows (*quantised is set then).
+int route_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z, float* logits_out,
+               int32_t* ids_out, float* w_out, int32_t* perm_out, int32_t* offsets_out,
+               hipStream_t s, const BoundaryArgs* bnd, const CombineArgs* cb, bool* quantised) {
+  const beam_moe_config& c = h->cfg;
+  const int k = c.topk, E = c.n_experts;
+  const int slots = T * k;
+  const bool fused_route = bnd || (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots);
+  const RowQuantArgs rq = h->act_mx && T <= kStreamMaxT && fused_route
+                              ? RowQuantArgs{ws.zq, ws.zqs, ws.zr}
+                              : RowQuantArgs{nullptr, nullptr, nullptr};
+  *quantised = rq.zq != nullptr;
+  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, ws.ids, ws.counts,
+              ws.offsets, ws.perm, ws.block_cnt, ws.block_base, ws.active, ws.n_active,
+              ws.tile_start, perm_out, offsets_out};
+  float* lg = logits_out ? logits_out : ws.logits;
+  TopkArgs ta = topk_args(h, ws, T, lg, ids_out, w_out);
+  if (bnd) {
+    ProfScope ps(cb ? K_COMBINE_ROUTE : K_ROUTER, s);  // [combine,] boundary, routing: one launch
+    RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
+    return hip_status(
+        launch_boundary_route_fused(*bnd, ra, ta, pa, ws.route_done, ws.route_sc, rq, cb, s));
+  }
+  if (fused_route) {
+    ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
+    RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
+    return hip_status(launch_route_fused_tiny(ra, ta, pa, ws.route_done, ws.route_sc, rq, s));
+  }
+  int st = run_router(h, T, z, lg, s);
+  if (st != BEAM_OK) return st;
+  if (slots <= kPermChunk) {
+    ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
+    return hip_status(launch_route_permute_small(ta, pa, s));
+  }
+  {
+    ProfScope ps(K_TOPK, s);
+    if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  ProfScope ps(K_PERMUTE, s);
+  return hip_status(launch_permute(pa, s));
+}
+
+// The MoE forward after validation. Routing: replayed (ids_in), left by the previous layer's
+// call (pre_routed; pre_quantised: with the rows' 4-bit quantisation) or computed here (bnd:
+// see route_impl). Tail: the combine into y_out; post: the next sublayer's boundary with x =
+// the MoE output, in the combine launch (d <= kBoundaryWgMaxD; y_out may then be null) or
+// after it (wider rows, through y_out); next (with post): then the next layer's routing of
+// post->z_out into next's workspace — for one token in the same launch as the combine and
+// the boundary.
 int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z, uint16_t* y_out,
                  const int32_t* ids_in, const float* w_in, float* logits_out, int32_t* ids_out,
                  float* w_out, int32_t* perm_out, int32_t* offsets_out, hipStream_t s,
-                 const BoundaryArgs* bnd, const BoundaryArgs* post) {
+                 const BoundaryArgs* bnd, const BoundaryArgs* post, bool pre_routed = false,
+                 bool pre_quantised = false, beam_moe_ctx* next = nullptr) {
   const beam_moe_config& c = h->cfg;
   const int k = c.topk, E = c.n_experts;
   const int slots = T * k;
 
-  const int32_t* ids = ids_in;
-  const float* w = w_in;
-  // 4-bit activations on the weight streams: the fused routing launches quantise the rows
-  const bool a4_stream = h->act_mx && T <= kStreamMaxT;
-  const bool fused_route =
-      !ids_in && (bnd || (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots));
-  const RowQuantArgs rq = a4_stream && fused_route ? RowQuantArgs{ws.zq, ws.zqs, ws.zr}
-                                                   : RowQuantArgs{nullptr, nullptr, nullptr};
-  PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, nullptr, ws.counts,
-              ws.offsets, ws.perm, ws.block_cnt, ws.block_base, ws.active, ws.n_active,
-              ws.tile_start, perm_out, offsets_out};
-  if (!ids_in) {
-    float* lg = logits_out ? logits_out : ws.logits;
-    ids = ws.ids;
-    w = ws.w;
-    pa.ids = ids;
-    TopkArgs ta = topk_args(h, ws, T, lg, ids_out, w_out);
-    if (bnd) {
-      ProfScope ps(K_ROUTER, s);  // boundary, router, top-k and grouping in one launch
-      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_boundary_route_fused(*bnd, ra, ta, pa, ws.route_done, ws.route_sc, rq, s) !=
-          hipSuccess)
-        return BEAM_ERR_HIP;
-    } else if (T <= kFusedRouteMaxT && slots <= kFusedRouteMaxSlots) {
-      ProfScope ps(K_ROUTER, s);  // router, top-k and grouping in one launch
-      RouterArgs ra{T, c.hidden, E, z, h->router_w, lg};
-      if (launch_route_fused_tiny(ra, ta, pa, ws.route_done, ws.route_sc, rq, s) != hipSuccess)
-        return BEAM_ERR_HIP;
-    } else if (slots <= kPermChunk) {
-      int st = run_router(h, T, z, lg, s);
-      if (st != BEAM_OK) return st;
-      ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
-      if (launch_route_permute_small(ta, pa, s) != hipSuccess) return BEAM_ERR_HIP;
-    } else {
-      int st = run_router(h, T, z, lg, s);
-      if (st != BEAM_OK) return st;
-      {
-        ProfScope ps(K_TOPK, s);
-        if (launch_topk(ta, s) != hipSuccess) return BEAM_ERR_HIP;
-      }
-      ProfScope ps(K_PERMUTE, s);
-      if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
-    }
-  } else {
+  const int32_t* ids = ids_in ? ids_in : ws.ids;
+  const float* w = w_in ? w_in : ws.w;
+  bool rows_quantised = pre_quantised;
+  if (ids_in) {
     if (ids_out &&
         hipMemcpyAsync(ids_out, ids_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
       return BEAM_ERR_HIP;
     if (w_out &&
         hipMemcpyAsync(w_out, w_in, (size_t)slots * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
       return BEAM_ERR_HIP;
-    pa.ids = ids;
+    PermArgs pa{slots, E, (slots + kPermChunk - 1) / kPermChunk, kGemmBM, ids, ws.counts,
+                ws.offsets, ws.perm, ws.block_cnt, ws.block_base, ws.active, ws.n_active,
+                ws.tile_start, perm_out, offsets_out};
     ProfScope ps(K_PERMUTE, s);
     if (launch_permute(pa, s) != hipSuccess) return BEAM_ERR_HIP;
+  } else if (!pre_routed) {
+    const int st = route_impl(h, ws, T, z, logits_out, ids_out, w_out, perm_out, offsets_out, s,
+                              bnd, nullptr, &rows_quantised);
+    if (st != BEAM_OK) return st;
   }
+  const bool a4_stream = h->act_mx && T <= kStreamMaxT;
   ExpertArgs ea{T, k, c.hidden, c.d_ff, E, z, h->wgu, h->wdp, ws.perm, ws.offsets, ws.active,
                 ws.n_active, ws.tile_start, w, ws.act, ws.yk, h->qgu, h->sgu, h->qd, h->sd,
                 h->pqgu, h->psgu, h->pqd, h->psd};
@@ -378,7 +408,7 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
     ea.aq = ws.aq;
     ea.aqs = ws.aqs;
     const bool stream = a4_stream;
-    if (!rq.zq) {
+    if (!rows_quantised) {
       ProfScope ps(K_QUANT, s);
       if (launch_quantize_rows_a4((int64_t)T * (c.hidden / 32), z, ws.zq, ws.zqs,
                                   stream ? ws.zr : nullptr, s) != hipSuccess)
@@ -450,14 +480,44 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
       if (launch_down_gemm(ea, max_tiles, s) != hipSuccess) return BEAM_ERR_HIP;
     }
   }
-  ProfScope ps(K_COMBINE, s);
-  if (!post) return hip_status(launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s));
-  if (c.hidden <= kBoundaryWgMaxD)
-    return hip_status(launch_combine_boundary(*post, CombineArgs{k, E, ids, ws.yk, y_out}, s));
-  if (launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s) != hipSuccess) return BEAM_ERR_HIP;
-  BoundaryArgs pb = *post;
-  pb.x = y_out;
-  return hip_status(launch_boundary(pb, s));
+  if (next && T == 1 && c.hidden <= kBoundaryWgMaxD && k <= kChainMaxK &&
+      next->cfg.topk <= kFusedRouteMaxSlots) {
+    // combine, next boundary and the next layer's routing in one launch
+    const CombineArgs cb{k, E, ids, ws.yk, y_out};
+    bool q = false;
+    const int st = route_impl(next, next->ws, T, post->z_out, nullptr, nullptr, nullptr, nullptr,
+                              nullptr, s, post, &cb, &q);
+    if (st == BEAM_OK) {
+      next->routed_T = T;
+      next->routed_z = post->z_out;
+      next->routed_quant = q;
+    }
+    return st;
+  }
+  {
+    ProfScope ps(K_COMBINE, s);
+    if (!post) return hip_status(launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s));
+    if (c.hidden <= kBoundaryWgMaxD) {
+      if (launch_combine_boundary(*post, CombineArgs{k, E, ids, ws.yk, y_out}, s) != hipSuccess)
+        return BEAM_ERR_HIP;
+    } else {
+      if (launch_combine(T, k, c.hidden, E, ids, ws.yk, y_out, s) != hipSuccess)
+        return BEAM_ERR_HIP;
+      BoundaryArgs pb = *post;
+      pb.x = y_out;
+      if (launch_boundary(pb, s) != hipSuccess) return BEAM_ERR_HIP;
+    }
+  }
+  if (!next) return BEAM_OK;
+  bool q = false;
+  const int st = route_impl(next, next->ws, T, post->z_out, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, s, nullptr, nullptr, &q);
+  if (st == BEAM_OK) {
+    next->routed_T = T;
+    next->routed_z = post->z_out;
+    next->routed_quant = q;
+  }
+  return st;
 }
 
 
@@ -620,6 +680,7 @@ int beam_moe_set_activation_format(beam_moe_handle h, int32_t format) {
     return BEAM_ERR_INVALID_ARG;
   if (format == BEAM_ACT_MXFP4 && !h->mxfp4) return BEAM_ERR_UNSUPPORTED;
   h->act_mx = format == BEAM_ACT_MXFP4;
+  clear_routed(h);
   return BEAM_OK;
 }
 
@@ -734,6 +795,7 @@ int beam_router_topk(beam_moe_handle h, int32_t T, const uint16_t* z, float* log
   if (!z || !ids_out || !w_out || !aligned16(z) || ((uintptr_t)ids_out & 3u) ||
       ((uintptr_t)w_out & 3u) || (logits_out && ((uintptr_t)logits_out & 3u)))
     return BEAM_ERR_INVALID_ARG;
+  clear_routed(h);
   return route(h, h->ws, T, z, logits_out ? logits_out : h->ws.logits, ids_out, w_out,
                (hipStream_t)stream);
 }
@@ -747,6 +809,7 @@ int beam_grouped_topk(beam_moe_handle h, int32_t T, const float* logits, int32_t
       ((uintptr_t)w_out & 3u))
     return BEAM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  clear_routed(h);
   ProfScope ps(K_TOPK, s);
   TopkArgs ta = topk_args(h, h->ws, T, logits, nullptr, nullptr);
   ta.ids = ids_out;
@@ -769,6 +832,7 @@ int beam_moe_forward(beam_moe_handle h, int32_t T, const uint16_t* z, uint16_t* 
     if (p && ((uintptr_t)p & 3u)) return BEAM_ERR_INVALID_ARG;
   const beam_moe_config& c = h->cfg;
   if (overlaps(y_out, z, (int64_t)T * c.hidden * 2)) return BEAM_ERR_INVALID_ARG;
+  clear_routed(h);
   return forward_impl(h, h->ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, perm_out,
                       offsets_out, (hipStream_t)stream, nullptr, nullptr);
 }
@@ -834,8 +898,48 @@ int beam_moe_forward_boundary(beam_moe_handle h, int32_t T, const uint16_t* z,
   const float c1 = (float)sqrt((double)(n - 1) / (double)n);
   const float c2 = (float)(1.0 / sqrt((double)n));
   BoundaryArgs post{T, d, h_in, nullptr, w_post, w_pre, h_out, z_out, c1, c2, eps};
+  clear_routed(h);
   return forward_impl(h, h->ws, T, z, y_out, ids_in, w_in, logits_out, ids_out, w_out, nullptr,
                       nullptr, (hipStream_t)stream, nullptr, &post);
+}
+
+int beam_moe_forward_boundary_route(beam_moe_handle h, beam_moe_handle next, int32_t T,
+                                    const uint16_t* z, const uint16_t* h_in,
+                                    const uint16_t* w_post, const uint16_t* w_pre, int32_t n,
+                                    float eps, uint16_t* h_out, uint16_t* z_out, uint16_t* y_out,
+                                    int32_t routed, void* stream) {
+  if (!h || !next || h->dense || next->dense || T < 0) return BEAM_ERR_INVALID_ARG;
+  if (next->cfg.hidden != h->cfg.hidden) return BEAM_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens || T > next->cfg.max_tokens) return BEAM_ERR_CAPACITY;
+  if (T == 0) return BEAM_OK;
+  const int d = h->cfg.hidden;
+  if (n < 1 || !(eps >= 0.0f) || !isfinite(eps)) return BEAM_ERR_INVALID_ARG;
+  if (!z || !h_in || !w_post || !w_pre || !h_out || !z_out) return BEAM_ERR_INVALID_ARG;
+  if (!aligned16(z) || !aligned16(h_in) || !aligned16(w_post) || !aligned16(w_pre) ||
+      !aligned16(h_out) || !aligned16(z_out) || (y_out && !aligned16(y_out)))
+    return BEAM_ERR_INVALID_ARG;
+  if (d > kBoundaryWgMaxD && !y_out) return BEAM_ERR_UNSUPPORTED;
+  const int64_t bytes = (int64_t)T * d * 2;
+  // as beam_moe_forward_boundary: h_out may be h_in and z_out may be z
+  if ((h_out != h_in && overlaps(h_out, h_in, bytes)) || overlaps(h_out, z_out, bytes) ||
+      overlaps(z_out, h_in, bytes) || (z_out != z && overlaps(z_out, z, bytes)) ||
+      overlaps(h_out, z, bytes))
+    return BEAM_ERR_INVALID_ARG;
+  if (y_out) {
+    const void* others[] = {z, h_in, h_out, z_out};
+    for (const void* p : others)
+      if (overlaps(y_out, p, bytes)) return BEAM_ERR_INVALID_ARG;
+  }
+  if (routed && (h->routed_T != T || h->routed_z != z)) return BEAM_ERR_INVALID_ARG;
+  const bool pre_quantised = routed && h->routed_quant;
+  clear_routed(h);
+  clear_routed(next);
+  const float c1 = (float)sqrt((double)(n - 1) / (double)n);
+  const float c2 = (float)(1.0 / sqrt((double)n));
+  BoundaryArgs post{T, d, h_in, nullptr, w_post, w_pre, h_out, z_out, c1, c2, eps};
+  return forward_impl(h, h->ws, T, z, y_out, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, (hipStream_t)stream, nullptr, &post, routed != 0, pre_quantised,
+                      next);
 }
 
 int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, const uint16_t* x,
@@ -867,6 +971,7 @@ int beam_sublayer_forward(beam_moe_handle h, int32_t T, const uint16_t* h_in, co
   const float c1 = (float)sqrt((double)(n - 1) / (double)n);
   const float c2 = (float)(1.0 / sqrt((double)n));
   hipStream_t s = (hipStream_t)stream;
+  clear_routed(h);
   BoundaryArgs ba{T, d, h_in, x, w_post, w_pre, h_out, z_out, c1, c2, eps};
   if (T == 1 && d <= kBoundaryWgMaxD && c.topk <= kFusedRouteMaxSlots)
     return forward_impl(h, h->ws, T, z_out, y_out, nullptr, nullptr, logits_out, ids_out, w_out,

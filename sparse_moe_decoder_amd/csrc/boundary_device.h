@@ -68,7 +68,8 @@ struct BoundaryRow4 {
 
 __device__ __forceinline__ void boundary_row_4waves_load(const BoundaryArgs& a, int64_t t,
                                                          BoundaryRow4& b) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nch = a.d >> 3, nv = (nch + 63) >> 6;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -87,7 +88,9 @@ __device__ __forceinline__ void boundary_row_4waves_load(const BoundaryArgs& a, 
 __device__ __forceinline__ void boundary_row_4waves_finish(const BoundaryArgs& a, int64_t t,
                                                            BoundaryRow4& b, uint16_t* zl,
                                                            uint16_t* z_out, float (*red)[16]) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar branches keep the load counters exact for loads still in flight)
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nch = a.d >> 3, nv = (nch + 63) >> 6;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

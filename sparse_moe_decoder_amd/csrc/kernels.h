@@ -17,6 +17,7 @@ constexpr int kRouteSub = 16;
 constexpr int kRouteCounterStride = 64;
 constexpr int kRouteDoneWords = (1 + kRouteSub) * kRouteCounterStride;
 constexpr int kBoundaryWgMaxD = 8192;   // boundary rows up to this width: a workgroup per row
+constexpr int kChainMaxK = 8;  // combine + boundary + next routing in one launch up to this k
 
 struct BoundaryArgs {
   int T, d;
@@ -167,10 +168,13 @@ hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const
                                    uint32_t* done, uint64_t* sc, const RowQuantArgs& q,
                                    hipStream_t s);
 // one token (d <= 8192): the boundary of that token inside the same launch; z goes to
-// b.z_out and the router reads it, h' to b.h_out (which may be b.h)
+// b.z_out and the router reads it, h' to b.h_out (which may be b.h). cb not null: the
+// boundary's x is the combine of the previous MoE's expert rows (b.x unused; the combined
+// row goes to cb->y when that is not null).
 hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
                                        const PermArgs& a, uint32_t* done, uint64_t* sc,
-                                       const RowQuantArgs& q, hipStream_t s);
+                                       const RowQuantArgs& q, const CombineArgs* cb,
+                                       hipStream_t s);
 hipError_t launch_repack(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
                          uint16_t* wgu, uint16_t* wdp, int E, int f, int d, hipStream_t s);
 hipError_t launch_gateup_stream(const ExpertArgs& a, int max_active, hipStream_t s);

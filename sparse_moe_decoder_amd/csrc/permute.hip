@@ -507,6 +507,77 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
   }
 }
 
+// The row loads of boundary_row_4waves_load for one token (t = 0) with x the weighted combine
+// of the token's k expert rows of the previous MoE (cb), in combine_chunk's arithmetic: every
+// slot's row chunk and the slot ids are loaded together (slot j's row is in bounds whatever
+// its id), then the FP32 adds in slot order from -0.0 skip the invalid ids, and one rounding.
+// after_loads() issues the caller's own loads behind the rows. k <= 8 (kChainMaxK).
+template <class AfterLoads>
+__device__ __forceinline__ void boundary_row_4waves_load_combine(const BoundaryArgs& a,
+                                                                 const CombineArgs& cb,
+                                                                 BoundaryRow4& b,
+                                                                 AfterLoads after_loads) {
+  const int lane = threadIdx.x & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform branches
+  const int nch = a.d >> 3, nv = (nch + 63) >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int vv = wvu + 4 * j, idx = 64 * vv + lane;
+    const int li = idx < nch ? idx : 0;
+    if (vv < nv) {
+      b.hv[j] = ld_u32x4((const u32x4*)a.h + li);
+      b.wo[j] = ld_u32x4((const u32x4*)a.w_post + li);
+      b.wr[j] = ld_u32x4((const u32x4*)a.w_pre + li);
+    }
+  }
+  float acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = -0.0f;
+  // slots j0 .. j0 + 7: ids and rows loaded together, then the adds in slot order
+  auto slots8 = [&](int j0) {
+    int e8[8];
+    u32x4 v[4][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int slot = j0 + u < cb.k ? j0 + u : j0;  // past k: a valid row, not added
+      e8[u] = j0 + u < cb.k ? cb.ids[slot] : -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vv = wvu + 4 * j, idx = 64 * vv + lane;
+        if (vv < nv)
+          v[j][u] = ld_u32x4((const u32x4*)(cb.yk + (int64_t)slot * a.d) + (idx < nch ? idx : 0));
+      }
+    }
+    if (j0 == 0) {  // the caller's loads go out behind the first rows
+      __builtin_amdgcn_sched_barrier(0);
+      after_loads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = e8[u] >= 0 && e8[u] < cb.E;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (wvu + 4 * j < nv) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // an invalid slot leaves the sum as it is (even -0.0)
+            const float s0 = acc[j][2 * i] + lo_bf(v[j][u][i]);
+            const float s1 = acc[j][2 * i + 1] + hi_bf(v[j][u][i]);
+            acc[j][2 * i] = ok ? s0 : acc[j][2 * i];
+            acc[j][2 * i + 1] = ok ? s1 : acc[j][2 * i + 1];
+          }
+        }
+    }
+  };
+  slots8(0);  // k <= 8: straight-line code, so the load counters stay exact
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.xv[j][i] = pack_bf2(acc[j][2 * i], acc[j][2 * i + 1]);
+}
+
 // Router, grouped top-k and grouping of a small batch (T <= 16 tokens, T * k <= 64
 // slots) in one launch: one workgroup per expert computes its logits exactly as the
 // stand-alone small-batch router does, writes them out, and publishes each token's
@@ -525,11 +596,16 @@ __device__ void route_one_token_wg(const TopkArgs& ta, const PermArgs& pa, const
 // four lanes to a block, and write each block's MXFP4 codes, scale and round trip next to
 // their logits (the rows are at hand; the stores complete before the workgroup counts
 // itself).
-template <bool BOUNDARY, bool QUANT>
+// COMBINE (with BOUNDARY): the boundary's x is the weighted combine of the previous MoE's
+// expert rows (cb; every workgroup combines the row itself; workgroup 0 writes it to cb.y
+// when that is not null): the combine, the next sublayer boundary and that sublayer's
+// routing in one launch. Every workgroup has read cb.ids before it counts itself, so the
+// last one may overwrite them (the same handle routing its next call).
+template <bool BOUNDARY, bool QUANT, bool COMBINE>
 __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, TopkArgs ta,
                                                                PermArgs pa, uint32_t* done,
                                                                uint64_t* sc, BoundaryArgs ba,
-                                                               RowQuantArgs rq) {
+                                                               RowQuantArgs rq, CombineArgs cb) {
   __shared__ float part[3][kRouterRT];
   __shared__ __attribute__((aligned(16))) float c_lds[4][256];
   __shared__ int32_t sel[4][32];
@@ -559,9 +635,23 @@ __global__ __launch_bounds__(256) void route_fused_tiny_kernel(RouterArgs ra, To
     __shared__ float red[2][16];
     __shared__ __attribute__((aligned(16))) uint16_t zl[kBoundaryWgMaxD];
     f32x4 w[kRouterPreChunks];
-    boundary_row_4waves_load(ba, 0, brow);
-    __builtin_amdgcn_sched_barrier(0);
-    router_load_w(ra, e, w);
+    if constexpr (COMBINE) {
+      // as below: the rows' loads (the expert rows and h; L2 or cache hits) first, the router
+      // weights (HBM) after them, so the combine and the boundary run while they are in flight
+      boundary_row_4waves_load_combine(ba, cb, brow, [&] { router_load_w(ra, e, w); });
+      if (e == 0 && cb.y) {
+        const int nch = ba.d >> 3, nv = (nch + 63) >> 6;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int vv = wv + 4 * j, idx = 64 * vv + lane;
+          if (vv < nv && idx < nch) st_u32x4((u32x4*)cb.y + idx, brow.xv[j]);
+        }
+      }
+    } else {
+      boundary_row_4waves_load(ba, 0, brow);
+      __builtin_amdgcn_sched_barrier(0);
+      router_load_w(ra, e, w);
+    }
     __builtin_amdgcn_sched_barrier(0);
     boundary_row_4waves_finish(ba, 0, brow, zl, e == 0 ? ba.z_out : nullptr, red);
     v = router_dot_1_lds(ra, w, zl, part);
@@ -638,23 +728,32 @@ hipError_t launch_route_fused_tiny(const RouterArgs& r, const TopkArgs& t, const
                                    uint32_t* done, uint64_t* sc, const RowQuantArgs& q,
                                    hipStream_t s) {
   if (q.zq)
-    hipLaunchKernelGGL((route_fused_tiny_kernel<false, true>), dim3((unsigned)r.E), dim3(256), 0, s,
-                       r, t, a, done, sc, BoundaryArgs{}, q);
+    hipLaunchKernelGGL((route_fused_tiny_kernel<false, true, false>), dim3((unsigned)r.E), dim3(256),
+                       0, s, r, t, a, done, sc, BoundaryArgs{}, q, CombineArgs{});
   else
-    hipLaunchKernelGGL((route_fused_tiny_kernel<false, false>), dim3((unsigned)r.E), dim3(256), 0,
-                       s, r, t, a, done, sc, BoundaryArgs{}, q);
+    hipLaunchKernelGGL((route_fused_tiny_kernel<false, false, false>), dim3((unsigned)r.E),
+                       dim3(256), 0, s, r, t, a, done, sc, BoundaryArgs{}, q, CombineArgs{});
   return hipGetLastError();
 }
 
 hipError_t launch_boundary_route_fused(const BoundaryArgs& b, const RouterArgs& r, const TopkArgs& t,
                                        const PermArgs& a, uint32_t* done, uint64_t* sc,
-                                       const RowQuantArgs& q, hipStream_t s) {
-  if (q.zq)
-    hipLaunchKernelGGL((route_fused_tiny_kernel<true, true>), dim3((unsigned)r.E), dim3(256), 0, s,
-                       r, t, a, done, sc, b, q);
-  else
-    hipLaunchKernelGGL((route_fused_tiny_kernel<true, false>), dim3((unsigned)r.E), dim3(256), 0, s,
-                       r, t, a, done, sc, b, q);
+                                       const RowQuantArgs& q, const CombineArgs* cb, hipStream_t s) {
+  const dim3 g((unsigned)r.E), blk(256);
+  if (cb) {
+    if (q.zq)
+      hipLaunchKernelGGL((route_fused_tiny_kernel<true, true, true>), g, blk, 0, s, r, t, a, done,
+                         sc, b, q, *cb);
+    else
+      hipLaunchKernelGGL((route_fused_tiny_kernel<true, false, true>), g, blk, 0, s, r, t, a, done,
+                         sc, b, q, *cb);
+  } else if (q.zq) {
+    hipLaunchKernelGGL((route_fused_tiny_kernel<true, true, false>), g, blk, 0, s, r, t, a, done, sc,
+                       b, q, CombineArgs{});
+  } else {
+    hipLaunchKernelGGL((route_fused_tiny_kernel<true, false, false>), g, blk, 0, s, r, t, a, done,
+                       sc, b, q, CombineArgs{});
+  }
   return hipGetLastError();
 }
 

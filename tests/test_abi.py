@@ -99,11 +99,13 @@ def test_handle_calls_reject_null_handle(L):
                                    None) == -1
     assert L.beam_moe_forward_boundary(None, 1, p, p, p, p, 20, 1e-6, p, p, None, None, None,
                                        None, None, None, None) == -1
+    assert L.beam_moe_forward_boundary_route(None, None, 1, p, p, p, p, 20, 1e-6, p, p, None, 0,
+                                             None) == -1
     assert L.beam_moe_destroy(None) == 0
 
 
 def test_profile_api_without_records(L):
-    assert L.beam_kernel_count() == 8
+    assert L.beam_kernel_count() == 9
     assert L.beam_kernel_name(4) == b"gate_up"
     assert L.beam_kernel_name(99) is None
     ms, n = ctypes.c_double(), ctypes.c_int64()
