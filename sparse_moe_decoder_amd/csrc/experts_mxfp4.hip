@@ -288,6 +288,161 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertArgs a) {
   }
 }
 
+// Single-token gate/up (T = 1, d / 4 <= 2048): gateup_fp4_kernel<1, U, 1>'s grid, split,
+// k-step order and reduction, with the token row staged in LDS (one_row_load) so the
+// register ring of U quads holds codes and scales only. Every row an expert holds at
+// T = 1 is the one token, so the result is written to each of them. Same results bit
+// for bit.
+template <int U>
+__global__ __launch_bounds__(256) void gateup_fp4_one_kernel(ExpertArgs a) {
+  const int NJ = a.f / 16;
+  const int j0 = blockIdx.x % NJ;
+  const int e = active_expert(a, blockIdx.x / NJ);
+  if (e < 0) return;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int KQ = a.d / 128, kqw = KQ / 4, kq0 = wv * kqw;
+  const int64_t quad0 = ((int64_t)e * NJ + j0) * KQ + kq0;
+  const uint8_t* cp = a.qgu + quad0 * 2 * 1024 + lane * 16;
+  const uint8_t* sp = a.sgu + quad0 * 2 * 64 + (lane & 15) * 4;
+  __shared__ u32x4 xs[4][kOneRowChunks * 64];
+  __shared__ f32x4 red[3][2][64];
+  one_row_load(xs[wv], a.z + kq0 * 128, kqw * 16, lane);  // the token is row 0 of z
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 cg[U], cu[U];
+  uint32_t sg[U], su[U];
+  auto load = [&](int u, int kq) {
+    const int64_t q = (int64_t)kq * 2;
+    cg[u] = ld_stream_u32x4(cp + q * 1024);
+    cu[u] = ld_stream_u32x4(cp + q * 1024 + 1024);
+    sg[u] = ld_stream_u32(sp + q * 64);
+    su[u] = ld_stream_u32(sp + q * 64 + 64);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  one_row_wait<4 * U>();
+  const u32x4* xp = xs[wv] + (lane >> 4);
+  f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+  auto use = [&](int u, int kq) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 x = xp[(kq * 4 + s) * 4];
+      const u32x4 bg = fp4x8_to_bf16(cg[u][s], e8m0_scale((sg[u] >> (8 * s)) & 255u));
+      const u32x4 bu = fp4x8_to_bf16(cu[u][s], e8m0_scale((su[u] >> (8 * s)) & 255u));
+      ag = mfma16(x, bg, ag);
+      au = mfma16(x, bu, au);
+    }
+  };
+  for (int kq = 0; kq < kqw - U; kq += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      use(u, kq + u);
+      load(u, kq + U + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) use(u, kqw - U + u);
+  if (wv > 0) {
+    red[wv - 1][0][lane] = ag;
+    red[wv - 1][1][lane] = au;
+  }
+  __syncthreads();
+  if (wv == 0 && lane < 16) {  // output row 0 (lanes 0..15, element 0)
+    int row0, cnt;
+    expert_rows(a, e, row0, cnt);
+    float g = ag[0], u = au[0];
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      g += red[w][0][lane][0];
+      u += red[w][1][lane][0];
+    }
+    const float gv = bf2f(f2bf(g)), uv = bf2f(f2bf(u));
+    const uint16_t v = f2bf(silu(gv) * uv);
+    for (int r = 0; r < cnt; ++r) a.act[(int64_t)(row0 + r) * a.f + j0 * 16 + lane] = v;
+  }
+}
+
+// Single-token down (T = 1, f / 4 <= 2048): down_split_fp4_kernel<·, 2>'s grid, split and
+// order, with the expert's activation row staged in LDS after the weights' first U quads
+// are issued, and each row's slot written from the one sum.
+template <int U>
+__global__ __launch_bounds__(256) void down_fp4_one_kernel(ExpertArgs a) {
+  constexpr int NTW = 2;
+  const int ND = a.d / 16, NB = ND / NTW;
+  const int nt0 = (blockIdx.x % NB) * NTW;
+  const int e = active_expert(a, blockIdx.x / NB);
+  if (e < 0) return;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int KQ = a.f / 128, kqw = KQ / 4, kq0 = wv * kqw;
+  const int64_t quad0 = ((int64_t)e * ND + nt0) * KQ + kq0;
+  const uint8_t* cp = a.qd + quad0 * 1024 + lane * 16;
+  const uint8_t* sp = a.sd + quad0 * 64 + (lane & 15) * 4;
+  __shared__ u32x4 xs[4][kOneRowChunks * 64];
+  __shared__ f32x4 red[3][NTW][64];
+  u32x4 c[U][NTW];
+  uint32_t sc[U][NTW];
+  auto load = [&](int u, int kq) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      c[u][t] = ld_stream_u32x4(cp + ((int64_t)t * KQ + kq) * 1024);
+      sc[u][t] = ld_stream_u32(sp + ((int64_t)t * KQ + kq) * 64);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int row0, cnt;
+  expert_rows(a, e, row0, cnt);
+  one_row_load(xs[wv], a.act + (int64_t)row0 * a.f + kq0 * 128, kqw * 16, lane);
+  one_row_wait<0>();
+  const u32x4* xp = xs[wv] + (lane >> 4);
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto use = [&](int u, int kq) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 x = xp[(kq * 4 + s) * 4];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[t] = mfma16(x, fp4x8_to_bf16(c[u][t][s], e8m0_scale((sc[u][t] >> (8 * s)) & 255u)),
+                        acc[t]);
+    }
+  };
+  for (int kq = 0; kq < kqw - U; kq += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      use(u, kq + u);
+      load(u, kq + U + u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) use(u, kqw - U + u);
+  if (wv > 0) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) red[wv - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wv == 0 && lane < 16) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      float v = acc[t][0];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) v += red[w][t][lane][0];
+      for (int r = 0; r < cnt; ++r) {
+        const int slot = a.perm[row0 + r];
+        a.yk[(int64_t)slot * a.d + (nt0 + t) * 16 + lane] = f2bf(a.w[slot] * v);
+      }
+    }
+  }
+}
+
 // Down for batches up to 16 tokens: one workgroup per (active expert, NTW tiles of
 // 16 output columns), the four waves split K (f) into quarters with a ring of U
 // quads each; the quarters are added in wave order and bf16(w * sum) goes to the
@@ -461,11 +616,21 @@ __global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
 // height changes no result, and most experts hold few rows at these batch sizes.
 // Tiles per wave and ring depths (measured on Beam's shapes): gate/up one tile per
 // wave up to 16 tokens (more workgroups for the few experts), two above; down two
-// tiles per wave up to 16 tokens, four above with a ring of two quads. Deeper rings
-// at one token (five quads, all of a wave's quarter) cost occupancy and measured slower.
+// tiles per wave up to 16 tokens, four above with a ring of two quads. One token takes
+// the single-token kernels (row in LDS) with rings of five quads (half of a gate/up
+// wave's quarter, all of a down wave's): with the row out of the ring, deeper rings
+// keep the occupancy that rows in registers cost.
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int kqw = a.d / 128 / 4;  // >= 1; U = 2 when it divides
-  if (a.T <= 16) {
+  if (a.T == 1 && kqw * 16 <= kOneRowChunks * 64) {
+    dim3 g((unsigned)(max_active * (a.f / 16))), blk(256);
+    if (kqw % 5 == 0)
+      hipLaunchKernelGGL((gateup_fp4_one_kernel<5>), g, blk, 0, s, a);
+    else if (kqw % 2 == 0)
+      hipLaunchKernelGGL((gateup_fp4_one_kernel<2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((gateup_fp4_one_kernel<1>), g, blk, 0, s, a);
+  } else if (a.T <= 16) {
     dim3 g((unsigned)(max_active * (a.f / 16))), blk(256);
     if (kqw % 2 == 0)
       hipLaunchKernelGGL((gateup_fp4_kernel<1, 2, 1>), g, blk, 0, s, a);
@@ -482,7 +647,16 @@ hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s)
 }
 
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
-  if (a.T <= kSplitDownMaxT) {
+  const int kqw = a.f / 128 / 4;
+  if (a.T == 1 && kqw * 16 <= kOneRowChunks * 64) {
+    dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
+    if (kqw % 5 == 0)
+      hipLaunchKernelGGL((down_fp4_one_kernel<5>), g, blk, 0, s, a);
+    else if (kqw % 2 == 0)
+      hipLaunchKernelGGL((down_fp4_one_kernel<2>), g, blk, 0, s, a);
+    else
+      hipLaunchKernelGGL((down_fp4_one_kernel<1>), g, blk, 0, s, a);
+  } else if (a.T <= kSplitDownMaxT) {
     dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
     hipLaunchKernelGGL((down_split_fp4_kernel<1, 2>), g, blk, 0, s, a);
   } else {

@@ -6,11 +6,13 @@
 
 namespace beam {
 
-// 2^(s - 127) as an FP32 multiplier (s = 0 is 2^-127, a subnormal; s = 255, the
-// E8M0 NaN, is never produced by the quantiser)
-__device__ __forceinline__ float e8m0_scale(uint32_t s) {
-  return __uint_as_float(s ? (s << 23) : 0x00400000u);
-}
+// The scale operand of v_cvt_scalef32_pk_bf16_fp4 for E8M0 byte s (2^(s - 127)): the
+// byte in the FP32 exponent field. The instruction takes the scale from that field alone,
+// so s = 0 (0.0 here) converts as 2^-127 — on gfx950 every code pair converts to the same
+// bits with this operand as with the exact multiplier (the subnormal 2^-127 for s = 0),
+// for every s in 0 .. 254. s = 255, the E8M0 NaN, is never produced by the quantiser.
+// Only for the conversion instructions: not an FP32 multiplier for s = 0.
+__device__ __forceinline__ float e8m0_scale(uint32_t s) { return __uint_as_float(s << 23); }
 
 // Eight codes (one dword) times the scale: the BF16 operand fragment, element i in
 // half-word i. v_cvt_scalef32_pk_bf16_fp4 converts the code pair of one byte; every

@@ -126,9 +126,10 @@ def test_mxfp4_equals_bf16_on_dequantised(layer, T):
     torch.cuda.synchronize()
     assert np.array_equal(r4["ids_out"].cpu().numpy(), rd["ids_out"].cpu().numpy())
     assert np.array_equal(P.bits(y4), P.bits(yd)), f"T={T}"
-    # replayed routing (a few slots pointing at no expert)
+    # replayed routing (a slot pointing at no expert, one naming an expert twice)
     ids = r4["ids_out"].clone()
     ids[0, 1] = -1
+    ids[0, 2] = ids[0, 0]
     w = r4["w_out"].clone()
     y4r = layer["moe4"].forward(z, ids_in=ids, w_in=w)
     ydr = layer["moe_deq"].forward(z, ids_in=ids, w_in=w)

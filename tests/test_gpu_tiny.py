@@ -159,6 +159,25 @@ def test_replay_invalid_and_all_experts(gpu, host):
                               WL.E)
 
 
+def test_replay_one_token_repeated_expert(gpu, host):
+    """One token whose replayed routing names one expert three times (and has an invalid
+    slot): that expert holds three rows of the same token, each slot scaled by its own
+    weight, as the oracle's per-slot experts give."""
+    import torch
+    z1 = host["z"][:1].copy()
+    ids = host["ids"][:1].copy()
+    ids[0, 1] = ids[0, 0]
+    ids[0, 5] = ids[0, 0]
+    ids[0, 3] = -1
+    w = host["w"][:1].copy()
+    y, r = gpu["moe"].forward(P.to_dev(z1), ids_in=torch.from_numpy(ids).cuda(),
+                              w_in=torch.from_numpy(w).cuda(), want_routing=True)
+    o_y, _ = oracle.moe_experts(z1, ids, w, WL.E, host["experts"].__getitem__)
+    P.assert_bf16_close(P.bits(y), o_y, "tiny y (one token, repeated expert)")
+    P.check_permutation_valid(ids, r["perm_out"].cpu().numpy(), r["offsets_out"].cpu().numpy(),
+                              WL.E)
+
+
 def test_deterministic(gpu, host):
     z = P.to_dev(host["z"])
     a = P.bits(gpu["moe"].forward(z))
