@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -97,11 +98,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(*names):
+def source_hash(unit):
+    """Hash of a kernel source file and every local header it includes (transitively):
+    a committed counter summary applies only while this is unchanged."""
+    csrc = os.path.join(ROOT, "sparse_moe_decoder_amd", "csrc")
+    seen, todo = [], [unit]
+    while todo:
+        n = todo.pop(0)
+        if n in seen:
+            continue
+        seen.append(n)
+        with open(os.path.join(csrc, n)) as fh:
+            for line in fh:
+                m = re.match(r'\s*#include\s+"([^"]+)"', line)
+                if m and os.path.exists(os.path.join(csrc, m.group(1))):
+                    todo.append(m.group(1))
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "sparse_moe_decoder_amd", "csrc", n), "rb") as fh:
-            h.update(fh.read())
+    for n in sorted(seen):
+        with open(os.path.join(csrc, n), "rb") as fh:
+            h.update(n.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -301,9 +316,11 @@ def measure(wl, moe, dense_h, args, mx):
     gu_us = kernel_us.get("gate_up")
     a4 = args.act == "mxfp4"
     a4_gemm = a4 and T > STREAM_MAX_T  # up to 128 tokens W4A4 runs on the 4-bit weight streams
-    src = source_hash(*(("experts_w4a4.hip", "gemm_device.h", "mxfp4_device.h", "common.h") if a4_gemm
-                        else ("experts.hip", "experts_mxfp4.hip", "common.h") if mx
-                        else ("experts.hip", "common.h")))
+    # the gate/up kernel's source file: W4A4 GEMMs, 4-bit weight streams, else experts.hip
+    # (BF16 streams and grouped GEMMs, and the 4-bit-weight grouped GEMM)
+    src = source_hash("experts_w4a4.hip" if a4_gemm
+                      else "experts_mxfp4.hip" if (mx and T <= STREAM_MAX_T)
+                      else "experts.hip")
     ctr_name = "gate_up_w4a4" if a4_gemm else "gate_up_mxfp4" if mx else "gate_up"
     wbytes = (0.5 + 1.0 / 32) if mx else 2.0  # bytes per expert weight (codes + scales)
     if decode:
