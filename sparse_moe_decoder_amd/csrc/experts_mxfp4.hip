@@ -365,12 +365,12 @@ __global__ __launch_bounds__(256) void gateup_fp4_one_kernel(ExpertArgs a) {
   }
 }
 
-// Single-token down (T = 1, f / 4 <= 2048): down_split_fp4_kernel<·, 2>'s grid, split and
-// order, with the expert's activation row staged in LDS after the weights' first U quads
-// are issued, and each row's slot written from the one sum.
-template <int U>
+// Single-token down (T = 1, f / 4 <= 2048): down_split_fp4_kernel's K split and order over
+// NTW 16-column tiles per wave (one at one token: twice the workgroups of the split kernel,
+// measured faster), with the expert's activation row staged in LDS after the weights' first
+// U quads are issued, and each row's slot written from the one sum.
+template <int U, int NTW>
 __global__ __launch_bounds__(256) void down_fp4_one_kernel(ExpertArgs a) {
-  constexpr int NTW = 2;
   const int ND = a.d / 16, NB = ND / NTW;
   const int nt0 = (blockIdx.x % NB) * NTW;
   const int e = active_expert(a, blockIdx.x / NB);
@@ -618,8 +618,8 @@ __global__ __launch_bounds__(256) void down_stream_fp4_kernel(ExpertArgs a) {
 // wave up to 16 tokens (more workgroups for the few experts), two above; down two
 // tiles per wave up to 16 tokens, four above with a ring of two quads. One token takes
 // the single-token kernels (row in LDS) with rings of five quads (half of a gate/up
-// wave's quarter, all of a down wave's): with the row out of the ring, deeper rings
-// keep the occupancy that rows in registers cost.
+// wave's quarter, all of a down wave's) and one down tile per wave: with the row out
+// of the ring, deeper rings keep the occupancy that rows in registers cost.
 hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int kqw = a.d / 128 / 4;  // >= 1; U = 2 when it divides
   if (a.T == 1 && kqw * 16 <= kOneRowChunks * 64) {
@@ -649,13 +649,13 @@ hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s)
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int kqw = a.f / 128 / 4;
   if (a.T == 1 && kqw * 16 <= kOneRowChunks * 64) {
-    dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
+    dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
     if (kqw % 5 == 0)
-      hipLaunchKernelGGL((down_fp4_one_kernel<5>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((down_fp4_one_kernel<5, 1>), g, blk, 0, s, a);
     else if (kqw % 2 == 0)
-      hipLaunchKernelGGL((down_fp4_one_kernel<2>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((down_fp4_one_kernel<2, 1>), g, blk, 0, s, a);
     else
-      hipLaunchKernelGGL((down_fp4_one_kernel<1>), g, blk, 0, s, a);
+      hipLaunchKernelGGL((down_fp4_one_kernel<1, 1>), g, blk, 0, s, a);
   } else if (a.T <= kSplitDownMaxT) {
     dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
     hipLaunchKernelGGL((down_split_fp4_kernel<1, 2>), g, blk, 0, s, a);
