@@ -136,6 +136,43 @@ def test_mxfp4_equals_bf16_on_dequantised(layer, T):
     assert np.array_equal(P.bits(y4r), P.bits(ydr)), f"T={T} replay"
 
 
+@pytest.mark.parametrize("d", [8192, 8704])
+def test_mxfp4_one_token_wide_rows(d):
+    """One token on rows at the single-token passes' limit (hidden 8192: a wave's quarter of
+    the row fills its LDS area) and past it (8704: the generic passes), with computed routing
+    and with replayed routing that names an expert twice: the 4-bit handle equals the BF16
+    handle on the oracle's dequantised weights bit for bit."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    wl = synth.Workload(f"wide{d}", T=1, d=d, E=8, G=2, kg=1, k=2, f=512)
+    print(f"[mxfp4] wide layer {wl}", flush=True)
+    q, deq = quantised_experts(wl, range(wl.E))
+    stack = lambda m, i: np.stack([q[e][m][i] for e in range(wl.E)])  # noqa: E731
+    W, b = sd.router(wl)
+    cfg = sd.moe_config(wl, max_tokens=4)
+    moe4 = beam.BeamMoE(cfg, W, b, None, None, None,
+                        mxfp4=tuple(P.to_dev(stack(m, i)) for m in range(3) for i in range(2)))
+    moed = beam.BeamMoE(cfg, W, b, *[P.to_dev(np.stack([deq[e][m] for e in range(wl.E)]))
+                                     for m in range(3)])
+    try:
+        z = sd.tokens(wl, "h", T=1)
+        y4, r4 = moe4.forward(z, want_routing=True)
+        yd, rd = moed.forward(z, want_routing=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(r4["ids_out"].cpu().numpy(), rd["ids_out"].cpu().numpy())
+        assert np.array_equal(P.bits(y4), P.bits(yd)), f"d={d}"
+        ids = r4["ids_out"].clone()
+        ids[0, 1] = ids[0, 0]
+        w = r4["w_out"].clone()
+        y4r = moe4.forward(z, ids_in=ids, w_in=w)
+        ydr = moed.forward(z, ids_in=ids, w_in=w)
+        assert np.array_equal(P.bits(y4r), P.bits(ydr)), f"d={d} replay"
+    finally:
+        moe4.close()
+        moed.close()
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_mxfp4_fused_entry_points(layer, T):
     """beam_sublayer_forward and beam_moe_forward_boundary on an MXFP4 handle equal the
