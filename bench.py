@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--act", choices=("bf16", "mxfp4"), default="bf16",
                    help="activation format of the expert GEMMs: BF16, or MXFP4 (4-bit activations "
                         "on the FP4 matrix cores; needs --experts mxfp4)")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip measuring the copy and vendor-GEMM references on this GPU")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies of BYTES (for scaling HBM "
                         "counter readings) and exit")
@@ -96,6 +98,43 @@ def copy_calibration(nbytes: int, reps: int = 5):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_peaks(reps: int = 5):
+    """What this GPU itself reaches, reported beside the published peaks: a plain
+    device-to-device copy of 1 GiB (bytes read + bytes written per second) and the vendor
+    BF16 GEMM (torch.matmul, hipBLASLt) on 8192 x 8192 x 8192 random operands; each the
+    fastest of `reps` timed runs after one untimed run."""
+    import torch
+
+    def best_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * n / (best_ms(lambda: dst.copy_(src)) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((m, m), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((m, m), device="cuda", dtype=torch.bfloat16, generator=g)
+    gemm_tf = 2.0 * m ** 3 / (best_ms(lambda: torch.matmul(a, b)) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+            "what": "1 GiB device copy (read + write bytes); torch.matmul BF16 8192^3 (hipBLASLt)"}
 
 
 def source_hash(unit):
@@ -443,6 +482,15 @@ def main():
         if dense_h is not None:
             beam.beam_moe_destroy(dense_h)
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        log(f"measured on this GPU: {peaks}")
+        for ent in entries.values():
+            r = ent["roofline"]
+            ref = (peaks["hbm_copy_GBps"] if r["bound"] == "hbm"
+                   else peaks["bf16_gemm_TFLOPs"] if r["peak"] == BF16_PEAK_TFLOPS else None)
+            r["frac_of_measured"] = round(r["achieved"] / ref, 4) if ref else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(head, args.cpu_sample, mxfp4=mx, act4=args.act == "mxfp4")
@@ -472,6 +520,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init weights of Beam's MoE layer)",
         "config": config,
         "roofline": e["roofline"],
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
