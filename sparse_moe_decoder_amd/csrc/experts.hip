@@ -470,9 +470,11 @@ hipError_t launch_down_stream(const ExpertArgs& a, int max_active, hipStream_t s
 // for gate/up: the z rows of their tokens), columns are 128 gate + 128 up outputs
 // (gate/up) or 256 outputs (down). Wave w = 4 wm + wn owns the 32-row tiles
 // 2 mt + wm (mt < MW) x columns [64 wn, 64 wn + 64) as MW x 2 MFMA tiles; MW =
-// ceil(rows / 64), the same for every wave, so a partial tile costs in 64-row steps.
-// An expert's rows are cut into ceil(rows / 256) tiles of equal size (a multiple of
-// 64), so the tiles that share one weight tile take the same time.
+// ceil(rows / 64). With an odd number of 32-row tiles the wm = 1 waves skip their last
+// tile's MFMAs; each SIMD holds one wm = 0 and one wm = 1 wave, so its matrix core does
+// the work of the rows rounded up to 32. An expert's rows are cut into ceil(rows / 256)
+// tiles of equal size (a multiple of 32), so the tiles that share one weight tile take
+// the same time.
 //
 // K advances 32 at a time through NS LDS stages (NS = 5 when K / 32 is a multiple
 // of 5, else 4) filled by direct global-to-LDS 16-byte loads (global_load_lds_dwordx4:
@@ -532,12 +534,15 @@ constexpr int GSTAGE_Q = 4096 + 256;  // bytes per 4-bit B stage
 
 template <bool GATEUP, int MW, int NS, bool FP4 = false>
 __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTile& t,
-                                               uint16_t* smem) {
+                                               uint16_t* smem, bool odd) {
   constexpr int NW = 8;
   static_assert(NS >= 3 && NS <= GMAXST && NS - 2 <= 3, "stages");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
   const int wm = wvu >> 2, wn = wvu & 3;
+  // an odd number of 32-row tiles leaves wm = 1 one tile short: its last MFMAs are skipped
+  // (the SIMD it shares with a wm = 0 wave then does 2 MW - 1 tiles' work)
+  const bool skip_last = odd && wm == 1;
   const int K = GATEUP ? a.d : a.f;
   const int KS = K / 32;
   const int nkb = K / GBK;  // a multiple of NS
@@ -676,8 +681,10 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int mt = 0; mt < MW; ++mt) {
+        if (mt + 1 < MW || !skip_last) {
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
+          for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
+        }
         const int q = kk * MW + mt;
         if (q % EVERY == 0 && q / EVERY < CP) {
           __builtin_amdgcn_sched_barrier(0);
@@ -770,11 +777,13 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
 
 template <bool GATEUP, int NS, bool FP4 = false>
 __device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile& t, uint16_t* smem) {
-  switch ((t.rows + 63) >> 6) {  // 64-row steps: tiles per wave
-    case 1: gemm_tile_body<GATEUP, 1, NS, FP4>(a, t, smem); break;
-    case 2: gemm_tile_body<GATEUP, 2, NS, FP4>(a, t, smem); break;
-    case 3: gemm_tile_body<GATEUP, 3, NS, FP4>(a, t, smem); break;
-    default: gemm_tile_body<GATEUP, 4, NS, FP4>(a, t, smem); break;
+  const int n32 = (t.rows + 31) >> 5;  // 32-row tiles: wm = 0 takes the even ones, wm = 1 the odd
+  const bool odd = n32 & 1;
+  switch ((n32 + 1) >> 1) {  // tiles per wave
+    case 1: gemm_tile_body<GATEUP, 1, NS, FP4>(a, t, smem, odd); break;
+    case 2: gemm_tile_body<GATEUP, 2, NS, FP4>(a, t, smem, odd); break;
+    case 3: gemm_tile_body<GATEUP, 3, NS, FP4>(a, t, smem, odd); break;
+    default: gemm_tile_body<GATEUP, 4, NS, FP4>(a, t, smem, odd); break;
   }
 }
 

@@ -120,11 +120,13 @@ __device__ __forceinline__ f32x16 mfma_fp4(const u32x4& a, uint32_t sa, const u3
 
 template <bool GATEUP, int MW>
 __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const GemmTile& t,
-                                                  uint8_t* smem) {
+                                                  uint8_t* smem, bool odd) {
   constexpr int NW = 8;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int wm = wvu >> 2, wn = wvu & 3;
+  // an odd number of 32-row tiles leaves wm = 1 one tile short: its last MFMAs are skipped
+  const bool skip_last = odd && wm == 1;
   const int K = GATEUP ? a.d : a.f;
   const int nkb = K / QBK;  // a multiple of QNS - 1 is not needed: the loop handles any count
   const int e = t.e, row0 = t.row0, rows = t.rows, nb = t.nb;
@@ -239,9 +241,11 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
       }
 #pragma unroll
       for (int mt = 0; mt < MW; ++mt) {
+        if (mt + 1 < MW || !skip_last) {
 #pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-          acc[mt][nn] = mfma_fp4(fa[mt], sa[mt], fb[nn], sb[nn], acc[mt][nn]);
+          for (int nn = 0; nn < 2; ++nn)
+            acc[mt][nn] = mfma_fp4(fa[mt], sa[mt], fb[nn], sb[nn], acc[mt][nn]);
+        }
         if (q < CP) {
           __builtin_amdgcn_sched_barrier(0);
           if (more) issue(kn, sn, q);
@@ -340,11 +344,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_a4_kernel(ExpertArgs a) {
   const int L = xcd * R + q;
   if (q >= R || L >= total) return;
   const GemmTile t = decode_tile(a, NT, L);
-  switch ((t.rows + 63) >> 6) {
-    case 1: gemm_a4_tile_body<GATEUP, 1>(a, t, smem); break;
-    case 2: gemm_a4_tile_body<GATEUP, 2>(a, t, smem); break;
-    case 3: gemm_a4_tile_body<GATEUP, 3>(a, t, smem); break;
-    default: gemm_a4_tile_body<GATEUP, 4>(a, t, smem); break;
+  const int n32 = (t.rows + 31) >> 5;  // 32-row tiles: wm = 0 takes the even ones, wm = 1 the odd
+  const bool odd = n32 & 1;
+  switch ((n32 + 1) >> 1) {
+    case 1: gemm_a4_tile_body<GATEUP, 1>(a, t, smem, odd); break;
+    case 2: gemm_a4_tile_body<GATEUP, 2>(a, t, smem, odd); break;
+    case 3: gemm_a4_tile_body<GATEUP, 3>(a, t, smem, odd); break;
+    default: gemm_a4_tile_body<GATEUP, 4>(a, t, smem, odd); break;
   }
 }
 

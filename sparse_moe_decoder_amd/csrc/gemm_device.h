@@ -56,8 +56,8 @@ __device__ __forceinline__ GemmTile decode_tile(const ExpertArgs& a, int NT, int
   const int mtiles = a.tile_start[e + 1] - a.tile_start[e];
   const int within = L - a.tile_start[e] * NT;
   const int cnt = a.offsets[e + 1] - a.offsets[e];
-  // equal tiles, a multiple of 64 rows each (at most GBM; the last one is not empty)
-  const int per = (((cnt + mtiles - 1) / mtiles) + 63) & ~63;
+  // equal tiles, a multiple of 32 rows each (at most GBM; the last one is not empty)
+  const int per = (((cnt + mtiles - 1) / mtiles) + 31) & ~31;
   // an expert's tiles in blocks of up to kGemmMBlock m-tiles: block by block, each
   // n-tile with the block's m-tiles (an expert of at most kGemmMBlock m-tiles is one
   // block: n-tile by n-tile, all its m-tiles)
