@@ -52,20 +52,26 @@ __device__ __forceinline__ uint32_t mxfp4_scale_byte(uint32_t amax) {
 }
 
 // Eight values (half-word e of v is element e) to their codes with scale byte sbyte:
-// element e in nibble e
+// element e in nibble e. v_cvt_scalef32_pk_fp4_f32 divides two FP32 values by its scale
+// operand and rounds each quotient to E2M1 with ties to the even code and saturation at 6,
+// the sign kept (the first value in the low nibble of the selected byte, the other bytes
+// kept): on gfx950 it gives exactly the codes of the rule above for every finite BF16 value
+// and every scale exponent X in [-127, 127] when the operand is 2^X (checked exhaustively,
+// 2^-127 passed as the subnormal), so one instruction per pair replaces seven comparisons
+// per value. The pairs are unpacked to FP32 explicitly: the packed-BF16 form of the
+// instruction, fed from elements of a vector, was compiled with one source register for all
+// four byte positions.
 __device__ __forceinline__ uint32_t mxfp4_codes8(const u32x4& v, uint32_t sbyte) {
-  const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^-X
+  const float sc = __uint_as_float(sbyte ? (sbyte << 23) : 0x00400000u);  // 2^X exactly
   uint32_t out = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint32_t bits = hh ? (v[j] >> 16) : (v[j] & 0xFFFFu);
-      const float q = __uint_as_float((bits & 0x7FFFu) << 16) * inv;
-      const uint32_t m = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
-                         (q > 2.5f) + (q >= 3.5f) + (q > 5.0f);
-      out |= (m | ((bits >> 12) & 8u)) << (4 * (j * 2 + hh));
-    }
+#define BEAM_FP4_PAIR(j)                                                                   \
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v[j] << 16),        \
+                                                 __uint_as_float(v[j] & 0xFFFF0000u), sc, j)
+  BEAM_FP4_PAIR(0);
+  BEAM_FP4_PAIR(1);
+  BEAM_FP4_PAIR(2);
+  BEAM_FP4_PAIR(3);
+#undef BEAM_FP4_PAIR
   return out;
 }
 
