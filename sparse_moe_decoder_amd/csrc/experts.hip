@@ -725,25 +725,33 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // epilogue through LDS: the stages hold the output tile
+  // epilogue through LDS (row quads, quad_store / quad_rows): the stages hold the output tile
   uint16_t* stage = smem;
+  const int nq = (rows + 3) >> 2;  // row quads holding rows
   if (GATEUP) {
     // act tile [256 rows][128 q]; wave (wm, wn) holds 32-row tiles 2 mt + wm, q [32 wn, +32)
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (2 * mt + wm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int q = wn * 32 + l32;
-        const float gv = bf2f(f2bf(acc[mt][0][r])), uv = bf2f(f2bf(acc[mt][1][r]));
-        stage[row * 128 + q] = f2bf(silu(gv) * uv);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gv = bf2f(f2bf(acc[mt][0][4 * i + j])), uv = bf2f(f2bf(acc[mt][1][4 * i + j]));
+          h[j] = f2bf(silu(gv) * uv);
+        }
+        quad_store<128>(stage, (2 * mt + wm) * 8 + 2 * i + lh, wn * 32 + l32, h[0] | (h[1] << 16),
+                        h[2] | (h[3] << 16));
       }
     }
     __syncthreads();
-    for (int c = tid; c < rows * 16; c += 64 * NW) {
-      const int r = c >> 4, ch = c & 15;
-      st_u32x4(a.act + (int64_t)(row0 + r) * a.f + nb * 128 + ch * 8,
-               ld_u32x4(&stage[r * 128 + ch * 8]));
+    for (int c = tid; c < nq * 16; c += 64 * NW) {
+      const int q = c >> 4, k = c & 15;
+      u32x4 v[4];
+      quad_rows<128>(stage, q, k, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < rows) st_u32x4(a.act + (int64_t)(row0 + 4 * q + j) * a.f + nb * 128 + k * 8, v[j]);
     }
   } else {
     // output tile [256 rows][256 cols] in the first 128 KB, weighted and rounded;
@@ -758,19 +766,24 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
+      for (int i = 0; i < 4; ++i) {
+        const int rq = (2 * mt + wm) * 8 + 2 * i + lh;
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(w_row + 4 * rq);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (2 * mt + wm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int col = wn * 64 + nn * 32 + l32;
-          stage[row * 256 + col] = f2bf(w_row[row] * acc[mt][nn][r]);
-        }
+        for (int nn = 0; nn < 2; ++nn)
+          quad_store<256>(stage, rq, wn * 64 + nn * 32 + l32,
+                          pack_bf2(w4[0] * acc[mt][nn][4 * i], w4[1] * acc[mt][nn][4 * i + 1]),
+                          pack_bf2(w4[2] * acc[mt][nn][4 * i + 2], w4[3] * acc[mt][nn][4 * i + 3]));
+      }
     }
     __syncthreads();
-    for (int c = tid; c < rows * 32; c += 64 * NW) {
-      const int r = c >> 5, ch = c & 31;
-      st_u32x4(a.yk + (int64_t)slot_row[r] * a.d + nb * 256 + ch * 8,
-               ld_u32x4(&stage[r * 256 + ch * 8]));
+    for (int c = tid; c < nq * 32; c += 64 * NW) {
+      const int q = c >> 5, k = c & 31;
+      u32x4 v[4];
+      quad_rows<256>(stage, q, k, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < rows) st_u32x4(a.yk + (int64_t)slot_row[4 * q + j] * a.d + nb * 256 + k * 8, v[j]);
     }
   }
 }

@@ -279,7 +279,8 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
 
   // epilogue through LDS
   if (GATEUP) {
-    // act tile [256 rows][128 q] BF16; wave (wm, wn) holds 32-row tiles 2 mt + wm, q [32 wn, +32)
+    // act tile [256 rows][128 q] BF16, row-major (the quantiser reads whole 32-value row
+    // blocks, one per thread); wave (wm, wn) holds 32-row tiles 2 mt + wm, q [32 wn, +32)
     uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
@@ -317,19 +318,26 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
+      for (int i = 0; i < 4; ++i) {
+        const int rq = (2 * mt + wm) * 8 + 2 * i + lh;
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(w_row + 4 * rq);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (2 * mt + wm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int col = wn * 64 + nn * 32 + l32;
-          stage[row * 256 + col] = f2bf(w_row[row] * acc[mt][nn][r]);
-        }
+        for (int nn = 0; nn < 2; ++nn)
+          quad_store<256>(stage, rq, wn * 64 + nn * 32 + l32,
+                          pack_bf2(w4[0] * acc[mt][nn][4 * i], w4[1] * acc[mt][nn][4 * i + 1]),
+                          pack_bf2(w4[2] * acc[mt][nn][4 * i + 2], w4[3] * acc[mt][nn][4 * i + 3]));
+      }
     }
     __syncthreads();
-    for (int c = tid; c < rows * 32; c += 64 * NW) {
-      const int r = c >> 5, ch = c & 31;
-      st_u32x4(a.yk + (int64_t)slot_row[r] * a.d + nb * 256 + ch * 8,
-               ld_u32x4(&stage[r * 256 + ch * 8]));
+    // copy-out through row quads (quad_store / quad_rows in gemm_device.h)
+    const int nq = (rows + 3) >> 2;
+    for (int c = tid; c < nq * 32; c += 64 * NW) {
+      const int q = c >> 5, k = c & 31;
+      u32x4 v[4];
+      quad_rows<256>(stage, q, k, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < rows) st_u32x4(a.yk + (int64_t)slot_row[4 * q + j] * a.d + nb * 256 + k * 8, v[j]);
     }
   }
 }

@@ -32,6 +32,33 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
+// Epilogue staging of a GEMM output tile in row quads. A 32x32 MFMA result holds, in lane l
+// and register 4 i + j, row 8 i + 4 (l / 32) + j and column l % 32 of its tile: four
+// consecutive rows of one column. The tile (NC columns) is staged with element (row, col) at
+// half-word ((row / 4) NC + col) 4 + row % 4, so those four values are one 8-byte LDS write
+// (a quarter of the write instructions of a row-major tile), and a 4-row x 8-column block is
+// 64 contiguous bytes, which quad_rows regroups into the four rows' 16-byte chunks.
+template <int NC>
+__device__ __forceinline__ void quad_store(uint16_t* stage, int rq, int col, uint32_t rows01,
+                                           uint32_t rows23) {
+  *reinterpret_cast<uint2*>(stage + ((rq * NC) + col) * 4) = make_uint2(rows01, rows23);
+}
+
+// Rows 4 q .. 4 q + 3, columns 8 k .. 8 k + 7 of a row-quad tile: out[j] is row 4 q + j's
+// 16-byte chunk (column 8 k + c in half-word c). Column m of the block sits in dwords 2 m and
+// 2 m + 1 (rows 0-1, 2-3); v_perm_b32 takes one half-word from each of two such dwords.
+template <int NC>
+__device__ __forceinline__ void quad_rows(const uint16_t* stage, int q, int k, u32x4 out[4]) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(stage + (q * NC + k * 8) * 4);
+  const u32x4 b[4] = {src[0], src[1], src[2], src[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)  // columns 2 p (low half-word) and 2 p + 1
+      out[j][p] = __builtin_amdgcn_perm(b[p][2 + (j >> 1)], b[p][j >> 1],
+                                        (j & 1) ? 0x07060302u : 0x05040100u);
+}
+
 // One tile of a grouped GEMM: expert e, its rows [row0, row0 + rows) in the expert-grouped
 // order, column tile nb.
 struct GemmTile {
