@@ -137,9 +137,18 @@ def measured_peaks(reps: int = 5):
             "what": "1 GiB device copy (read + write bytes); torch.matmul BF16 8192^3 (hipBLASLt)"}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed (the sources hold no
+    string literal with a comment marker inside)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(unit):
-    """Hash of a kernel source file and every local header it includes (transitively):
-    a committed counter summary applies only while this is unchanged."""
+    """Hash of the code (comments and layout aside) of a kernel source file and every local
+    header it includes (transitively): a committed counter summary applies only while this
+    is unchanged."""
     csrc = os.path.join(ROOT, "sparse_moe_decoder_amd", "csrc")
     seen, todo = [], [unit]
     while todo:
@@ -154,8 +163,8 @@ def source_hash(unit):
                     todo.append(m.group(1))
     h = hashlib.sha256()
     for n in sorted(seen):
-        with open(os.path.join(csrc, n), "rb") as fh:
-            h.update(n.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, n)) as fh:
+            h.update(n.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

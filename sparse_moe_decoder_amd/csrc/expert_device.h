@@ -35,11 +35,13 @@ __device__ __forceinline__ int expert_of_block(const ExpertArgs& a, int slot, in
 // stages its K quarter of that row into LDS once (nc 16-byte chunks, chunk c = values
 // 8c .. 8c + 7 of the quarter, at xs[c]) and reads the MFMA A operand from there, leaving
 // the register ring to the weights alone. The row arrives by direct global-to-LDS copies
-// (lds_dma16) issued before the weight ring's loads; one_row_wait<N>, with N the number of
-// weight loads issued since, waits for the row and for nothing younger, so the ring stays
-// in flight and the compiler's own waits name exactly its oldest slot. Lanes past the last
-// chunk re-read it into positions past nc (xs holds kOneRowChunks * 64 chunks): every lane
-// issues the same copies, with no branch.
+// (lds_dma16), which the compiler does not count: one_row_wait<N>, with N the number of
+// vector loads issued after the copies, waits for them. Gate/up issues them before its
+// weight ring (N = the ring's loads, so the ring stays in flight); down, whose row address
+// needs the expert's offset, issues its ring first and then the copies (N = 0). Either way
+// the loop's own waits name exactly the ring's oldest slot. Lanes past the last chunk
+// re-read it into positions past nc (xs holds kOneRowChunks * 64 chunks): every lane issues
+// the same copies, with no branch.
 constexpr int kOneRowChunks = 4;  // chunks per lane: a K quarter of at most 2048 values
 
 __device__ __forceinline__ void one_row_load(u32x4* xs, const uint16_t* src, int nc, int lane) {
