@@ -350,8 +350,11 @@ int route_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z, f
   }
   int st = run_router(h, T, z, lg, s);
   if (st != BEAM_OK) return st;
-  if (slots <= kPermChunk) {
-    ProfScope ps(K_PERMUTE, s);  // routing and grouping fused
+  // routing and grouping in one workgroup while each of its 16 waves routes at most one
+  // token; beyond that the tokens go one per wave over many workgroups (topk_kernel, the
+  // same selection) and the grouping follows (one workgroup up to kPermChunk slots)
+  if (slots <= kPermChunk && T <= kRoutePermuteSmallMaxT) {
+    ProfScope ps(K_PERMUTE, s);
     return hip_status(launch_route_permute_small(ta, pa, s));
   }
   {

@@ -126,7 +126,6 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// SiLU in FP32, v / (1 + e^-v), with the accurate library exp.
 // silu(v) = v / (1 + e^-v) in FP32, with the hardware exp2 (v_exp_f32) and reciprocal
 // (v_rcp_f32): a few ulp of FP32, far below the BF16 rounding of silu(g) * u that follows,
 // and five instructions where expf and an IEEE division take about twenty-five (the SiLU of

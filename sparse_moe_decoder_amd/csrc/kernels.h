@@ -12,6 +12,7 @@ constexpr int kSplitDownMaxT = 16;  // largest T whose down pass splits K over f
 constexpr int kDenseSplitK = 4;     // dense layers, T <= 16: workgroups per down column tile
 constexpr int kFusedRouteMaxT = 16;     // router + top-k + grouping in one launch up to this T
 constexpr int kFusedRouteMaxSlots = 64;  // ... and up to this many slots (T * k)
+constexpr int kRoutePermuteSmallMaxT = 16;  // top-k + grouping in one workgroup (16 waves)
 // its arrival count: a top counter and kRouteSub sub-counters, kRouteCounterStride words apart
 constexpr int kRouteSub = 16;
 constexpr int kRouteCounterStride = 64;
