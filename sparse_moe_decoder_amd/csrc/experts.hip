@@ -532,17 +532,17 @@ __device__ __forceinline__ void wait_blocks3(int n) {
 constexpr int GSTAGE_Q = 4096 + 256;  // bytes per 4-bit B stage
 
 
-template <bool GATEUP, int MW, int NS, bool FP4 = false>
+// SKIP: this wave's last 32-row tile is empty (an odd number of 32-row tiles leaves wm = 1 one
+// tile short), so its MFMAs are left out; the SIMD it shares with a wm = 0 wave then does
+// 2 MW - 1 tiles' work. A template parameter, so the K loop has no branch.
+template <bool GATEUP, int MW, int NS, bool FP4, bool SKIP>
 __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTile& t,
-                                               uint16_t* smem, bool odd) {
+                                               uint16_t* smem) {
   constexpr int NW = 8;
   static_assert(NS >= 3 && NS <= GMAXST && NS - 2 <= 3, "stages");
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform for the LDS base
   const int wm = wvu >> 2, wn = wvu & 3;
-  // an odd number of 32-row tiles leaves wm = 1 one tile short: its last MFMAs are skipped
-  // (the SIMD it shares with a wm = 0 wave then does 2 MW - 1 tiles' work)
-  const bool skip_last = odd && wm == 1;
   const int K = GATEUP ? a.d : a.f;
   const int KS = K / 32;
   const int nkb = K / GBK;  // a multiple of NS
@@ -645,7 +645,10 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // fragments of stage st, then the MFMAs with the copies of K block kb + NS - 1
-  // placed after MFMA groups (one copy per MW / 2 groups of two)
+  // placed after MFMA groups (one copy per MW / 2 groups of two). Past the last K block the
+  // copies repeat the last block into the stage just freed (block kb - 1's, read by every
+  // wave before this step's barrier), so every step issues the same copies with no branch
+  // and every wait counts NS - 2 blocks behind the one it waits for.
   auto compute = [&](int st, int kb) {
     const uint16_t* A = stage_a(st);
     const uint16_t* B = stage_b(st);
@@ -674,47 +677,43 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
         for (int mt = 0; mt < MW; ++mt) fa[kk][mt] = ld_u32x4(A + aread[kk] + mt * 64 * GBK);
       }
     }
-    const bool more = kb + NS - 1 < nkb;
-    const int kn = kb + NS - 1, sn = (st + NS - 1) % NS;
+    const int kn = min(kb + NS - 1, nkb - 1), sn = (st + NS - 1) % NS;
     constexpr int EVERY = MW >= 2 ? MW / 2 : 1;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int mt = 0; mt < MW; ++mt) {
-        if (mt + 1 < MW || !skip_last) {
+        if (mt + 1 < MW || !SKIP) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn) acc[mt][nn] = mfma32(fa[kk][mt], fb[kk][nn], acc[mt][nn]);
         }
         const int q = kk * MW + mt;
         if (q % EVERY == 0 && q / EVERY < CP) {
           __builtin_amdgcn_sched_barrier(0);
-          if (more) issue(kn, sn, q / EVERY);
+          issue(kn, sn, q / EVERY);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     if (MW == 1) {  // two MFMA groups: the remaining copies go after them
       __builtin_amdgcn_sched_barrier(0);
-      if (more) {
 #pragma unroll
-        for (int p = 2; p < CP; ++p) issue(kn, sn, p);
-      }
+      for (int p = 2; p < CP; ++p) issue(kn, sn, p);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // step kb: blocks kb + 1 .. kb + NS - 2 may still be in flight behind block kb
+  // step kb: blocks kb + 1 .. kb + NS - 2 (or their repeats) are in flight behind block kb
   auto step = [&](int kb, auto S) {
     constexpr int st = decltype(S)::value;
-    const int later = nkb - 1 - kb;
-    if constexpr (FP4) wait_blocks3(later < NS - 2 ? later : NS - 2);
-    else wait_blocks(later < NS - 2 ? later : NS - 2);
+    if constexpr (FP4) wait_blocks3(NS - 2);
+    else wait_blocks(NS - 2);
     __builtin_amdgcn_s_barrier();
     compute(st, kb);
   };
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
 #pragma unroll
-    for (int p = 0; p < CP; ++p) issue(j, j, p);
+    for (int p = 0; p < CP; ++p) issue(min(j, nkb - 1), j, p);
   for (int kb = 0; kb < nkb; kb += NS) {
     step(kb, std::integral_constant<int, 0>{});
     step(kb + 1, std::integral_constant<int, 1>{});
@@ -788,15 +787,23 @@ __device__ __forceinline__ void gemm_tile_body(const ExpertArgs& a, const GemmTi
   }
 }
 
+template <bool GATEUP, int MW, int NS, bool FP4>
+__device__ __forceinline__ void gemm_tile_skip(const ExpertArgs& a, const GemmTile& t, uint16_t* smem,
+                                               bool skip) {
+  if (skip) gemm_tile_body<GATEUP, MW, NS, FP4, true>(a, t, smem);
+  else gemm_tile_body<GATEUP, MW, NS, FP4, false>(a, t, smem);
+}
+
 template <bool GATEUP, int NS, bool FP4 = false>
 __device__ __forceinline__ void gemm_tile_mw(const ExpertArgs& a, const GemmTile& t, uint16_t* smem) {
   const int n32 = (t.rows + 31) >> 5;  // 32-row tiles: wm = 0 takes the even ones, wm = 1 the odd
-  const bool odd = n32 & 1;
+  const int wm = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >> 2;
+  const bool skip = (n32 & 1) && wm == 1;
   switch ((n32 + 1) >> 1) {  // tiles per wave
-    case 1: gemm_tile_body<GATEUP, 1, NS, FP4>(a, t, smem, odd); break;
-    case 2: gemm_tile_body<GATEUP, 2, NS, FP4>(a, t, smem, odd); break;
-    case 3: gemm_tile_body<GATEUP, 3, NS, FP4>(a, t, smem, odd); break;
-    default: gemm_tile_body<GATEUP, 4, NS, FP4>(a, t, smem, odd); break;
+    case 1: gemm_tile_skip<GATEUP, 1, NS, FP4>(a, t, smem, skip); break;
+    case 2: gemm_tile_skip<GATEUP, 2, NS, FP4>(a, t, smem, skip); break;
+    case 3: gemm_tile_skip<GATEUP, 3, NS, FP4>(a, t, smem, skip); break;
+    default: gemm_tile_skip<GATEUP, 4, NS, FP4>(a, t, smem, skip); break;
   }
 }
 
