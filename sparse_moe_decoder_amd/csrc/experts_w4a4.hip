@@ -25,7 +25,8 @@
 // c ^ ((r / 4) % 4)), A scales 256 rows x 4 B (the row's four block scales), B codes 4 K
 // blocks x 4 KB and B scales 4 x 256 B copied verbatim from the weight layout. Each wave
 // issues five direct-to-LDS copies per stage: two of A codes, two of B codes, and one of
-// A scales (waves 0-3) or B scales (waves 4-7).
+// 4 bytes per lane holding A scales (waves 0-3) or B scales (waves 4-7). The K loop has no
+// branch: past the last K block the copies repeat it into the stage just freed.
 #include "common.h"
 #include "kernels.h"
 #include "gemm_device.h"
@@ -118,17 +119,17 @@ __device__ __forceinline__ f32x16 mfma_fp4(const u32x4& a, uint32_t sa, const u3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-template <bool GATEUP, int MW>
+// SKIP: this wave's last 32-row tile is empty (an odd number of 32-row tiles leaves wm = 1 one
+// tile short), so its MFMAs are left out.
+template <bool GATEUP, int MW, bool SKIP>
 __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const GemmTile& t,
-                                                  uint8_t* smem, bool odd) {
+                                                  uint8_t* smem) {
   constexpr int NW = 8;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int wm = wvu >> 2, wn = wvu & 3;
-  // an odd number of 32-row tiles leaves wm = 1 one tile short: its last MFMAs are skipped
-  const bool skip_last = odd && wm == 1;
   const int K = GATEUP ? a.d : a.f;
-  const int nkb = K / QBK;  // a multiple of QNS - 1 is not needed: the loop handles any count
+  const int nkb = K / QBK;  // any count: the loop is not unrolled by stages
   const int e = t.e, row0 = t.row0, rows = t.rows, nb = t.nb;
 
   // A codes: wave w fills rows [32 w, 32 w + 32) with 2 copies of 16 rows; lane l covers
@@ -145,19 +146,28 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
     const int64_t src_row = GATEUP ? (int64_t)(a.perm[row0 + rr] / a.k) : (int64_t)(row0 + rr);
     aoff[i] = src_row * arow_b + c * 16;
   }
-  // A scales (waves 0-3): lane l covers row 64 w + l, its four block scales of the stage
-  int64_t asoff = 0;
-  if (wvu < 4) {
-    const int r = wv * 64 + lane;
-    const int rr = r < rows ? r : 0;
-    const int64_t src_row = GATEUP ? (int64_t)(a.perm[row0 + rr] / a.k) : (int64_t)(row0 + rr);
-    asoff = src_row * arow_s;
-  }
   // B: the weight layout's (expert, n-tile, 32-wide K block) blocks, four per stage
   const int NTL = GATEUP ? a.f / 128 : a.d / 256;
   const int64_t blk0 = ((int64_t)e * NTL + nb) * (K / 32);
   const uint8_t* bq = (GATEUP ? a.pqgu : a.pqd) + blk0 * 4096 + wv * 2048 + lane * 16;
-  const uint8_t* bs = (GATEUP ? a.psgu : a.psd) + blk0 * 256 + (wv & 3) * 256 + lane * 16;
+  // scales, 4 bytes per lane and stage: waves 0-3 A's (lane l: row 64 w + l, its four block
+  // scales of the stage, sc_step bytes per stage), waves 4-7 B's (scale block w - 4 of the
+  // stage's four, 1024 bytes per stage)
+  const uint8_t* sc_src;
+  int sc_step;
+  uint32_t sc_dst;
+  if (wvu < 4) {
+    const int r = wv * 64 + lane;
+    const int rr = r < rows ? r : 0;
+    const int64_t src_row = GATEUP ? (int64_t)(a.perm[row0 + rr] / a.k) : (int64_t)(row0 + rr);
+    sc_src = asbase + src_row * arow_s;
+    sc_step = 4;
+    sc_dst = QA + wvu * 256;
+  } else {
+    sc_src = (GATEUP ? a.psgu : a.psd) + blk0 * 256 + (wvu - 4) * 256 + lane * 4;
+    sc_step = 4 * 256;
+    sc_dst = QA + QAS + QB + (wvu - 4) * 256;
+  }
 
   // down: thread r < 256 holds row r's slot and routing weight for the epilogue
   int my_slot = 0;
@@ -177,11 +187,8 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
     } else if (p < 4) {
       lds_dma16((const uint16_t*)(bq + (int64_t)kb * 4 * 4096 + (p - 2) * 1024),
                 lds_addr(S + QA + QAS) + (uint32_t)(wvu * 2048) + (p - 2) * 1024);
-    } else if (wvu < 4) {
-      lds_dma4(asbase + asoff + kb * 4, lds_addr(S + QA) + (uint32_t)(wvu * 256));
-    } else if (lane < 16) {
-      lds_dma16((const uint16_t*)(bs + (int64_t)kb * 4 * 256),
-                lds_addr(S + QA + QAS + QB) + (uint32_t)((wvu - 4) * 256));
+    } else {
+      lds_dma4(sc_src + (int64_t)kb * sc_step, lds_addr(S) + sc_dst);
     }
   };
 
@@ -216,8 +223,7 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
     const uint8_t* SAS = S + QA;
     const uint8_t* SB = S + QA + QAS;
     const uint8_t* SBS = S + QA + QAS + QB;
-    const bool more = kb + QNS - 1 < nkb;
-    const int kn = kb + QNS - 1, sn = (st + QNS - 1) % QNS;
+    const int kn = min(kb + QNS - 1, nkb - 1), sn = (st + QNS - 1) % QNS;
     int q = 0;  // MFMA groups done, for placing the next block's copies
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -241,36 +247,32 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
       }
 #pragma unroll
       for (int mt = 0; mt < MW; ++mt) {
-        if (mt + 1 < MW || !skip_last) {
+        if (mt + 1 < MW || !SKIP) {
 #pragma unroll
           for (int nn = 0; nn < 2; ++nn)
             acc[mt][nn] = mfma_fp4(fa[mt], sa[mt], fb[nn], sb[nn], acc[mt][nn]);
         }
         if (q < CP) {
           __builtin_amdgcn_sched_barrier(0);
-          if (more) issue(kn, sn, q);
+          issue(kn, sn, q);
           __builtin_amdgcn_sched_barrier(0);
           ++q;
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      for (; q < CP; ++q) issue(kn, sn, q);
-    }
+#pragma unroll
+    for (; q < CP; ++q) issue(kn, sn, q);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: stages 0 .. QNS - 2
+  // prologue: stages 0 .. QNS - 2 (blocks past the last repeat it)
 #pragma unroll
   for (int j = 0; j < QNS - 1; ++j)
-    if (j < nkb) {
 #pragma unroll
-      for (int p = 0; p < CP; ++p) issue(j, j, p);
-    }
+    for (int p = 0; p < CP; ++p) issue(min(j, nkb - 1), j, p);
   for (int kb = 0; kb < nkb; ++kb) {
-    const int later = nkb - 1 - kb;  // blocks issued after kb (at most QNS - 2 are pending)
-    wait_blocks5(later < QNS - 2 ? later : QNS - 2);
+    wait_blocks5(QNS - 2);  // blocks kb + 1 .. kb + QNS - 2 (or repeats) stay in flight
     __builtin_amdgcn_s_barrier();
     compute(kb % QNS, kb);
   }
@@ -342,6 +344,13 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
   }
 }
 
+template <bool GATEUP, int MW>
+__device__ __forceinline__ void gemm_a4_tile_skip(const ExpertArgs& a, const GemmTile& t, uint8_t* smem,
+                                                  bool skip) {
+  if (skip) gemm_a4_tile_body<GATEUP, MW, true>(a, t, smem);
+  else gemm_a4_tile_body<GATEUP, MW, false>(a, t, smem);
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(512) void grouped_gemm_a4_kernel(ExpertArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[QNS * QSTAGE];
@@ -353,12 +362,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_a4_kernel(ExpertArgs a) {
   if (q >= R || L >= total) return;
   const GemmTile t = decode_tile(a, NT, L);
   const int n32 = (t.rows + 31) >> 5;  // 32-row tiles: wm = 0 takes the even ones, wm = 1 the odd
-  const bool odd = n32 & 1;
+  const int wm = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >> 2;
+  const bool skip = (n32 & 1) && wm == 1;
   switch ((n32 + 1) >> 1) {
-    case 1: gemm_a4_tile_body<GATEUP, 1>(a, t, smem, odd); break;
-    case 2: gemm_a4_tile_body<GATEUP, 2>(a, t, smem, odd); break;
-    case 3: gemm_a4_tile_body<GATEUP, 3>(a, t, smem, odd); break;
-    default: gemm_a4_tile_body<GATEUP, 4>(a, t, smem, odd); break;
+    case 1: gemm_a4_tile_skip<GATEUP, 1>(a, t, smem, skip); break;
+    case 2: gemm_a4_tile_skip<GATEUP, 2>(a, t, smem, skip); break;
+    case 3: gemm_a4_tile_skip<GATEUP, 3>(a, t, smem, skip); break;
+    default: gemm_a4_tile_skip<GATEUP, 4>(a, t, smem, skip); break;
   }
 }
 
