@@ -200,12 +200,17 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
     const int m = wm * 32 + l32;
     ar[s] = m * 64 + (((2 * s + lh) ^ ((m >> 2) & 3)) << 4);
   }
-  // B column of this lane's N tile nn (gate/up: 128 gate then 128 up stage columns)
-  int bc[2], bsw[2];
+  // B column of this lane's N tile nn (gate/up: 128 gate then 128 up stage columns). The
+  // weight layout swaps the 8-byte halves of columns with bit 4 set; the fragment is read as
+  // two 8-byte halves from swapped offsets, which puts them back in order and keeps each
+  // read free of bank conflicts (the swap exists for that).
+  int bc[2], blo[2], bhi[2];
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
     bc[nn] = GATEUP ? nn * 128 + 32 * wn + l32 : 64 * wn + 32 * nn + l32;
-    bsw[nn] = (bc[nn] >> 4) & 1;
+    const int sw = ((bc[nn] >> 4) & 1) * 8;
+    blo[nn] = bc[nn] * 16 + sw;
+    bhi[nn] = bc[nn] * 16 + 8 - sw;
   }
 
   f32x16 acc[MW][2];
@@ -232,9 +237,9 @@ __device__ __forceinline__ void gemm_a4_tile_body(const ExpertArgs& a, const Gem
       uint32_t sb[2];
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) {
-        const u32x4 raw = ld_u32x4(SB + b * 4096 + bc[nn] * 16);
-        // undo the layout's half swap of columns with bit 4 set
-        fb[nn] = bsw[nn] ? u32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+        const uint2 lo = *(const uint2*)(SB + b * 4096 + blo[nn]);
+        const uint2 hi = *(const uint2*)(SB + b * 4096 + bhi[nn]);
+        fb[nn] = u32x4{lo.x, lo.y, hi.x, hi.y};
         sb[nn] = SBS[b * 256 + bc[nn]];
       }
       u32x4 fa[MW];
