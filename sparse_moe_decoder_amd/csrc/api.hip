@@ -427,7 +427,7 @@ int forward_impl(beam_moe_ctx* h, const Workspace& ws, int T, const uint16_t* z,
         ProfScope ps(K_GATEUP, s);
         if (launch_gateup_fp4(es, max_active, s) != hipSuccess) return BEAM_ERR_HIP;
       }
-      {
+      if (!down_fp4_rounds_act(es)) {  // one token: the down pass rounds its row itself
         ProfScope ps(K_QUANT, s);
         if (launch_act_round_trip_a4(slots, c.d_ff, ws.offsets + E, ws.act, ws.aq, ws.aqs, s) !=
             hipSuccess)

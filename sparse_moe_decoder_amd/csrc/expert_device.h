@@ -36,10 +36,11 @@ __device__ __forceinline__ int expert_of_block(const ExpertArgs& a, int slot, in
 // 8c .. 8c + 7 of the quarter, at xs[c]) and reads the MFMA A operand from there, leaving
 // the register ring to the weights alone. The row arrives by direct global-to-LDS copies
 // (lds_dma16), which the compiler does not count: one_row_wait<N>, with N the number of
-// vector loads issued after the copies, waits for them. Gate/up issues them before its
-// weight ring (N = the ring's loads, so the ring stays in flight); down, whose row address
-// needs the expert's offset, issues its ring first and then the copies (N = 0). Either way
-// the loop's own waits name exactly the ring's oldest slot. Lanes past the last chunk
+// vector loads issued after the copies, waits for them. Both passes issue them before their
+// weight rings (N = the ring's loads, so the ring stays in flight; down first loads the
+// expert's offset, a scalar load, for the row address: measured faster than issuing its ring
+// first and waiting for all of it with the row), so the loop's own waits name exactly the
+// ring's oldest slot. Lanes past the last chunk
 // re-read it into positions past nc (xs holds kOneRowChunks * 64 chunks): every lane issues
 // the same copies, with no branch.
 constexpr int kOneRowChunks = 4;  // chunks per lane: a K quarter of at most 2048 values

@@ -367,9 +367,15 @@ __global__ __launch_bounds__(256) void gateup_fp4_one_kernel(ExpertArgs a) {
 
 // Single-token down (T = 1, f / 4 <= 2048): down_split_fp4_kernel's K split and order over
 // NTW 16-column tiles per wave (one at one token: twice the workgroups of the split kernel,
-// measured faster), with the expert's activation row staged in LDS after the weights' first
+// measured faster), with the expert's activation row staged in LDS before the weights' first
 // U quads are issued, and each row's slot written from the one sum.
-template <int U, int NTW>
+// RT (4-bit activations): the row staged in LDS is the expert's BF16 activation row, and
+// each wave replaces its quarter there by the MXFP4 round trip (OCP MX blocks of 32 along f)
+// before the MFMAs, while its first weight quads are in flight; every workgroup of the expert
+// computes the same values, and the one with column tile 0 also writes the row's codes
+// (GEMM order) and scales to a.aq / a.aqs, as the separate round-trip pass does for more
+// tokens.
+template <int U, int NTW, bool RT>
 __global__ __launch_bounds__(256) void down_fp4_one_kernel(ExpertArgs a) {
   const int ND = a.d / 16, NB = ND / NTW;
   const int nt0 = (blockIdx.x % NB) * NTW;
@@ -391,15 +397,35 @@ __global__ __launch_bounds__(256) void down_fp4_one_kernel(ExpertArgs a) {
       sc[u][t] = ld_stream_u32(sp + ((int64_t)t * KQ + kq) * 64);
     }
   };
+  // the row first (its address needs the expert's offset, a scalar load), then the weight
+  // ring, which stays in flight while the row is waited for (and, with RT, rounded)
+  int row0, cnt;
+  expert_rows(a, e, row0, cnt);
+  one_row_load(xs[wv], a.act + (int64_t)row0 * a.f + kq0 * 128, kqw * 16, lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     load(u, u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  int row0, cnt;
-  expert_rows(a, e, row0, cnt);
-  one_row_load(xs[wv], a.act + (int64_t)row0 * a.f + kq0 * 128, kqw * 16, lane);
-  one_row_wait<0>();
+  one_row_wait<2 * NTW * U>();
+  if constexpr (RT) {
+    // chunk ch (values 8 ch .. of the quarter) by lane ch % 64: lanes 4 j .. 4 j + 3 hold a
+    // block; the quarter's 16 kqw chunks are whole blocks, so each block's four lanes are
+    // active together
+    // (a token that names the expert more than once, under replayed routing, gives it
+    // identical rows: each gets the codes)
+    const bool keep = nt0 == 0;
+    for (int ch = lane; ch < kqw * 16; ch += 64) {
+      const int blk = kq0 * 4 + (ch >> 2);  // block of the row
+      const u32x4 v = xs[wv][ch];
+      xs[wv][ch] = mxfp4_block_rt_4lanes(v, a.aq + (int64_t)row0 * (a.f / 2) + blk * 16,
+                                         a.aqs + (int64_t)row0 * (a.f / 32) + blk, keep);
+      for (int r = 1; keep && r < cnt; ++r)
+        (void)mxfp4_block_rt_4lanes(v, a.aq + (int64_t)(row0 + r) * (a.f / 2) + blk * 16,
+                                    a.aqs + (int64_t)(row0 + r) * (a.f / 32) + blk, true);
+    }
+  }
   const u32x4* xp = xs[wv] + (lane >> 4);
   f32x4 acc[NTW];
 #pragma unroll
@@ -646,16 +672,27 @@ hipError_t launch_gateup_fp4(const ExpertArgs& a, int max_active, hipStream_t s)
   return hipGetLastError();
 }
 
+bool down_fp4_rounds_act(const ExpertArgs& a) {
+  return a.aq != nullptr && a.T == 1 && (a.f / 128 / 4) * 16 <= kOneRowChunks * 64;
+}
+
+template <bool RT>
+static void launch_down_fp4_one(const ExpertArgs& a, int max_active, hipStream_t s) {
+  const int kqw = a.f / 128 / 4;
+  dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
+  if (kqw % 5 == 0)
+    hipLaunchKernelGGL((down_fp4_one_kernel<5, 1, RT>), g, blk, 0, s, a);
+  else if (kqw % 2 == 0)
+    hipLaunchKernelGGL((down_fp4_one_kernel<2, 1, RT>), g, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL((down_fp4_one_kernel<1, 1, RT>), g, blk, 0, s, a);
+}
+
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s) {
   const int kqw = a.f / 128 / 4;
   if (a.T == 1 && kqw * 16 <= kOneRowChunks * 64) {
-    dim3 g((unsigned)(max_active * (a.d / 16))), blk(256);
-    if (kqw % 5 == 0)
-      hipLaunchKernelGGL((down_fp4_one_kernel<5, 1>), g, blk, 0, s, a);
-    else if (kqw % 2 == 0)
-      hipLaunchKernelGGL((down_fp4_one_kernel<2, 1>), g, blk, 0, s, a);
-    else
-      hipLaunchKernelGGL((down_fp4_one_kernel<1, 1>), g, blk, 0, s, a);
+    if (down_fp4_rounds_act(a)) launch_down_fp4_one<true>(a, max_active, s);
+    else launch_down_fp4_one<false>(a, max_active, s);
   } else if (a.T <= kSplitDownMaxT) {
     dim3 g((unsigned)(max_active * (a.d / 32))), blk(256);
     hipLaunchKernelGGL((down_split_fp4_kernel<1, 2>), g, blk, 0, s, a);

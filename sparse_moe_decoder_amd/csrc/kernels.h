@@ -152,6 +152,9 @@ hipError_t launch_down_splitk_dense(const ExpertArgs& a, int P, float* part, hip
 hipError_t launch_dense_plan(int T, int max_tokens, bool init, const PermArgs& a, float* w,
                              hipStream_t s);
 hipError_t launch_down_fp4(const ExpertArgs& a, int max_active, hipStream_t s);
+// whether launch_down_fp4 rounds the activations through MXFP4 itself (one token with 4-bit
+// activations: a.aq set), so the separate round-trip pass is left out
+bool down_fp4_rounds_act(const ExpertArgs& a);
 // the boundary with x = the combine of c (b.x unused); b.d <= kBoundaryWgMaxD
 hipError_t launch_combine_boundary(const BoundaryArgs& b, const CombineArgs& c, hipStream_t s);
 hipError_t launch_router_fp32(const RouterArgs& a, hipStream_t s);

@@ -115,20 +115,28 @@ __device__ __forceinline__ void mxfp4_block_out(u32x4 v[4], uint8_t* codes, uint
 }
 
 // One block of 32 BF16 values held by four consecutive lanes (lane 4 j + q holds elements
-// 8 q .. 8 q + 7 in v): its codes (16 bytes at codes, GEMM order), its scale byte (at scale)
-// and its round trip (32 BF16 values at rt); every lane of the four passes the block's
-// pointers. The four lanes must be active together.
-__device__ __forceinline__ void mxfp4_block_out_4lanes(const u32x4& v, uint8_t* codes,
-                                                       uint8_t* scale, uint16_t* rt) {
+// 8 q .. 8 q + 7 in v): this lane's eight values of the block's round trip; with keep, also
+// the block's codes (16 bytes at codes, GEMM order) and scale byte (at scale), which every
+// lane of the four passes. The four lanes must be active together.
+__device__ __forceinline__ u32x4 mxfp4_block_rt_4lanes(const u32x4& v, uint8_t* codes,
+                                                      uint8_t* scale, bool keep) {
   const int q = threadIdx.x & 3;
   uint32_t amax = bf16x8_amax(v);
-  amax = max_u32(amax, (uint32_t)__shfl_xor((int)amax, 1, 4));
-  amax = max_u32(amax, (uint32_t)__shfl_xor((int)amax, 2, 4));
+  amax = max_u32(amax, dpp_u32<0xB1>(amax));  // the four lanes are a DPP quad: quad_perm [1,0,3,2]
+  amax = max_u32(amax, dpp_u32<0x4E>(amax));  // quad_perm [2,3,0,1]
   const uint32_t sbyte = mxfp4_scale_byte(amax);
   const uint32_t c = mxfp4_codes8(v, sbyte);
-  reinterpret_cast<uint32_t*>(codes)[q == 1 ? 2 : q == 2 ? 1 : q] = c;  // GEMM order
-  if (q == 0) *scale = (uint8_t)sbyte;
-  st_u32x4(rt + 8 * q, fp4x8_to_bf16(c, e8m0_scale(sbyte)));
+  if (keep) {
+    reinterpret_cast<uint32_t*>(codes)[q == 1 ? 2 : q == 2 ? 1 : q] = c;  // GEMM order
+    if (q == 0) *scale = (uint8_t)sbyte;
+  }
+  return fp4x8_to_bf16(c, e8m0_scale(sbyte));
+}
+
+// The same block with its codes, scale and round trip (32 BF16 values at rt) written out.
+__device__ __forceinline__ void mxfp4_block_out_4lanes(const u32x4& v, uint8_t* codes,
+                                                       uint8_t* scale, uint16_t* rt) {
+  st_u32x4(rt + 8 * (threadIdx.x & 3), mxfp4_block_rt_4lanes(v, codes, scale, true));
 }
 
 }  // namespace beam

@@ -60,23 +60,24 @@ def dequant(codes, scales):
     return P.F(oracle.mxfp4_dequantize(codes, scales)).astype(np.float64)
 
 
-def run(moe, z, ids_in=None, w_in=None):
+def run(moe, z, ids_in=None, w_in=None, wl=WL):
     import torch
     T = z.shape[0]
     y, r = moe.forward(P.to_dev(z), ids_in=ids_in, w_in=w_in, want_routing=True)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in r.items()}
     g["y"] = P.bits(y)
-    S = T * WL.k
-    g["zq"] = moe.inspect("z_codes", T * WL.d // 2).cpu().numpy().reshape(T, WL.d // 2)
-    g["zs"] = moe.inspect("z_scales", T * WL.d // 32).cpu().numpy().reshape(T, WL.d // 32)
-    g["aq"] = moe.inspect("act_codes", S * WL.f // 2).cpu().numpy().reshape(S, WL.f // 2)
-    g["as"] = moe.inspect("act_scales", S * WL.f // 32).cpu().numpy().reshape(S, WL.f // 32)
+    S = T * wl.k
+    g["zq"] = moe.inspect("z_codes", T * wl.d // 2).cpu().numpy().reshape(T, wl.d // 2)
+    g["zs"] = moe.inspect("z_scales", T * wl.d // 32).cpu().numpy().reshape(T, wl.d // 32)
+    g["aq"] = moe.inspect("act_codes", S * wl.f // 2).cpu().numpy().reshape(S, wl.f // 2)
+    g["as"] = moe.inspect("act_scales", S * wl.f // 32).cpu().numpy().reshape(S, wl.f // 32)
     return g
 
 
-def check_stages(g, z, ids, w, host, what):
+def check_stages(g, z, ids, w, host, what, wl=WL):
     T, k = ids.shape
+    WL = wl  # noqa: N806 (the stage checks below read the workload's shapes)
     # 1. token rows
     o_zq, o_zs = oracle.mxfp4_quantize(z)
     assert np.array_equal(natural_order(g["zq"], WL.d), o_zq), what
@@ -199,6 +200,58 @@ def test_w4a4_fused_entry_points(layer, T):
     torch.cuda.synchronize()
     assert np.array_equal(P.bits(y2), P.bits(y1))
     assert np.array_equal(P.bits(y3), P.bits(y1))
+
+
+WL_ROW = Workload("w4a4_row", T=1, d=5120, E=16, G=4, kg=2, k=4, f=2560)
+
+
+@pytest.mark.parametrize("repeat", [False, True])
+def test_w4a4_one_token_beam_rows(repeat):
+    """One token at Beam's hidden size and d_ff: the single-token down pass rounds the
+    activation row through MXFP4 itself (80 chunks of the row per wave, two passes of 64
+    lanes, the five-deep weight ring). Every stage is checked as in the decode tests: the
+    activation codes and scales against the oracle's MXFP4 of the oracle's activations, y
+    against the oracle's down + combine on the GPU's codes. With replayed routing that names
+    one expert twice, that expert's two rows both carry the codes."""
+    import torch
+    import sparse_moe_decoder_amd as beam
+    from synth import device as sd
+    wl = WL_ROW
+    print(f"[w4a4] one token, Beam rows, repeat={repeat}", flush=True)
+    W, b = sd.router(wl)
+    fp4 = []
+    for t in sd.experts(wl):
+        fp4 += list(beam.beam_mxfp4_quantize(t))
+        del t
+    moe = beam.BeamMoE(sd.moe_config(wl, max_tokens=1), W, b, None, None, None, mxfp4=tuple(fp4))
+    del fp4
+    try:
+        moe.set_activation_format(beam.ACT_MXFP4)
+        torch.cuda.synchronize()
+
+        class Host(dict):  # the oracle's dequantised 4-bit weights, per expert on first use
+            def __missing__(self, e):
+                self[e] = tuple(oracle.mxfp4_dequantize(*oracle.mxfp4_quantize(m))
+                                for m in synth.expert_weights(wl, e))
+                return self[e]
+
+        host = Host()
+        z = synth.token_rows(wl, range(1), "x")
+        g = run(moe, z, wl=wl)
+        ids, w = g["ids_out"].reshape(1, wl.k), g["w_out"].reshape(1, wl.k)
+        if repeat:
+            ids = ids.copy()
+            ids[0, 1] = ids[0, 0]
+            g = run(moe, z, ids_in=P.to_dev(ids), w_in=P.to_dev(w), wl=wl)
+            nv = int(g["offsets_out"][-1])
+            e0 = int(ids[0, 0])
+            rows = np.nonzero(ids.ravel()[g["perm_out"][:nv]] == e0)[0]
+            assert rows.size == 2
+            assert np.array_equal(g["aq"][rows[0]], g["aq"][rows[1]])
+            assert np.array_equal(g["as"][rows[0]], g["as"][rows[1]])
+        check_stages(g, z, ids, w, host, f"one token, Beam rows, repeat={repeat}", wl=wl)
+    finally:
+        moe.close()
 
 
 WL_FEW = Workload("w4a4_few", T=8, d=4096, E=8, G=2, kg=1, k=2, f=512)
