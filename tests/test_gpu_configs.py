@@ -8,8 +8,10 @@
   its two-level arrival count: sub-counters with unequal arrivals (24 experts), and fewer
   experts than sub-counters (8);
 - batch sizes that take each routing, grouping and expert path: the one-launch
-  small-batch routing (T <= 16 and T*k <= 64), the one-workgroup grouping, the
-  multi-block grouping, the split and the streaming down passes, the grouped GEMMs.
+  small-batch routing (T <= 16 and T*k <= 64), routing and grouping in one workgroup
+  (T <= 16), the one-wave-per-token top-k before the one-workgroup grouping (from 17
+  tokens; 16 and 17 sit on either side), the multi-block grouping, the split and the
+  streaming down passes, the grouped GEMMs.
 
 Routing is compared bit for bit with the oracle on identical logits (the GPU's own);
 the logits to 1e-5 per row; the permutation exactly; the output element by element
@@ -35,7 +37,7 @@ CONFIGS = [
     Workload("e8g2", T=1, d=256, E=8, G=2, kg=1, k=2, f=256),        # fewer experts than counters
 ]
 MAX_T = 300
-T_FORWARD = (1, 7, 40, MAX_T)
+T_FORWARD = (1, 7, 16, 17, 40, MAX_T)
 
 
 @pytest.fixture(scope="module", params=CONFIGS, ids=[c.name for c in CONFIGS])
